@@ -1,0 +1,308 @@
+/*
+ * CPU oracle for the Longformer "diagonaled matmul" family and its banded softmax.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or load
+ * this file or the library built from it; only the test suite, the smoke check
+ * and the CPU-baseline leg of the benchmark do.  It shares no code with the HIP
+ * library: its own element conversions, its own index arithmetic, its own loops.
+ *
+ * What is computed (sources are the three web pages the method is described on):
+ *
+ *   TVM Discuss, "Developing a faster schedule for Longformer's kernel":
+ *     post 1   - the kernel is a banded matrix product that evaluates only certain
+ *                diagonals of the output matrix (figures 2.b / 2.c of the
+ *                Longformer paper: sliding window, optionally dilated);
+ *     post 3   - dilation is the gap between the selected diagonals, 0 = none;
+ *     post 5   - parameters b, n, h, m, w, w_upper, padding, transpose_t1, t1d3, t3d3;
+ *                w_upper is the window to the right of the word;
+ *     post 6   - one forward function (last dim of the result t3d3 = 2w+1) and two
+ *                backward functions told apart by transpose_t1, whose first operand
+ *                t1 is the band (last dim 2w+1); "padding" is any constant.
+ *   csarofeen/pytorch issue 2096, first fusion repro: the attention softmax recipe
+ *     (scale the scores, take the row max, subtract, exp, row sum, divide).
+ *
+ * Readings where the pages leave a step open (each is listed in the design notes):
+ *   - stride s = max(dilation, 1): 0 and 1 both mean contiguous diagonals, and
+ *     dilation 3 puts slot k of row i on key i + (k - w) * 3;
+ *   - K = w + w_upper + 1 slots per row; slot k is key offset (k - w) * s, so slots
+ *     below w look left, slot w is the main diagonal, slots above w look right;
+ *   - a slot whose key index falls outside [0, n) is "out of range": qk writes the
+ *     padding constant there; pv / pvT skip such terms by index, whatever the band
+ *     holds; the banded softmax masks them to -inf, so their probability is 0;
+ *   - dense layout [b][n][h][d], band layout [b][n][h][K], both contiguous.
+ *
+ * Arithmetic: every element is widened exactly to double, products and sums are
+ * formed in double, and the result is rounded once, to nearest-even, to the output
+ * type (OR_F64 keeps the unrounded double, for tolerance checks).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_F64 = 3 };
+
+/* ---------------------------------------------------------------- conversions */
+
+static double or_half_to_double(uint16_t bits)
+{
+    int sign = bits >> 15;
+    int e = (bits >> 10) & 0x1f;
+    int m = bits & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 25); /* (1024 + m) * 2^(e - 15 - 10) */
+    return sign ? -v : v;
+}
+
+static double or_bf16_to_double(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round x to the nearest multiple of 2^qexp, ties to even (rint in the default
+ * rounding mode); scaling by a power of two is exact in double. */
+static double or_round_to_quantum(double x, int qexp)
+{
+    return ldexp(rint(ldexp(x, -qexp)), qexp);
+}
+
+/* binary16: 1 sign, 5 exponent (bias 15), 10 mantissa bits; max 65504. */
+static uint16_t or_double_to_half(double x)
+{
+    if (isnan(x)) return 0x7e00;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isinf(a)) return sign | 0x7c00;
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);          /* a = f * 2^e, f in [0.5, 1): unbiased exponent is e - 1 */
+    int E = e - 1;
+    int qexp = (E < -14) ? -24 : E - 10;
+    double r = or_round_to_quantum(a, qexp);
+    if (r > 65504.0) return sign | 0x7c00;
+    if (r < ldexp(1.0, -14)) /* subnormal (or rounded up to exactly 2^-14, same bits) */
+        return sign | (uint16_t)ldexp(r, 24);
+    frexp(r, &e);
+    E = e - 1;
+    uint16_t mant = (uint16_t)(ldexp(r, 10 - E) - 1024.0);
+    return sign | (uint16_t)((E + 15) << 10) | mant;
+}
+
+/* bfloat16: the upper half of a binary32; 8 exponent bits, 7 mantissa bits. */
+static uint16_t or_double_to_bf16(double x)
+{
+    if (isnan(x)) return 0x7fc0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isinf(a)) return sign | 0x7f80;
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);
+    int E = e - 1;
+    int qexp = (E < -126) ? -133 : E - 7;
+    double r = or_round_to_quantum(a, qexp);
+    if (r > 3.3895313892515355e38) return sign | 0x7f80; /* above the largest finite */
+    float f = (float)r;    /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return sign | (uint16_t)(u >> 16);
+}
+
+static double or_load(const void* p, int64_t idx, int dt)
+{
+    switch (dt) {
+    case OR_F32: return (double)((const float*)p)[idx];
+    case OR_F16: return or_half_to_double(((const uint16_t*)p)[idx]);
+    case OR_BF16: return or_bf16_to_double(((const uint16_t*)p)[idx]);
+    default: return ((const double*)p)[idx];
+    }
+}
+
+static void or_store(void* p, int64_t idx, int dt, double v)
+{
+    switch (dt) {
+    case OR_F32: ((float*)p)[idx] = (float)v; break; /* C cast: round to nearest even */
+    case OR_F16: ((uint16_t*)p)[idx] = or_double_to_half(v); break;
+    case OR_BF16: ((uint16_t*)p)[idx] = or_double_to_bf16(v); break;
+    default: ((double*)p)[idx] = v; break;
+    }
+}
+
+/* Exposed for the tests that pin the conversions against library routines. */
+void oracle_convert(const double* x, void* out, int64_t count, int dt)
+{
+    for (int64_t t = 0; t < count; ++t) or_store(out, t, dt, x[t]);
+}
+
+void oracle_widen(const void* x, double* out, int64_t count, int dt)
+{
+    for (int64_t t = 0; t < count; ++t) out[t] = or_load(x, t, dt);
+}
+
+/* ------------------------------------------------------------------ indexing */
+
+static int64_t or_stride(int64_t dilation) { return dilation > 1 ? dilation : 1; }
+
+static int or_check(int64_t b, int64_t n, int64_t h, int64_t d, int64_t w, int64_t wu,
+                    int64_t dil, int in_dt, int out_dt)
+{
+    if (b < 0 || n < 0 || h < 0 || d < 1 || w < 0 || wu < 0 || dil < 0) return 1;
+    if (in_dt < OR_F32 || in_dt > OR_F64 || out_dt < OR_F32 || out_dt > OR_F64) return 2;
+    return 0;
+}
+
+/* Row list: rows[r] is a flattened (batch, position) index bb * n + i.  When rows is
+ * NULL every row is computed, in order.  Otherwise only the listed rows are, and every
+ * row-local operand (Q for qk, the band for pv and the softmax, and the output) is
+ * packed: its row r belongs to position rows[r].  Operands reached through the index
+ * map (K, V, X, and the band of pvT) are always the full [b][n][h][.] tensors. */
+static int64_t or_row(const int64_t* rows, int64_t r) { return rows ? rows[r] : r; }
+
+/* ------------------------------------------------------------------ qk
+ * band[bb,i,hh,k] = sum_c Q[bb,i,hh,c] * K[bb,j,hh,c]   with j = i + (k - w) * s,
+ * and = padding where j is outside [0, n).  The forward function of the pages'
+ * kernel: t1 = Q, t2 = K, t3 = the band with last dimension w + w_upper + 1. */
+int oracle_qk(const void* q, const void* kmat, void* out, int64_t b, int64_t n, int64_t h,
+              int64_t d, int64_t w, int64_t wu, int64_t dil, double pad, int in_dt,
+              int out_dt, const int64_t* rows, int64_t nrows, int nthreads)
+{
+    int bad = or_check(b, n, h, d, w, wu, dil, in_dt, out_dt);
+    if (bad) return bad;
+    const int64_t K = w + wu + 1, s = or_stride(dil);
+    if (!rows) nrows = b * n;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t bi = or_row(rows, r), bb = bi / n, i = bi % n;
+        for (int64_t hh = 0; hh < h; ++hh) {
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t j = i + (k - w) * s;
+                const int64_t o = (r * h + hh) * K + k;
+                if (j < 0 || j >= n) {
+                    or_store(out, o, out_dt, pad);
+                    continue;
+                }
+                double acc = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    acc += or_load(q, (r * h + hh) * d + c, in_dt) *
+                           or_load(kmat, ((bb * n + j) * h + hh) * d + c, in_dt);
+                or_store(out, o, out_dt, acc);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ pv
+ * out[bb,i,hh,c] = sum_k P[bb,i,hh,k] * V[bb,j,hh,c] over the slots k whose key
+ * j = i + (k - w) * s is inside [0, n).  The backward function with transpose_t1 = 0:
+ * t1 is the band (last dimension 2w+1 when w_upper = w), t2 is dense. */
+int oracle_pv(const void* band, const void* v, void* out, int64_t b, int64_t n, int64_t h,
+              int64_t d, int64_t w, int64_t wu, int64_t dil, int in_dt, int out_dt,
+              const int64_t* rows, int64_t nrows, int nthreads)
+{
+    int bad = or_check(b, n, h, d, w, wu, dil, in_dt, out_dt);
+    if (bad) return bad;
+    const int64_t K = w + wu + 1, s = or_stride(dil);
+    if (!rows) nrows = b * n;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t bi = or_row(rows, r), bb = bi / n, i = bi % n;
+        for (int64_t hh = 0; hh < h; ++hh) {
+            for (int64_t c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const int64_t j = i + (k - w) * s;
+                    if (j < 0 || j >= n) continue;
+                    acc += or_load(band, (r * h + hh) * K + k, in_dt) *
+                           or_load(v, ((bb * n + j) * h + hh) * d + c, in_dt);
+                }
+                or_store(out, (r * h + hh) * d + c, out_dt, acc);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ pvT
+ * The backward function with transpose_t1 = 1: the band is used transposed.
+ * out[bb,j,hh,c] = sum over the pairs (i, k) with i + (k - w) * s = j of
+ *                  G[bb,i,hh,k] * X[bb,i,hh,c];
+ * for each output row j and slot k there is exactly one candidate
+ * i = j - (k - w) * s, taken when it lies inside [0, n). */
+int oracle_pvT(const void* band, const void* x, void* out, int64_t b, int64_t n, int64_t h,
+               int64_t d, int64_t w, int64_t wu, int64_t dil, int in_dt, int out_dt,
+               const int64_t* rows, int64_t nrows, int nthreads)
+{
+    int bad = or_check(b, n, h, d, w, wu, dil, in_dt, out_dt);
+    if (bad) return bad;
+    const int64_t K = w + wu + 1, s = or_stride(dil);
+    if (!rows) nrows = b * n;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t bj = or_row(rows, r), bb = bj / n, j = bj % n;
+        for (int64_t hh = 0; hh < h; ++hh) {
+            for (int64_t c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const int64_t i = j - (k - w) * s;
+                    if (i < 0 || i >= n) continue;
+                    acc += or_load(band, ((bb * n + i) * h + hh) * K + k, in_dt) *
+                           or_load(x, ((bb * n + i) * h + hh) * d + c, in_dt);
+                }
+                or_store(out, (r * h + hh) * d + c, out_dt, acc);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ softmax
+ * Per (bb, i, hh) row of K slots: x_k = scale * S[k] for in-range slots, -inf for
+ * the others; P_k = exp(x_k - max x) / sum_k exp(x_k - max x).  Out-of-range slots
+ * get exactly 0.  The row always holds slot w (key i itself), so it is never empty.
+ * The recipe (scale, max, subtract, exp, sum, divide) is the attention softmax of
+ * the first fusion repro on the csarofeen/pytorch issue 2096 page. */
+int oracle_softmax(const void* scores, void* probs, int64_t b, int64_t n, int64_t h,
+                   int64_t w, int64_t wu, int64_t dil, double scale, int in_dt, int out_dt,
+                   const int64_t* rows, int64_t nrows, int nthreads)
+{
+    int bad = or_check(b, n, h, 1, w, wu, dil, in_dt, out_dt);
+    if (bad) return bad;
+    const int64_t K = w + wu + 1, s = or_stride(dil);
+    if (!rows) nrows = b * n;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = or_row(rows, r) % n;
+        for (int64_t hh = 0; hh < h; ++hh) {
+            const int64_t row = (r * h + hh) * K;
+            double m = -INFINITY;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t j = i + (k - w) * s;
+                if (j < 0 || j >= n) continue;
+                const double x = scale * or_load(scores, row + k, in_dt);
+                if (x > m) m = x;
+            }
+            double sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t j = i + (k - w) * s;
+                if (j < 0 || j >= n) continue;
+                sum += exp(scale * or_load(scores, row + k, in_dt) - m);
+            }
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t j = i + (k - w) * s;
+                double p = 0.0;
+                if (j >= 0 && j < n) p = exp(scale * or_load(scores, row + k, in_dt) - m) / sum;
+                or_store(probs, row + k, out_dt, p);
+            }
+        }
+    }
+    return 0;
+}

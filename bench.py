@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the diagonaled-matmul hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of the forward workload of the
+TVM Discuss thread "Developing a faster schedule for Longformer's kernel" (post 6: b=1,
+n=4096, h=12, hidden 768 so d=64, w=w_upper=256, 513 diagonals), at both dilations the
+thread asks for (post 4: 0 and 3):
+
+    for dilation in (0, 3):
+        S  = diagmm_qk(Q, K)                      band [1, 4096, 12, 513] f16
+        P  = diagmm_banded_softmax(S, scale 1/8)  in place
+        O  = diagmm_pv(P, V)                      [1, 4096, 12, 64] f16
+        dX = diagmm_pvT(P, dO)                    [1, 4096, 12, 64] f16
+
+Inputs are seeded synthetic tensors (Q, K, V, dO ~ N(0,1)/8 in f16), resident in HBM
+before the timed region; R rotating buffer sets (> 256 MB in total) keep one step's
+operands out of the Infinity Cache of the previous steps.  The value is the whole
+step's algorithmic HBM bytes per second (each input read once, each output written
+once; pv / pvT / softmax read only in-range band slots); useful TFLOP/s (2*d per
+in-range slot of qk, pv, pvT) is reported beside it.  The roofline object is for the
+qk kernel at dilation 0, timed with HIP events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense f16 MFMA
+
+B, N, H, D, W, WU = 1, 4096, 12, 64, 256, 256
+DILATIONS = (0, 3)
+K = W + WU + 1
+SCALE = 0.125
+E = 2  # bytes per f16 element
+
+
+def in_range_per_head(n, w, wu, dil):
+    s = max(dil, 1)
+    return sum(min(w, i // s) + min(wu, (n - 1 - i) // s) + 1 for i in range(n))
+
+
+def op_costs(dil):
+    """Algorithmic bytes and useful flops of each op at one dilation."""
+    cnt = in_range_per_head(N, W, WU, dil) * B * H
+    dense = B * N * H * D * E
+    band = B * N * H * K * E
+    return {
+        "qk": {"bytes": 2 * dense + band, "flops": 2 * D * cnt},
+        "softmax": {"bytes": cnt * E + band, "flops": 0},
+        "pv": {"bytes": cnt * E + 2 * dense, "flops": 2 * D * cnt},
+        "pvT": {"bytes": cnt * E + 2 * dense, "flops": 2 * D * cnt},
+    }
+
+
+def kernel_source_hash() -> str:
+    csrc = os.path.join(ROOT, "sliding_window_attention_diagmm_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM traffic per qk launch from the committed rocprofv3 counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "qk_f16_n4096_dil0_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for ln in open(path):
+        if ":" in ln and not ln.startswith("#"):
+            k_, v = ln.split(":", 1)
+            vals[k_.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_threads() -> int:
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_baseline(target_s: float = 12.0):
+    """The oracle on the host cores over a bounded sample of the same step: all 12 heads
+    of a set of positions, for qk, softmax, pv and pvT at both dilations."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import oracle
+
+    g = datagen.rng(77)
+    shape = (B, N, H, D)
+    q = datagen.normal(g, shape, "f16", 0.125)
+    k = datagen.normal(g, shape, "f16", 0.125)
+    v = datagen.normal(g, shape, "f16", 0.125)
+    do = datagen.normal(g, shape, "f16", 0.125)
+    probs = datagen.softmax_rows(g, (B, N, H, K), "f16")
+    threads = cpu_threads()
+
+    def run(rows):
+        qr = q.reshape(N, H, D)[torch.from_numpy(rows)]
+        for dil in DILATIONS:
+            s = oracle.qk(qr, k, W, WU, dil, 0.0, rows=rows, threads=threads)
+            p = oracle.softmax(s, W, WU, dil, SCALE, n=N, rows=rows, threads=threads)
+            oracle.pv(p, v, W, WU, dil, rows=rows, threads=threads)
+            oracle.pvT(probs, do, W, WU, dil, rows=rows, threads=threads)
+
+    probe = np.arange(0, N, N // 32, dtype=np.int64)[:32]
+    t0 = time.perf_counter()
+    run(probe)
+    t_probe = time.perf_counter() - t0
+    count = int(min(N, max(32, 32 * target_s / max(t_probe, 1e-3))))
+    rows = np.linspace(0, N - 1, count).astype(np.int64)
+    rows = np.unique(rows)
+    t0 = time.perf_counter()
+    run(rows)
+    dt = time.perf_counter() - t0
+    total_bytes = sum(c["bytes"] for dil in DILATIONS for c in op_costs(dil).values())
+    frac = len(rows) / N
+    return {
+        "value": round(total_bytes * frac / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(rows)} of {N} positions (all {H} heads), qk+softmax+pv+pvT at "
+                   f"dilation 0 and 3, {dt:.1f} s wall on {threads} threads; bytes scaled "
+                   f"by the sampled fraction of rows"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards over batch*heads with no communication, but no multi-GPU "
+              "run is part of it.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import datagen
+    import sliding_window_attention_diagmm_amd as dm
+
+    dm.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    sets = []
+    for r in range(args.sets):
+        g = datagen.rng(1000 + r)
+        t = {n_: datagen.normal(g, (B, N, H, D), "f16", 0.125).to(dev) for n_ in ("q", "k", "v", "do")}
+        for dil in DILATIONS:
+            t[f"S{dil}"] = torch.empty((B, N, H, K), dtype=torch.float16, device=dev)
+            t[f"O{dil}"] = torch.empty((B, N, H, D), dtype=torch.float16, device=dev)
+            t[f"X{dil}"] = torch.empty((B, N, H, D), dtype=torch.float16, device=dev)
+        sets.append(t)
+    torch.cuda.synchronize()
+
+    ops = [(dil, op) for dil in DILATIONS for op in ("qk", "softmax", "pv", "pvT")]
+    events = {key: [] for key in ops}
+
+    def step(t, record):
+        for dil in DILATIONS:
+            S = t[f"S{dil}"]
+            for op in ("qk", "softmax", "pv", "pvT"):
+                if record:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                if op == "qk":
+                    dm.diagmm_qk(t["q"], t["k"], W, WU, dil, 0.0, out=S)
+                elif op == "softmax":
+                    dm.diagmm_banded_softmax(S, W, WU, dil, SCALE, inplace=True)
+                elif op == "pv":
+                    dm.diagmm_pv(S, t["v"], W, WU, dil, out=t[f"O{dil}"])
+                else:
+                    dm.diagmm_pvT(S, t["do"], W, WU, dil, out=t[f"X{dil}"])
+                if record:
+                    e1.record(stream)
+                    events[(dil, op)].append((e0, e1))
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)], False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % len(sets)], True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per_op = {}
+    step_bytes = step_flops = 0
+    for (dil, op) in ops:
+        ms = sum(a.elapsed_time(b_) for a, b_ in events[(dil, op)]) / len(events[(dil, op)])
+        c = op_costs(dil)[op]
+        step_bytes += c["bytes"]
+        step_flops += c["flops"]
+        per_op[f"{op}_dil{dil}"] = {
+            "us": round(ms * 1e3, 2),
+            "GB/s": round(c["bytes"] / (ms * 1e-3) / 1e9, 1),
+            "TFLOP/s": round(c["flops"] / (ms * 1e-3) / 1e12, 2),
+            "kernel": dm.diagmm_plan(op, B, N, H, D, W, WU, dil, torch.float16)["kernel"],
+        }
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    qk_us = per_op["qk_dil0"]["us"]
+    qk_bytes = op_costs(0)["qk"]["bytes"]
+    achieved = qk_bytes / (qk_us * 1e-6) / 1e9
+    traffic = load_traffic()
+
+    line = {
+        "metric": "diagmm_qk/pv TFLOP/s + HBM GB/s (% roofline), n=4096 w=256 h=12 d=64, dil 0/3",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "longformer_fwd_n4096_w256_h12_d64_dil0+dil3",
+                   "b": B, "n": N, "h": H, "d": D, "w": W, "w_upper": WU,
+                   "dilations": list(DILATIONS), "ops": ["qk", "softmax", "pv", "pvT"],
+                   "step_bytes": step_bytes, "step_useful_flops": step_flops,
+                   "rotating_sets": args.sets},
+        "tflops": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "per_op": per_op,
+        "roofline": {"kernel": per_op["qk_dil0"]["kernel"], "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": qk_bytes,
+                     "avg_launch_us": qk_us},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+/*
+ * libdiagmm - the Longformer "diagonaled matmul" family on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (TVM Discuss, "Developing a faster schedule for Longformer's kernel",
+ * post 1): a banded matrix product that evaluates only selected diagonals of Q.K^T -
+ * a sliding window of w diagonals to the left of the main one and w_upper to the right
+ * (post 5), optionally dilated, i.e. with gaps between the selected diagonals
+ * (post 3; 0 means no gaps).  Post 6 lists one forward function (result last
+ * dimension 2w+1) and two backward functions selected by transpose_t1, whose first
+ * operand is the band.  This library has one call per function, plus the attention
+ * softmax that sits between the forward calls (csarofeen/pytorch issue 2096, first
+ * fusion repro: scale, row max, subtract, exp, row sum, divide).
+ *
+ * Notation used below
+ *   b, n, h, d   batch, sequence length, heads, head dimension
+ *   w, w_upper   diagonals to the left / right of the main one (w_upper "should be 0 or
+ *                w" on the pages; any value >= 0 is accepted)
+ *   K            w + w_upper + 1, slots per band row
+ *   s            max(dilation, 1): dilation 0 and 1 both select contiguous diagonals;
+ *                dilation 3 selects every third one
+ *   j(i, k)      i + (k - w) * s, the key position of slot k of row i.  Slot w is the
+ *                main diagonal; slots below w look left, slots above look right.  A slot
+ *                is in range when 0 <= j(i, k) < n.
+ *
+ * Layouts (all row-major and contiguous, element offsets are 64-bit)
+ *   dense   [b][n][h][d]   (Q, K, V, X, dense outputs)
+ *   band    [b][n][h][K]
+ *
+ * Types: inputs are f32, f16 or bf16 (both operands of one call share the type);
+ * outputs are the input type or f32.  Products accumulate in f32 and are rounded
+ * once, to nearest even, into the output type.
+ *
+ * Ownership and streams: every pointer is a device pointer owned by the caller.  The
+ * library never allocates, frees or synchronises; each call only enqueues kernels on
+ * `stream` (a hipStream_t; NULL is the default stream) and returns.  Calls are
+ * thread-safe; the only state is the calling thread's last-error text.
+ *
+ * Errors: every call returns a diagmm_status_t and never aborts.  On any status other
+ * than DIAGMM_OK nothing has been enqueued, except DIAGMM_ERR_HIP, which reports a
+ * failed launch (the text from the HIP runtime is in diagmm_last_error()).  A call
+ * with b * n * h == 0 returns DIAGMM_OK and enqueues nothing.
+ */
+#ifndef DIAGMM_H
+#define DIAGMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIAGMM_ABI_VERSION 1
+
+typedef enum {
+    DIAGMM_F32 = 0,
+    DIAGMM_F16 = 1,
+    DIAGMM_BF16 = 2
+} diagmm_dtype_t;
+
+typedef enum {
+    DIAGMM_OK = 0,
+    DIAGMM_ERR_NULL = 1,        /* a required pointer is NULL */
+    DIAGMM_ERR_SHAPE = 2,       /* negative size, d < 1, or an element count past int64 */
+    DIAGMM_ERR_DTYPE = 3,       /* unknown dtype, or an unsupported in/out pair */
+    DIAGMM_ERR_ALIAS = 4,       /* the output overlaps an input */
+    DIAGMM_ERR_UNSUPPORTED = 5, /* valid arguments this build cannot run */
+    DIAGMM_ERR_HIP = 6          /* the HIP runtime rejected a launch */
+} diagmm_status_t;
+
+/*
+ * diagmm_qk - the forward function (post 6: t1 = Q, t2 = K, t3 = result, t3d3 = 2w+1).
+ *   band[bb,i,hh,k] = sum_c q[bb,i,hh,c] * k[bb,j(i,k),hh,c]   for in-range slots,
+ *   band[bb,i,hh,k] = padding_value                             otherwise.
+ * q, k      dense [b][n][h][d] of in_dtype (read only)
+ * band      band  [b][n][h][K] of out_dtype (written in full)
+ * padding_value is rounded once (nearest even) to out_dtype and stored bit-exactly in
+ * every out-of-range slot ("padding: any const", posts 5 and 6); -inf and -0.0 allowed.
+ * The band must not overlap q or k (DIAGMM_ERR_ALIAS).
+ */
+diagmm_status_t diagmm_qk(const void* q, const void* k, void* band, int64_t b, int64_t n,
+                          int64_t h, int64_t d, int64_t w, int64_t w_upper, int64_t dilation,
+                          float padding_value, diagmm_dtype_t in_dtype,
+                          diagmm_dtype_t out_dtype, void* stream);
+
+/*
+ * diagmm_pv - backward function with transpose_t1 = 0 (post 6: t1 is the band, last
+ * dimension 2w+1); in the forward pass it is probabilities times V.
+ *   out[bb,i,hh,c] = sum over in-range slots k of band[bb,i,hh,k] * v[bb,j(i,k),hh,c]
+ * band      band  [b][n][h][K] of in_dtype; out-of-range slots are never read into the
+ *           sum (skipped by index, so NaN or garbage there has no effect)
+ * v         dense [b][n][h][d] of in_dtype
+ * out       dense [b][n][h][d] of out_dtype (written in full)
+ * padding_value is accepted for a uniform signature and ignored.
+ */
+diagmm_status_t diagmm_pv(const void* band, const void* v, void* out, int64_t b, int64_t n,
+                          int64_t h, int64_t d, int64_t w, int64_t w_upper, int64_t dilation,
+                          float padding_value, diagmm_dtype_t in_dtype,
+                          diagmm_dtype_t out_dtype, void* stream);
+
+/*
+ * diagmm_pvT - backward function with transpose_t1 = 1 (post 6): the band is used
+ * transposed, as for the gradients of K and V.
+ *   out[bb,j,hh,c] = sum over (i, k) with j(i,k) = j of band[bb,i,hh,k] * x[bb,i,hh,c]
+ * (for each j and k the only candidate is i = j - (k - w) * s, taken when 0 <= i < n).
+ * band, x, out, padding_value: as for diagmm_pv.
+ */
+diagmm_status_t diagmm_pvT(const void* band, const void* x, void* out, int64_t b, int64_t n,
+                           int64_t h, int64_t d, int64_t w, int64_t w_upper,
+                           int64_t dilation, float padding_value, diagmm_dtype_t in_dtype,
+                           diagmm_dtype_t out_dtype, void* stream);
+
+/*
+ * diagmm_banded_softmax - attention softmax over each band row (issue 2096 recipe).
+ *   x_k = scale * scores[bb,i,hh,k] for in-range slots, -inf for the others;
+ *   probs[bb,i,hh,k] = exp(x_k - max_k x) / sum_k exp(x_k - max_k x).
+ * Out-of-range slots become exactly +0.  Every row holds slot w (key i), so no row is
+ * empty.  scores and probs are band [b][n][h][K]; probs may be the same pointer as
+ * scores (in place) when in_dtype == out_dtype; any other overlap is DIAGMM_ERR_ALIAS.
+ */
+diagmm_status_t diagmm_banded_softmax(const void* scores, void* probs, int64_t b, int64_t n,
+                                      int64_t h, int64_t w, int64_t w_upper,
+                                      int64_t dilation, float scale, diagmm_dtype_t in_dtype,
+                                      diagmm_dtype_t out_dtype, void* stream);
+
+/* Static text for a status code. */
+const char* diagmm_status_string(diagmm_status_t status);
+
+/* Detail of the calling thread's most recent failure ("" if none). */
+const char* diagmm_last_error(void);
+
+/* DIAGMM_ABI_VERSION of the loaded library. */
+int diagmm_abi_version(void);
+
+/*
+ * Band-tile scheduler introspection (host only, no device access).  Describes how a
+ * call with these arguments is cut into workgroups: which kernel runs, the tile shape
+ * (rows per tile, slots per tile), how many tiles and workgroups, the LDS bytes per
+ * workgroup, and how many residue classes the dilation splits the rows into.
+ * mode: 0 = qk, 1 = pv, 2 = pvT, 3 = banded softmax.  Returns DIAGMM_ERR_SHAPE /
+ * DIAGMM_ERR_DTYPE for invalid arguments, as the compute calls would.
+ */
+typedef struct {
+    char kernel[48];        /* kernel family chosen, e.g. "qk_mfma_f16" or "qk_simple" */
+    int64_t rows_per_tile;  /* output rows per tile (per residue class) */
+    int64_t slots_per_tile; /* band slots (or dense columns) per tile */
+    int64_t tiles;          /* total tiles */
+    int64_t workgroups;     /* workgroups launched */
+    int64_t threads;        /* threads per workgroup */
+    int64_t lds_bytes;      /* LDS per workgroup */
+    int64_t residues;       /* residue classes the rows are split into (s) */
+} diagmm_plan_t;
+
+diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,
+                            int64_t w_upper, int64_t dilation, diagmm_dtype_t in_dtype,
+                            diagmm_dtype_t out_dtype, diagmm_plan_t* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIAGMM_H */

@@ -1,0 +1,218 @@
+"""Python binding of libdiagmm (the Longformer diagonaled matmul family on MI355X).
+
+Argument marshalling only: every call checks the torch tensors it is given (device,
+dtype, contiguity, shape), allocates the output with torch when none is passed, and
+hands raw device pointers, sizes and torch's current HIP stream to the C ABI in
+``libdiagmm.so`` (declared in ``include/diagmm.h``).  All arithmetic runs in the HIP
+kernels of that library; there is no CPU or PyTorch fallback - if the library is
+missing or fails to load, importing the ops raises.
+
+Operations (TVM Discuss, "Developing a faster schedule for Longformer's kernel": the
+banded product of post 1, parameters of post 5, forward / two backward functions of
+post 6), with ``K = w + w_upper + 1`` and stride ``s = max(dilation, 1)``:
+
+* ``diagmm_qk(q, k, w, ...)``   -> band ``[b, n, h, K]``: Q.K^T on the selected diagonals
+* ``diagmm_pv(band, v, w, ...)`` -> ``[b, n, h, d]``: band times V (transpose_t1 = 0)
+* ``diagmm_pvT(band, x, w, ...)``-> ``[b, n, h, d]``: transposed band times X (transpose_t1 = 1)
+* ``diagmm_banded_softmax(scores, w, ...)`` -> probabilities over each band row
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax", "diagmm_plan",
+           "diagmm_abi_version", "library_path", "load", "DiagmmError"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdiagmm.so")
+
+_DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+MODES = {"qk": 0, "pv": 1, "pvT": 2, "softmax": 3}
+
+
+class DiagmmError(RuntimeError):
+    """A libdiagmm call returned a status other than DIAGMM_OK."""
+
+    def __init__(self, status: int, text: str):
+        super().__init__(text)
+        self.status = status
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char * 48), ("rows_per_tile", ctypes.c_int64),
+                ("slots_per_tile", ctypes.c_int64), ("tiles", ctypes.c_int64),
+                ("workgroups", ctypes.c_int64), ("threads", ctypes.c_int64),
+                ("lds_bytes", ctypes.c_int64), ("residues", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libdiagmm.so (built in-tree by build.py).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libdiagmm.so not built at {_LIB_PATH}; run "
+                          "`python sliding_window_attention_diagmm_amd/build.py`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, f32, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    for name in ("diagmm_qk", "diagmm_pv", "diagmm_pvT"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp] + [i64] * 7 + [f32, ci, ci, vp]
+        fn.restype = ci
+    lib.diagmm_banded_softmax.argtypes = [vp, vp] + [i64] * 6 + [f32, ci, ci, vp]
+    lib.diagmm_banded_softmax.restype = ci
+    lib.diagmm_status_string.argtypes = [ci]
+    lib.diagmm_status_string.restype = ctypes.c_char_p
+    lib.diagmm_last_error.argtypes = []
+    lib.diagmm_last_error.restype = ctypes.c_char_p
+    lib.diagmm_abi_version.argtypes = []
+    lib.diagmm_abi_version.restype = ci
+    lib.diagmm_plan.argtypes = [ci] + [i64] * 7 + [ci, ci, ctypes.POINTER(_Plan)]
+    lib.diagmm_plan.restype = ci
+    _lib = lib
+    return lib
+
+
+def _raise(lib, st: int):
+    text = lib.diagmm_last_error().decode() or lib.diagmm_status_string(st).decode()
+    raise DiagmmError(st, text)
+
+
+def diagmm_abi_version() -> int:
+    return load().diagmm_abi_version()
+
+
+def _dense(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if t.dtype not in _DT:
+        raise TypeError(f"{name} has unsupported dtype {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _out(out, shape, dtype, device, name="out"):
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _dense(out, name)
+    if tuple(out.shape) != tuple(shape) or out.dtype != dtype or out.device != device:
+        raise ValueError(f"{name} must be {tuple(shape)} {dtype} on {device}")
+    return out
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _window(w, w_upper, dilation):
+    if w_upper is None:
+        w_upper = w
+    for name, v in (("w", w), ("w_upper", w_upper), ("dilation", dilation)):
+        if int(v) != v or v < 0:
+            raise ValueError(f"{name} must be a non-negative integer (got {v})")
+    return int(w), int(w_upper), int(dilation)
+
+
+def diagmm_qk(q, k, w, w_upper=None, dilation=0, padding_value=0.0, out_dtype=None, out=None):
+    """band[b,i,h,kk] = <q[b,i,h,:], k[b,i+(kk-w)*s,h,:]>, padding_value where that key
+    position is outside [0, n).  Returns ``[b, n, h, w + w_upper + 1]``."""
+    lib = load()
+    w, w_upper, dilation = _window(w, w_upper, dilation)
+    q, k = _dense(q, "q"), _dense(k, "k")
+    if q.shape != k.shape or q.dtype != k.dtype or q.device != k.device:
+        raise ValueError("q and k must have the same shape, dtype and device")
+    b, n, h, d = q.shape
+    out_dtype = out_dtype or q.dtype
+    band = _out(out, (b, n, h, w + w_upper + 1), out_dtype, q.device)
+    st = lib.diagmm_qk(q.data_ptr(), k.data_ptr(), band.data_ptr(), b, n, h, d, w, w_upper,
+                       dilation, float(padding_value), _DT[q.dtype], _DT[out_dtype],
+                       _stream(q.device))
+    if st:
+        _raise(lib, st)
+    return band
+
+
+def _pv_like(fn_name, band, x, w, w_upper, dilation, out_dtype, out):
+    lib = load()
+    w, w_upper, dilation = _window(w, w_upper, dilation)
+    band, x = _dense(band, "band"), _dense(x, "x")
+    b, n, h, d = x.shape
+    K = w + w_upper + 1
+    if tuple(band.shape) != (b, n, h, K):
+        raise ValueError(f"band must be {(b, n, h, K)}, got {tuple(band.shape)}")
+    if band.dtype != x.dtype or band.device != x.device:
+        raise ValueError("band and the dense operand must share dtype and device")
+    out_dtype = out_dtype or x.dtype
+    res = _out(out, (b, n, h, d), out_dtype, x.device)
+    st = getattr(lib, fn_name)(band.data_ptr(), x.data_ptr(), res.data_ptr(), b, n, h, d, w,
+                               w_upper, dilation, 0.0, _DT[x.dtype], _DT[out_dtype],
+                               _stream(x.device))
+    if st:
+        _raise(lib, st)
+    return res
+
+
+def diagmm_pv(band, v, w, w_upper=None, dilation=0, out_dtype=None, out=None):
+    """out[b,i,h,:] = sum over in-range slots kk of band[b,i,h,kk] * v[b,i+(kk-w)*s,h,:]."""
+    return _pv_like("diagmm_pv", band, v, w, w_upper, dilation, out_dtype, out)
+
+
+def diagmm_pvT(band, x, w, w_upper=None, dilation=0, out_dtype=None, out=None):
+    """out[b,j,h,:] = sum over (i, kk) with i+(kk-w)*s = j of band[b,i,h,kk] * x[b,i,h,:]."""
+    return _pv_like("diagmm_pvT", band, x, w, w_upper, dilation, out_dtype, out)
+
+
+def diagmm_banded_softmax(scores, w, w_upper=None, dilation=0, scale=1.0, out_dtype=None,
+                          out=None, inplace=False):
+    """Softmax of scale * scores over each band row's in-range slots; out-of-range slots
+    get exactly 0.  ``inplace=True`` overwrites ``scores`` (same dtype only)."""
+    lib = load()
+    w, w_upper, dilation = _window(w, w_upper, dilation)
+    s = _dense(scores, "scores")
+    b, n, h, K = s.shape
+    if K != w + w_upper + 1:
+        raise ValueError(f"scores last dim {K} != w + w_upper + 1 = {w + w_upper + 1}")
+    out_dtype = out_dtype or s.dtype
+    if inplace:
+        if out is not None or out_dtype != s.dtype:
+            raise ValueError("inplace softmax writes scores itself (same dtype)")
+        res = s
+    else:
+        res = _out(out, s.shape, out_dtype, s.device)
+    st = lib.diagmm_banded_softmax(s.data_ptr(), res.data_ptr(), b, n, h, w, w_upper, dilation,
+                                   float(scale), _DT[s.dtype], _DT[out_dtype], _stream(s.device))
+    if st:
+        _raise(lib, st)
+    return res
+
+
+def diagmm_plan(mode, b, n, h, d, w, w_upper=None, dilation=0, in_dtype=torch.float16,
+                out_dtype=None) -> dict:
+    """The band-tile scheduler's plan for a call (host only; no GPU needed)."""
+    lib = load()
+    w, w_upper, dilation = _window(w, w_upper, dilation)
+    out_dtype = out_dtype or in_dtype
+    pl = _Plan()
+    st = lib.diagmm_plan(MODES.get(mode, mode), b, n, h, d, w, w_upper, dilation,
+                         _DT[in_dtype], _DT[out_dtype], ctypes.byref(pl))
+    if st:
+        _raise(lib, st)
+    return {"kernel": pl.kernel.decode(), "rows_per_tile": pl.rows_per_tile,
+            "slots_per_tile": pl.slots_per_tile, "tiles": pl.tiles,
+            "workgroups": pl.workgroups, "threads": pl.threads, "lds_bytes": pl.lds_bytes,
+            "residues": pl.residues}

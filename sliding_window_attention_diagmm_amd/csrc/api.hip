@@ -1,0 +1,252 @@
+// The C ABI of libdiagmm: argument validation, dtype checks, alias checks, the
+// band-tile scheduler's choice of kernel, and error reporting.  Declarations and the
+// contract of every entry point are in include/diagmm.h.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/diagmm.h"
+#include "launch.hpp"
+#include "sched.hpp"
+
+namespace diagmm {
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+diagmm_status_t fail(diagmm_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+diagmm_status_t fail(diagmm_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+diagmm_status_t ok() {
+    g_last_error[0] = '\0';
+    return DIAGMM_OK;
+}
+
+constexpr int64_t kLimit = int64_t(1) << 62;
+
+// a * b without overflow past kLimit; returns -1 on overflow (all operands >= 0).
+int64_t mul_checked(int64_t a, int64_t b) {
+    if (a == 0 || b == 0) return 0;
+    if (a > kLimit / b) return -1;
+    return a * b;
+}
+
+size_t elem_size(int dt) { return dt == kF32 ? 4 : 2; }
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+// Shared checks of the four calls.  Fills p and the element counts of the dense and band
+// tensors; returns DIAGMM_OK, or the status to return.
+diagmm_status_t check_common(const char* fn, int64_t b, int64_t n, int64_t h, int64_t d,
+                             int64_t w, int64_t wu, int64_t dil, int in_dt, int out_dt,
+                             Problem* p, int64_t* dense_elems, int64_t* band_elems) {
+    if (b < 0 || n < 0 || h < 0 || w < 0 || wu < 0 || dil < 0)
+        return fail(DIAGMM_ERR_SHAPE, "%s: negative size (b=%lld n=%lld h=%lld w=%lld "
+                    "w_upper=%lld dilation=%lld)", fn, (long long)b, (long long)n, (long long)h,
+                    (long long)w, (long long)wu, (long long)dil);
+    if (d < 1) return fail(DIAGMM_ERR_SHAPE, "%s: d must be >= 1 (got %lld)", fn, (long long)d);
+    if (w >= kLimit / 4 || wu >= kLimit / 4 || dil >= kLimit / 4)
+        return fail(DIAGMM_ERR_SHAPE, "%s: window or dilation too large", fn);
+    const int64_t s = dil > 1 ? dil : 1;
+    if (mul_checked(w + 1, s) < 0 || mul_checked(wu + 1, s) < 0 || mul_checked(w + 1, s) > kLimit / 4 ||
+        mul_checked(wu + 1, s) > kLimit / 4)
+        return fail(DIAGMM_ERR_SHAPE, "%s: window times dilation overflows", fn);
+    if (in_dt < kF32 || in_dt > kBF16 || out_dt < kF32 || out_dt > kBF16)
+        return fail(DIAGMM_ERR_DTYPE, "%s: unknown dtype code (in=%d out=%d)", fn, in_dt, out_dt);
+    if (!(out_dt == in_dt || out_dt == kF32))
+        return fail(DIAGMM_ERR_DTYPE, "%s: output dtype must be the input dtype or f32", fn);
+    const int64_t K = w + wu + 1;
+    const int64_t rows = mul_checked(mul_checked(b, n), h);
+    const int64_t de = rows < 0 ? -1 : mul_checked(rows, d);
+    const int64_t be = rows < 0 ? -1 : mul_checked(rows, K);
+    if (rows < 0 || de < 0 || be < 0 || be > kLimit / 8 || de > kLimit / 8)
+        return fail(DIAGMM_ERR_SHAPE, "%s: element count overflows int64", fn);
+    *p = Problem{b, n, h, d, w, wu, s, K};
+    *dense_elems = de;
+    *band_elems = be;
+    return DIAGMM_OK;
+}
+
+diagmm_status_t launched(const char* fn, hipError_t e) {
+    if (e != hipSuccess) return fail(DIAGMM_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+// Round-to-nearest-even of a float into the 16-bit types, on the host.
+uint32_t pad_bits(float value, int out_dtype) {
+    uint32_t u;
+    std::memcpy(&u, &value, sizeof u);
+    if (out_dtype == kF32) return u;
+    const uint32_t sign = (u >> 16) & 0x8000u;
+    const uint32_t mag = u & 0x7fffffffu;
+    if (out_dtype == kBF16) {
+        if (mag > 0x7f800000u) return sign | 0x7fc0u;
+        return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    }
+    // binary16
+    if (mag > 0x7f800000u) return sign | 0x7e00u;         // NaN
+    if (mag >= 0x477ff000u) return sign | 0x7c00u;        // >= 65520 rounds to infinity
+    if (mag < 0x33000000u) return sign;                   // < 2^-25 rounds to zero
+    const int exp = static_cast<int>(mag >> 23) - 127;
+    uint32_t mant = (mag & 0x7fffffu) | 0x800000u;        // 24-bit significand
+    int shift;                                            // bits to drop
+    uint32_t base;
+    if (exp < -14) {                                      // half subnormal: quantum 2^-24
+        shift = -exp - 1;                                 // value = mant * 2^(exp-23)
+        base = 0;
+    } else {
+        shift = 13;
+        base = static_cast<uint32_t>(exp + 15) << 10;
+        mant &= 0x7fffffu;
+        mant |= 0x800000u;
+    }
+    uint32_t kept = mant >> shift;
+    const uint32_t rem = mant & ((1u << shift) - 1u);
+    const uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (kept & 1u))) ++kept;
+    if (exp < -14) return sign | kept;                    // may carry into 0x400: smallest normal
+    return sign | (base + (kept - 0x400u));               // kept in [0x400, 0x800]: carry bumps exp
+}
+
+}  // namespace diagmm
+
+using namespace diagmm;
+
+extern "C" {
+
+int diagmm_abi_version(void) { return DIAGMM_ABI_VERSION; }
+
+const char* diagmm_last_error(void) { return g_last_error; }
+
+const char* diagmm_status_string(diagmm_status_t st) {
+    switch (st) {
+    case DIAGMM_OK: return "ok";
+    case DIAGMM_ERR_NULL: return "null pointer";
+    case DIAGMM_ERR_SHAPE: return "invalid shape";
+    case DIAGMM_ERR_DTYPE: return "unsupported dtype";
+    case DIAGMM_ERR_ALIAS: return "output overlaps an input";
+    case DIAGMM_ERR_UNSUPPORTED: return "unsupported arguments";
+    case DIAGMM_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+diagmm_status_t diagmm_qk(const void* q, const void* k, void* band, int64_t b, int64_t n,
+                          int64_t h, int64_t d, int64_t w, int64_t w_upper, int64_t dilation,
+                          float padding_value, diagmm_dtype_t in_dtype,
+                          diagmm_dtype_t out_dtype, void* stream) {
+    Problem p;
+    int64_t de, be;
+    diagmm_status_t st = check_common("diagmm_qk", b, n, h, d, w, w_upper, dilation, in_dtype,
+                                      out_dtype, &p, &de, &be);
+    if (st != DIAGMM_OK) return st;
+    if (p.rows() * p.h == 0) return ok();
+    if (!q || !k || !band) return fail(DIAGMM_ERR_NULL, "diagmm_qk: null pointer");
+    const int64_t dbytes = de * elem_size(in_dtype), bbytes = be * elem_size(out_dtype);
+    if (overlaps(band, bbytes, q, dbytes) || overlaps(band, bbytes, k, dbytes))
+        return fail(DIAGMM_ERR_ALIAS, "diagmm_qk: band overlaps q or k");
+    const uint32_t pad = pad_bits(padding_value, out_dtype);
+    const Plan plan = plan_qk(p, in_dtype, out_dtype);
+    return launched("diagmm_qk", run_qk(plan, q, k, band, p, in_dtype, out_dtype, pad,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+static diagmm_status_t pv_like(const char* fn, int mode, const void* band, const void* x,
+                               void* out, int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,
+                               int64_t w_upper, int64_t dilation, int in_dtype, int out_dtype,
+                               void* stream) {
+    Problem p;
+    int64_t de, be;
+    diagmm_status_t st = check_common(fn, b, n, h, d, w, w_upper, dilation, in_dtype, out_dtype,
+                                      &p, &de, &be);
+    if (st != DIAGMM_OK) return st;
+    if (p.rows() * p.h == 0) return ok();
+    if (!band || !x || !out) return fail(DIAGMM_ERR_NULL, "%s: null pointer", fn);
+    const int64_t obytes = de * elem_size(out_dtype);
+    if (overlaps(out, obytes, band, be * elem_size(in_dtype)) ||
+        overlaps(out, obytes, x, de * elem_size(in_dtype)))
+        return fail(DIAGMM_ERR_ALIAS, "%s: output overlaps an input", fn);
+    const Plan plan = mode == 1 ? plan_pv(p, in_dtype, out_dtype) : plan_pvT(p, in_dtype, out_dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return launched(fn, mode == 1 ? run_pv(plan, band, x, out, p, in_dtype, out_dtype, s)
+                                  : run_pvT(plan, band, x, out, p, in_dtype, out_dtype, s));
+}
+
+diagmm_status_t diagmm_pv(const void* band, const void* v, void* out, int64_t b, int64_t n,
+                          int64_t h, int64_t d, int64_t w, int64_t w_upper, int64_t dilation,
+                          float padding_value, diagmm_dtype_t in_dtype,
+                          diagmm_dtype_t out_dtype, void* stream) {
+    (void)padding_value;
+    return pv_like("diagmm_pv", 1, band, v, out, b, n, h, d, w, w_upper, dilation, in_dtype,
+                   out_dtype, stream);
+}
+
+diagmm_status_t diagmm_pvT(const void* band, const void* x, void* out, int64_t b, int64_t n,
+                           int64_t h, int64_t d, int64_t w, int64_t w_upper,
+                           int64_t dilation, float padding_value, diagmm_dtype_t in_dtype,
+                           diagmm_dtype_t out_dtype, void* stream) {
+    (void)padding_value;
+    return pv_like("diagmm_pvT", 2, band, x, out, b, n, h, d, w, w_upper, dilation, in_dtype,
+                   out_dtype, stream);
+}
+
+diagmm_status_t diagmm_banded_softmax(const void* scores, void* probs, int64_t b, int64_t n,
+                                      int64_t h, int64_t w, int64_t w_upper,
+                                      int64_t dilation, float scale, diagmm_dtype_t in_dtype,
+                                      diagmm_dtype_t out_dtype, void* stream) {
+    Problem p;
+    int64_t de, be;
+    diagmm_status_t st = check_common("diagmm_banded_softmax", b, n, h, 1, w, w_upper, dilation,
+                                      in_dtype, out_dtype, &p, &de, &be);
+    if (st != DIAGMM_OK) return st;
+    if (p.rows() * p.h == 0) return ok();
+    if (!scores || !probs) return fail(DIAGMM_ERR_NULL, "diagmm_banded_softmax: null pointer");
+    const bool in_place = scores == probs && in_dtype == out_dtype;
+    if (!in_place && overlaps(probs, be * elem_size(out_dtype), scores, be * elem_size(in_dtype)))
+        return fail(DIAGMM_ERR_ALIAS, "diagmm_banded_softmax: probs overlaps scores (only "
+                    "exact in-place with equal dtypes is allowed)");
+    const Plan plan = plan_softmax(p, in_dtype, out_dtype);
+    return launched("diagmm_banded_softmax",
+                    run_softmax(plan, scores, probs, p, scale, in_dtype, out_dtype,
+                                static_cast<hipStream_t>(stream)));
+}
+
+diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,
+                            int64_t w_upper, int64_t dilation, diagmm_dtype_t in_dtype,
+                            diagmm_dtype_t out_dtype, diagmm_plan_t* out) {
+    if (!out) return fail(DIAGMM_ERR_NULL, "diagmm_plan: null plan pointer");
+    if (mode < 0 || mode > 3) return fail(DIAGMM_ERR_UNSUPPORTED, "diagmm_plan: mode %d", mode);
+    Problem p;
+    int64_t de, be;
+    diagmm_status_t st = check_common("diagmm_plan", b, n, h, mode == 3 ? 1 : d, w, w_upper,
+                                      dilation, in_dtype, out_dtype, &p, &de, &be);
+    if (st != DIAGMM_OK) return st;
+    Plan plan = mode == 0 ? plan_qk(p, in_dtype, out_dtype)
+              : mode == 1 ? plan_pv(p, in_dtype, out_dtype)
+              : mode == 2 ? plan_pvT(p, in_dtype, out_dtype)
+                          : plan_softmax(p, in_dtype, out_dtype);
+    std::memset(out, 0, sizeof *out);
+    std::snprintf(out->kernel, sizeof out->kernel, "%s", plan.kernel);
+    out->rows_per_tile = plan.rows_per_tile;
+    out->slots_per_tile = plan.slots_per_tile;
+    out->tiles = plan.tiles;
+    out->workgroups = plan.workgroups;
+    out->threads = plan.threads;
+    out->lds_bytes = plan.lds_bytes;
+    out->residues = plan.residues;
+    return ok();
+}
+
+}  // extern "C"

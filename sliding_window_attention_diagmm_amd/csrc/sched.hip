@@ -1,0 +1,94 @@
+// Band-tile scheduler (see sched.hpp).
+#include <cstdlib>
+#include <cstring>
+
+#include "launch.hpp"
+#include "sched.hpp"
+
+namespace diagmm {
+
+namespace {
+
+// DIAGMM_KERNEL=simple forces the element-per-thread kernels (a debugging and
+// comparison switch; the default picks the tiled kernels where they apply).
+bool force_simple() {
+    const char* e = std::getenv("DIAGMM_KERNEL");
+    return e && std::strcmp(e, "simple") == 0;
+}
+
+Plan simple_plan(const Problem& p, int64_t cols, const char* name) {
+    Plan pl;
+    pl.family = Family::kSimple;
+    pl.kernel = name;
+    pl.rows_per_tile = 1;
+    pl.slots_per_tile = 1;
+    pl.tiles = p.rows() * p.h * cols;
+    const int64_t blocks = (pl.tiles + 255) / 256;
+    pl.workgroups = blocks < (int64_t(1) << 20) ? blocks : (int64_t(1) << 20);
+    pl.threads = 256;
+    pl.lds_bytes = 0;
+    pl.residues = 1;
+    return pl;
+}
+
+}  // namespace
+
+Plan plan_qk(const Problem& p, int in_dt, int out_dt) {
+    (void)in_dt;
+    (void)out_dt;
+    (void)force_simple;
+    return simple_plan(p, p.K, "qk_simple");
+}
+
+Plan plan_pv(const Problem& p, int in_dt, int out_dt) {
+    (void)in_dt;
+    (void)out_dt;
+    return simple_plan(p, p.d, "pv_simple");
+}
+
+Plan plan_pvT(const Problem& p, int in_dt, int out_dt) {
+    (void)in_dt;
+    (void)out_dt;
+    return simple_plan(p, p.d, "pvT_simple");
+}
+
+Plan plan_softmax(const Problem& p, int in_dt, int out_dt) {
+    (void)in_dt;
+    (void)out_dt;
+    Plan pl;
+    pl.family = Family::kSoftmaxRow;
+    pl.kernel = "softmax_rows";
+    pl.rows_per_tile = 1;
+    pl.slots_per_tile = p.K;
+    pl.tiles = p.rows() * p.h;
+    pl.workgroups = pl.tiles < (int64_t(1) << 20) ? pl.tiles : (int64_t(1) << 20);
+    pl.threads = 256;
+    pl.lds_bytes = 16;
+    return pl;
+}
+
+hipError_t run_qk(const Plan& plan, const void* q, const void* k, void* band, const Problem& p,
+                  int in_dt, int out_dt, uint32_t pad, hipStream_t stream) {
+    (void)plan;
+    return launch_qk_simple(q, k, band, p, in_dt, out_dt, pad, stream);
+}
+
+hipError_t run_pv(const Plan& plan, const void* band, const void* v, void* out, const Problem& p,
+                  int in_dt, int out_dt, hipStream_t stream) {
+    (void)plan;
+    return launch_pv_simple(band, v, out, p, in_dt, out_dt, stream);
+}
+
+hipError_t run_pvT(const Plan& plan, const void* band, const void* x, void* out,
+                   const Problem& p, int in_dt, int out_dt, hipStream_t stream) {
+    (void)plan;
+    return launch_pvT_simple(band, x, out, p, in_dt, out_dt, stream);
+}
+
+hipError_t run_softmax(const Plan& plan, const void* scores, void* probs, const Problem& p,
+                       float scale, int in_dt, int out_dt, hipStream_t stream) {
+    (void)plan;
+    return launch_softmax_rows(scores, probs, p, scale, in_dt, out_dt, stream);
+}
+
+}  // namespace diagmm

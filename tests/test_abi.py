@@ -1,0 +1,131 @@
+"""The C ABI of libdiagmm on the host (no GPU needed, no kernel is launched).
+
+Checks that the library loads, exports every entry point include/diagmm.h declares,
+rejects bad arguments with the documented status before touching the device, treats
+empty problems as no-ops, and that the band-tile scheduler's plans cover the work.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import sliding_window_attention_diagmm_amd as dm
+from sliding_window_attention_diagmm_amd import build as dmbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "diagmm.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIAS, ERR_UNSUPPORTED, ERR_HIP = range(7)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if dmbuild.is_stale():
+        dmbuild.build()
+    return dm.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(diagmm_[a-zA-Z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for want in ("diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax",
+                 "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
+                 "diagmm_plan"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported by {dm.library_path()}"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert dm.diagmm_abi_version() == 1
+    seen = set()
+    for st in range(7):
+        s = lib.diagmm_status_string(st).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.diagmm_status_string(99).decode() == "unknown status"
+
+
+FAKE = 1 << 40  # never dereferenced: every call below fails validation or is empty
+
+
+def call_qk(lib, q=FAKE, k=FAKE + (1 << 30), band=FAKE + (1 << 34), b=1, n=8, h=1, d=4, w=2,
+            wu=2, dil=0, ind=1, outd=1):
+    return lib.diagmm_qk(q, k, band, b, n, h, d, w, wu, dil, 0.0, ind, outd, None)
+
+
+def test_validation_errors_are_reported_without_launching(lib):
+    assert call_qk(lib, q=0) == ERR_NULL
+    assert call_qk(lib, band=0) == ERR_NULL
+    assert call_qk(lib, n=-1) == ERR_SHAPE
+    assert call_qk(lib, d=0) == ERR_SHAPE
+    assert call_qk(lib, w=-3) == ERR_SHAPE
+    assert call_qk(lib, dil=-1) == ERR_SHAPE
+    assert call_qk(lib, b=1 << 40, n=1 << 20, h=1 << 10) == ERR_SHAPE
+    assert call_qk(lib, ind=7) == ERR_DTYPE
+    assert call_qk(lib, ind=1, outd=2) == ERR_DTYPE   # f16 -> bf16 is not offered
+    assert call_qk(lib, ind=0, outd=1) == ERR_DTYPE   # f32 -> f16 is not offered
+    msg = lib.diagmm_last_error().decode()
+    assert "diagmm_qk" in msg and "dtype" in msg
+    # band overlapping q
+    assert call_qk(lib, band=FAKE + 16) == ERR_ALIAS
+    for fn in (lib.diagmm_pv, lib.diagmm_pvT):
+        assert fn(FAKE, FAKE + (1 << 30), FAKE + 8, 1, 8, 1, 4, 2, 2, 0, 0.0, 1, 1, None) == ERR_ALIAS
+        assert fn(FAKE, 0, FAKE + (1 << 34), 1, 8, 1, 4, 2, 2, 0, 0.0, 1, 1, None) == ERR_NULL
+    sm = lib.diagmm_banded_softmax
+    assert sm(FAKE, FAKE + 2, 1, 8, 1, 2, 2, 0, 1.0, 1, 1, None) == ERR_ALIAS
+    assert sm(FAKE, FAKE, 1, 8, 1, 2, 2, 0, 1.0, 1, 0, None) == ERR_ALIAS  # in place needs equal dtypes
+    assert sm(FAKE, 0, 1, 8, 1, 2, 2, 0, 1.0, 1, 1, None) == ERR_NULL
+
+
+def test_empty_problems_are_noops(lib):
+    assert call_qk(lib, q=0, k=0, band=0, n=0) == OK
+    assert call_qk(lib, q=0, k=0, band=0, b=0) == OK
+    assert lib.diagmm_pv(0, 0, 0, 1, 8, 0, 4, 2, 2, 0, 0.0, 2, 0, None) == OK
+    assert lib.diagmm_banded_softmax(0, 0, 0, 8, 3, 2, 2, 0, 1.0, 1, 1, None) == OK
+    assert lib.diagmm_last_error().decode() == ""
+
+
+def test_python_binding_rejects_bad_tensors():
+    cpu = torch.zeros(1, 8, 1, 4)
+    with pytest.raises(ValueError):
+        dm.diagmm_qk(cpu, cpu, 2)
+    with pytest.raises(TypeError):
+        dm.diagmm_qk([1], cpu, 2)
+    with pytest.raises(ValueError):
+        dm.diagmm_pv(cpu, cpu, -1)
+
+
+@pytest.mark.parametrize("mode", ["qk", "pv", "pvT", "softmax"])
+@pytest.mark.parametrize("shape", [(1, 4096, 12, 64, 256, 256, 0), (1, 4096, 12, 64, 256, 256, 3),
+                                   (12, 4096, 12, 64, 256, 0, 0), (1, 32768, 12, 64, 4096, 4096, 0),
+                                   (1, 512, 1, 64, 32, 32, 0), (2, 37, 3, 24, 5, 0, 2)])
+def test_plans_are_consistent(lib, mode, shape):
+    b, n, h, d, w, wu, dil = shape
+    dt = torch.bfloat16 if wu == 0 else torch.float16
+    odt = torch.float32 if wu == 0 else dt
+    p = dm.diagmm_plan(mode, b, n, h, d, w, wu, dil, dt, odt)
+    assert p["kernel"]
+    assert p["threads"] in (64, 128, 256, 512, 1024)
+    assert 0 <= p["lds_bytes"] <= 160 * 1024
+    assert p["workgroups"] >= 1 and p["tiles"] >= 1
+    assert p["residues"] >= 1
+    if p["kernel"].endswith("simple"):
+        cols = (w + wu + 1) if mode == "qk" else d
+        assert p["tiles"] == b * n * h * cols
+
+
+def test_plan_rejects_what_the_calls_reject(lib):
+    with pytest.raises(dm.DiagmmError) as e:
+        dm.diagmm_plan("qk", 1, -4, 1, 64, 2)
+    assert e.value.status == ERR_SHAPE

@@ -1,0 +1,140 @@
+"""GPU robustness: nothing is written outside the output, results are deterministic,
+out-of-range band values never leak into pv / pvT, in-place softmax equals the
+out-of-place one, calls honour the caller's stream, and the tiled kernels agree with
+the element-per-thread kernels.
+"""
+import math
+import os
+
+import pytest
+import torch
+
+import datagen
+from _util import assert_bits_equal, check_close, in_range_mask
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [  # b, n, h, d, w, wu, dil, dtype
+    (1, 1000, 3, 64, 256, 256, 0, "f16"),
+    (2, 777, 2, 64, 64, 0, 3, "bf16"),
+    (1, 513, 2, 64, 32, 32, 2, "f32"),
+]
+
+
+def _inp(shape, seed=1):
+    b, n, h, d, w, wu, dil, dt = shape
+    g = datagen.rng(seed)
+    sc = 1 / math.sqrt(d)
+    q = datagen.normal(g, (b, n, h, d), dt, sc).cuda()
+    k = datagen.normal(g, (b, n, h, d), dt, sc).cuda()
+    p = datagen.softmax_rows(g, (b, n, h, w + wu + 1), dt).cuda()
+    return q, k, p
+
+
+def _guarded(shape, dtype, guard=4096):
+    numel = math.prod(shape)
+    buf = torch.empty(numel + 2 * guard, dtype=dtype, device="cuda")
+    buf.fill_(float("nan") if dtype != torch.float32 else 12345.0)
+    ref = buf.clone()
+    return buf, buf[guard:guard + numel].view(shape), ref, guard, numel
+
+
+def _guards_intact(buf, ref, guard, numel):
+    assert_bits_equal(buf[:guard], ref[:guard], "guard before the output")
+    assert_bits_equal(buf[guard + numel:], ref[guard + numel:], "guard after the output")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_no_writes_outside_outputs(shape):
+    import sliding_window_attention_diagmm_amd as dm
+    b, n, h, d, w, wu, dil, dt = shape
+    q, k, p = _inp(shape)
+    K = w + wu + 1
+    buf, out, ref, g, ne = _guarded((b, n, h, K), q.dtype)
+    dm.diagmm_qk(q, k, w, wu, dil, 0.0, out=out)
+    torch.cuda.synchronize()
+    _guards_intact(buf, ref, g, ne)
+    for fn in (dm.diagmm_pv, dm.diagmm_pvT):
+        buf, out, ref, g, ne = _guarded((b, n, h, d), torch.float32)
+        fn(p, k, w, wu, dil, out_dtype=torch.float32, out=out)
+        torch.cuda.synchronize()
+        _guards_intact(buf, ref, g, ne)
+    buf, out, ref, g, ne = _guarded((b, n, h, K), q.dtype)
+    dm.diagmm_banded_softmax(p, w, wu, dil, 0.5, out=out)
+    torch.cuda.synchronize()
+    _guards_intact(buf, ref, g, ne)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_bitwise_deterministic_reruns(shape):
+    import sliding_window_attention_diagmm_amd as dm
+    b, n, h, d, w, wu, dil, dt = shape
+    q, k, p = _inp(shape, 2)
+    for fn, args in ((dm.diagmm_qk, (q, k)), (dm.diagmm_pv, (p, k)), (dm.diagmm_pvT, (p, q))):
+        a = fn(*args, w, wu, dil)
+        b2 = fn(*args, w, wu, dil)
+        assert_bits_equal(a, b2, fn.__name__ + " rerun")
+    a = dm.diagmm_banded_softmax(p, w, wu, dil, 0.7)
+    assert_bits_equal(a, dm.diagmm_banded_softmax(p, w, wu, dil, 0.7), "softmax rerun")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("poison", [float("nan"), 1e30])
+def test_out_of_range_band_values_are_ignored(shape, poison):
+    import sliding_window_attention_diagmm_amd as dm
+    b, n, h, d, w, wu, dil, dt = shape
+    q, k, p = _inp(shape, 3)
+    mask = in_range_mask(b, n, h, w, wu, dil).cuda()
+    poisoned = torch.where(mask, p, torch.tensor(poison, dtype=p.dtype, device="cuda"))
+    for fn in (dm.diagmm_pv, dm.diagmm_pvT):
+        assert_bits_equal(fn(poisoned, k, w, wu, dil), fn(p, k, w, wu, dil), fn.__name__)
+    # the softmax never reads them either
+    sm = dm.diagmm_banded_softmax
+    assert_bits_equal(sm(poisoned, w, wu, dil, 0.3), sm(p, w, wu, dil, 0.3), "softmax")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_inplace_softmax_matches_out_of_place(shape):
+    import sliding_window_attention_diagmm_amd as dm
+    b, n, h, d, w, wu, dil, dt = shape
+    q, k, p = _inp(shape, 4)
+    s = dm.diagmm_qk(q, k, w, wu, dil, 0.0)
+    ref = dm.diagmm_banded_softmax(s, w, wu, dil, 0.125)
+    got = dm.diagmm_banded_softmax(s, w, wu, dil, 0.125, inplace=True)
+    assert got.data_ptr() == s.data_ptr()
+    assert_bits_equal(got, ref, "in-place softmax")
+
+
+def test_calls_run_on_the_callers_stream():
+    import sliding_window_attention_diagmm_amd as dm
+    shape = SHAPES[0]
+    b, n, h, d, w, wu, dil, dt = shape
+    q, k, p = _inp(shape, 5)
+    ref = dm.diagmm_qk(q, k, w, wu, dil)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = dm.diagmm_qk(q, k, w, wu, dil)
+        probs = dm.diagmm_banded_softmax(got, w, wu, dil, 0.125)
+        out = dm.diagmm_pv(probs, k, w, wu, dil)
+    side.synchronize()
+    assert_bits_equal(got, ref, "qk on a side stream")
+    assert_bits_equal(out, dm.diagmm_pv(dm.diagmm_banded_softmax(ref, w, wu, dil, 0.125),
+                                        k, w, wu, dil), "chain on a side stream")
+
+
+@pytest.mark.parametrize("shape", SHAPES + [(1, 4096, 12, 64, 256, 256, 0, "f16"),
+                                            (1, 4096, 12, 64, 256, 256, 3, "f16")])
+def test_tiled_kernels_agree_with_element_kernels(shape, monkeypatch):
+    import sliding_window_attention_diagmm_amd as dm
+    b, n, h, d, w, wu, dil, dt = shape
+    q, k, p = _inp(shape, 6)
+    fast = [dm.diagmm_qk(q, k, w, wu, dil, -2.0), dm.diagmm_pv(p, k, w, wu, dil),
+            dm.diagmm_pvT(p, q, w, wu, dil), dm.diagmm_banded_softmax(p, w, wu, dil, 0.5)]
+    monkeypatch.setenv("DIAGMM_KERNEL", "simple")
+    slow = [dm.diagmm_qk(q, k, w, wu, dil, -2.0), dm.diagmm_pv(p, k, w, wu, dil),
+            dm.diagmm_pvT(p, q, w, wu, dil), dm.diagmm_banded_softmax(p, w, wu, dil, 0.5)]
+    monkeypatch.delenv("DIAGMM_KERNEL")
+    for name, a, s in zip(("qk", "pv", "pvT", "softmax"), fast, slow):
+        check_close(a.cpu(), s.cpu().double(), q.dtype, name + " tiled vs element",
+                    abs_tol=None if q.dtype == torch.float32 else 2e-3)

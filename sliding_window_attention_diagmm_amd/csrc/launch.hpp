@@ -3,6 +3,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "tiles.hpp"
 
 namespace diagmm {
 
@@ -16,5 +17,20 @@ hipError_t launch_pvT_simple(const void* band, const void* x, void* out, const P
                              int in_dt, int out_dt, hipStream_t stream);
 hipError_t launch_softmax_rows(const void* scores, void* probs, const Problem& p, float scale,
                                int in_dt, int out_dt, hipStream_t stream);
+
+// qk on MFMA (f16 / bf16 inputs, d in {32, 64, 128}, 16-byte aligned pointers).
+constexpr int kQkRows = 64;                  // rows per tile
+constexpr int64_t kQkStageBytes = 66 * 1024; // LDS staging budget per workgroup
+
+struct QkTilePlan {
+    TileGrid grid;
+    int64_t rs = 0;         // staging row stride (elements)
+    int64_t lds_bytes = 0;
+};
+
+QkTilePlan plan_qk_mfma(const Problem& p, int out_dt);
+hipError_t launch_qk_mfma(const void* q, const void* k, void* band, const Problem& p,
+                          const QkTilePlan& tp, int in_dt, int out_dt, uint32_t pad,
+                          hipStream_t stream);
 
 }  // namespace diagmm

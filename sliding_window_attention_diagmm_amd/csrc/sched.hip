@@ -31,13 +31,27 @@ Plan simple_plan(const Problem& p, int64_t cols, const char* name) {
     return pl;
 }
 
+bool mfma_dtype(int in_dt) { return in_dt == kF16 || in_dt == kBF16; }
+bool mfma_depth(int64_t d) { return d == 32 || d == 64 || d == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 }  // namespace
 
 Plan plan_qk(const Problem& p, int in_dt, int out_dt) {
-    (void)in_dt;
-    (void)out_dt;
-    (void)force_simple;
-    return simple_plan(p, p.K, "qk_simple");
+    if (force_simple() || !mfma_dtype(in_dt) || !mfma_depth(p.d))
+        return simple_plan(p, p.K, "qk_simple");
+    const QkTilePlan tp = plan_qk_mfma(p, out_dt);
+    Plan pl;
+    pl.family = Family::kQkMfma;
+    pl.kernel = "qk_mfma";
+    pl.rows_per_tile = kQkRows;
+    pl.slots_per_tile = tp.grid.kb;
+    pl.tiles = tp.grid.tiles;
+    pl.workgroups = tp.grid.per_xcd * kXcds;
+    pl.threads = 256;
+    pl.lds_bytes = tp.lds_bytes;
+    pl.residues = p.s;
+    return pl;
 }
 
 Plan plan_pv(const Problem& p, int in_dt, int out_dt) {
@@ -69,7 +83,9 @@ Plan plan_softmax(const Problem& p, int in_dt, int out_dt) {
 
 hipError_t run_qk(const Plan& plan, const void* q, const void* k, void* band, const Problem& p,
                   int in_dt, int out_dt, uint32_t pad, hipStream_t stream) {
-    (void)plan;
+    // The tiled kernel moves 16-byte pieces; other pointers take the general path.
+    if (plan.family == Family::kQkMfma && aligned16(q) && aligned16(k) && aligned16(band))
+        return launch_qk_mfma(q, k, band, p, plan_qk_mfma(p, out_dt), in_dt, out_dt, pad, stream);
     return launch_qk_simple(q, k, band, p, in_dt, out_dt, pad, stream);
 }
 

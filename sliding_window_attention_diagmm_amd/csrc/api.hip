@@ -84,6 +84,21 @@ diagmm_status_t launched(const char* fn, hipError_t e) {
 
 }  // namespace
 
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev >= 64) dev = 63;
+    if (cached[dev] <= 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
 // Round-to-nearest-even of a float into the 16-bit types, on the host.
 uint32_t pad_bits(float value, int out_dtype) {
     uint32_t u;

@@ -58,6 +58,9 @@ struct Problem {
     __host__ __device__ int64_t rows() const { return b * n; }
 };
 
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_cus();
+
 // Host-side rounding of the padding constant to the output type (nearest even),
 // so every out-of-range slot receives the same bit pattern.
 uint32_t pad_bits(float value, int out_dtype);

@@ -20,12 +20,14 @@ hipError_t launch_softmax_rows(const void* scores, void* probs, const Problem& p
 
 // qk on MFMA (f16 / bf16 inputs, d in {32, 64, 128}, 16-byte aligned pointers).
 constexpr int kQkRows = 64;                  // rows per tile
-constexpr int64_t kQkStageBytes = 66 * 1024; // LDS staging budget per workgroup
+constexpr int64_t kQkLdsBytes = 160 * 1024;  // one workgroup per compute unit
 
 struct QkTilePlan {
     TileGrid grid;
     int64_t rs = 0;         // staging row stride (elements)
     int64_t lds_bytes = 0;
+    int64_t workgroups = 0; // persistent workgroups (at most one per compute unit)
+    bool ok = false;        // the shape fits the kernel's 32-bit tile arithmetic
 };
 
 QkTilePlan plan_qk_mfma(const Problem& p, int out_dt);

@@ -41,16 +41,17 @@ Plan plan_qk(const Problem& p, int in_dt, int out_dt) {
     if (force_simple() || !mfma_dtype(in_dt) || !mfma_depth(p.d))
         return simple_plan(p, p.K, "qk_simple");
     const QkTilePlan tp = plan_qk_mfma(p, out_dt);
+    if (!tp.ok) return simple_plan(p, p.K, "qk_simple");
     Plan pl;
     pl.family = Family::kQkMfma;
     pl.kernel = "qk_mfma";
     pl.rows_per_tile = kQkRows;
     pl.slots_per_tile = tp.grid.kb;
     pl.tiles = tp.grid.tiles;
-    pl.workgroups = tp.grid.per_xcd * kXcds;
-    pl.threads = 256;
+    pl.workgroups = tp.workgroups;
+    pl.threads = 512;
     pl.lds_bytes = tp.lds_bytes;
-    pl.residues = p.s;
+    pl.residues = tp.grid.res;
     return pl;
 }
 

@@ -41,6 +41,8 @@ CASES = [
     (2, 96, 2, 64, 40, 40, 3, "f32", "f32"),
     (1, 64, 1, 8, 0, 0, 0, "f16", "f16"),           # K = 1: only the main diagonal
     (1, 640, 4, 64, 128, 128, 0, "bf16", "bf16"),
+    (1, 5, 2, 64, 3, 3, 9, "f16", "f16"),           # dilation larger than the sequence
+    (3, 130, 2, 32, 600, 0, 2, "f16", "f32"),       # several slot blocks per row
 ]
 
 

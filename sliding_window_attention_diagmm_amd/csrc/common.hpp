@@ -50,6 +50,50 @@ struct BF16 {
     }
 };
 
+// ------------------------------------------------------------------ 16-byte pieces
+// Band rows are moved as aligned 16-byte pieces; a row's first and last piece may be
+// shared with the neighbouring row.  These helpers touch only elements [a, b) of such a
+// piece.  Each dword is handled as a named scalar with per-element branches: per-element
+// insertion into or extraction from a vector register inside divergent branches is
+// avoided on purpose (it has been miscompiled for 32-bit elements).
+
+// Dword j (0..3) of a partial piece: own elements loaded, the others zero.
+template <class ST>
+__device__ __forceinline__ uint32_t load_part_dword(const ST* gp, int j, int a, int b) {
+    if constexpr (sizeof(ST) == 4) {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(gp);
+        return (a <= j && j < b) ? p[j] : 0u;
+    } else {
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(gp);
+        const uint32_t lo = (a <= 2 * j && 2 * j < b) ? p[2 * j] : 0u;
+        const uint32_t hi = (a <= 2 * j + 1 && 2 * j + 1 < b) ? p[2 * j + 1] : 0u;
+        return lo | (hi << 16);
+    }
+}
+
+// Store elements [a, b) of a piece whose dwords are d0..d3.
+template <class ST>
+__device__ __forceinline__ void store_part(ST* gp, uint32_t d0, uint32_t d1, uint32_t d2,
+                                           uint32_t d3, int a, int b) {
+    if constexpr (sizeof(ST) == 4) {
+        uint32_t* p = reinterpret_cast<uint32_t*>(gp);
+        if (a <= 0 && 0 < b) p[0] = d0;
+        if (a <= 1 && 1 < b) p[1] = d1;
+        if (a <= 2 && 2 < b) p[2] = d2;
+        if (a <= 3 && 3 < b) p[3] = d3;
+    } else {
+        uint16_t* p = reinterpret_cast<uint16_t*>(gp);
+        if (a <= 0 && 0 < b) p[0] = static_cast<uint16_t>(d0);
+        if (a <= 1 && 1 < b) p[1] = static_cast<uint16_t>(d0 >> 16);
+        if (a <= 2 && 2 < b) p[2] = static_cast<uint16_t>(d1);
+        if (a <= 3 && 3 < b) p[3] = static_cast<uint16_t>(d1 >> 16);
+        if (a <= 4 && 4 < b) p[4] = static_cast<uint16_t>(d2);
+        if (a <= 5 && 5 < b) p[5] = static_cast<uint16_t>(d2 >> 16);
+        if (a <= 6 && 6 < b) p[6] = static_cast<uint16_t>(d3);
+        if (a <= 7 && 7 < b) p[7] = static_cast<uint16_t>(d3 >> 16);
+    }
+}
+
 // ------------------------------------------------------------------ problem descriptor
 
 struct Problem {

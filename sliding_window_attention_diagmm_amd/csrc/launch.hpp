@@ -18,6 +18,12 @@ hipError_t launch_pvT_simple(const void* band, const void* x, void* out, const P
 hipError_t launch_softmax_rows(const void* scores, void* probs, const Problem& p, float scale,
                                int in_dt, int out_dt, hipStream_t stream);
 
+// Banded softmax, one wavefront per row (equal in/out dtypes, rows up to ~8.7K slots,
+// 16-byte aligned pointers).
+bool softmax_wave_supported(const Problem& p, int in_dt, int out_dt);
+hipError_t launch_softmax_wave(const void* scores, void* probs, const Problem& p, float scale,
+                               int dt, hipStream_t stream);
+
 // qk on MFMA (f16 / bf16 inputs, d in {32, 64, 128}, 16-byte aligned pointers).
 constexpr int kQkRows = 64;                  // rows per tile
 constexpr int64_t kQkLdsBytes = 160 * 1024;  // one workgroup per compute unit

@@ -324,42 +324,54 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
                 const int e = il * rs + kMargin + (il & 3) + kVec * c - sh;
                 const int m = e & 3;
                 const unsigned char* lp = reinterpret_cast<const unsigned char*>(stage + (e - m));
-                u32x4 o;
+                // o0..o3: the piece's four dwords, named scalars throughout (no arrays)
+                uint32_t o0, o1, o2, o3;
                 if constexpr (sizeof(OT) == 2) {
-                    const u32x2 w0 = *reinterpret_cast<const u32x2*>(lp);
-                    const u32x2 w1 = *reinterpret_cast<const u32x2*>(lp + 8);
-                    const u32x2 w2 = *reinterpret_cast<const u32x2*>(lp + 16);
-                    const uint32_t w[6] = {w0[0], w0[1], w1[0], w1[1], w2[0], w2[1]};
-                    const bool hi = m & 2, odd = m & 1;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t lo_w = hi ? w[k + 1] : w[k];
-                        const uint32_t hi_w = hi ? w[k + 2] : w[k + 1];
-                        o[k] = odd ? __builtin_amdgcn_alignbit(hi_w, lo_w, 16) : lo_w;
+                    const u32x2 wa = *reinterpret_cast<const u32x2*>(lp);
+                    const u32x2 wb = *reinterpret_cast<const u32x2*>(lp + 8);
+                    const u32x2 wc = *reinterpret_cast<const u32x2*>(lp + 16);
+                    const bool hi = m & 2;
+                    const uint32_t l0 = hi ? wa[1] : wa[0];
+                    const uint32_t l1 = hi ? wb[0] : wa[1];
+                    const uint32_t l2 = hi ? wb[1] : wb[0];
+                    const uint32_t l3 = hi ? wc[0] : wb[1];
+                    const uint32_t l4 = hi ? wc[1] : wc[0];
+                    if (m & 1) {
+                        o0 = __builtin_amdgcn_alignbit(l1, l0, 16);
+                        o1 = __builtin_amdgcn_alignbit(l2, l1, 16);
+                        o2 = __builtin_amdgcn_alignbit(l3, l2, 16);
+                        o3 = __builtin_amdgcn_alignbit(l4, l3, 16);
+                    } else {
+                        o0 = l0;
+                        o1 = l1;
+                        o2 = l2;
+                        o3 = l3;
                     }
                 } else {
-                    const u32x4 w0 = *reinterpret_cast<const u32x4*>(lp);
-                    const u32x4 w1 = *reinterpret_cast<const u32x4*>(lp + 16);
-                    const uint32_t w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t a0 = (m & 1) ? w[k + 1] : w[k];
-                        const uint32_t a1 = (m & 1) ? w[k + 3] : w[k + 2];
-                        o[k] = (m & 2) ? a1 : a0;
-                    }
+                    const u32x4 wa = *reinterpret_cast<const u32x4*>(lp);
+                    const u32x4 wb = *reinterpret_cast<const u32x4*>(lp + 16);
+                    const bool odd = m & 1, hi = m & 2;
+                    const uint32_t t0_ = odd ? wa[1] : wa[0], u0_ = odd ? wa[3] : wa[2];
+                    const uint32_t t1_ = odd ? wa[2] : wa[1], u1_ = odd ? wb[0] : wa[3];
+                    const uint32_t t2_ = odd ? wa[3] : wa[2], u2_ = odd ? wb[1] : wb[0];
+                    const uint32_t t3_ = odd ? wb[0] : wa[3], u3_ = odd ? wb[2] : wb[1];
+                    o0 = hi ? u0_ : t0_;
+                    o1 = hi ? u1_ : t1_;
+                    o2 = hi ? u2_ : t2_;
+                    o3 = hi ? u3_ : t3_;
                 }
                 OT* gp = band + (g0 + il * gstep - sh) + c * kVec;     // 16-byte aligned
                 const int lo = c * kVec;
                 if (lo >= sh && lo + kVec <= sh + kbeff) {
-                    *reinterpret_cast<u32x4*>(gp) = o;
+                    *reinterpret_cast<u32x4*>(gp) = u32x4{o0, o1, o2, o3};
                 } else {
-                    const OT* ov = reinterpret_cast<const OT*>(&o);
-#pragma unroll
-                    for (int x = 0; x < kVec; ++x)
-                        if (lo + x >= sh && lo + x < sh + kbeff) gp[x] = ov[x];
+                    // partial piece: only this row's elements [a, b) of the piece
+                    const int pa = sh - lo > 0 ? sh - lo : 0;
+                    const int pb = sh + kbeff - lo < kVec ? sh + kbeff - lo : kVec;
+                    store_part<OT>(gp, o0, o1, o2, o3, pa, pb);
                 }
             }
-            il += step_rows;
+        il += step_rows;
             c += step_c;
             if (c >= ncmax) {
                 c -= ncmax;

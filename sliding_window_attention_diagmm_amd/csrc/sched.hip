@@ -68,9 +68,18 @@ Plan plan_pvT(const Problem& p, int in_dt, int out_dt) {
 }
 
 Plan plan_softmax(const Problem& p, int in_dt, int out_dt) {
-    (void)in_dt;
-    (void)out_dt;
     Plan pl;
+    if (!force_simple() && softmax_wave_supported(p, in_dt, out_dt)) {
+        pl.family = Family::kSoftmaxWave;
+        pl.kernel = "softmax_wave";
+        pl.rows_per_tile = 1;
+        pl.slots_per_tile = p.K;
+        pl.tiles = p.rows() * p.h;
+        pl.workgroups = (pl.tiles + 3) / 4;
+        pl.threads = 256;
+        pl.lds_bytes = 0;
+        return pl;
+    }
     pl.family = Family::kSoftmaxRow;
     pl.kernel = "softmax_rows";
     pl.rows_per_tile = 1;
@@ -104,7 +113,8 @@ hipError_t run_pvT(const Plan& plan, const void* band, const void* x, void* out,
 
 hipError_t run_softmax(const Plan& plan, const void* scores, void* probs, const Problem& p,
                        float scale, int in_dt, int out_dt, hipStream_t stream) {
-    (void)plan;
+    if (plan.family == Family::kSoftmaxWave && aligned16(scores) && aligned16(probs))
+        return launch_softmax_wave(scores, probs, p, scale, in_dt, stream);
     return launch_softmax_rows(scores, probs, p, scale, in_dt, out_dt, stream);
 }
 

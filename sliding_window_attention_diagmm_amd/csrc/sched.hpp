@@ -13,6 +13,7 @@ enum class Family {
     kPvMfma,      // pv: band tile un-skewed into MFMA operands
     kPvTMfma,     // pvT: transposed band tile into MFMA operands
     kSoftmaxRow,  // softmax: one workgroup per band row
+    kSoftmaxWave, // softmax: one wavefront per band row, row held in registers
 };
 
 struct Plan {

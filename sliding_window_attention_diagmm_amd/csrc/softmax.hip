@@ -1,0 +1,185 @@
+// Banded softmax, one wavefront per band row.
+//
+// The row (K slots, contiguous in [b][n][h][K]) is read once as aligned 16-byte pieces
+// into registers; the at most two pieces it shares with the neighbouring rows are read
+// and written element by element for this row's own slots only, so rows never touch
+// each other's data and the softmax may run in place.  Slots whose key lies outside the
+// sequence are masked by index (they hold -inf before the max and exactly +0 after).
+// The row max and the sum of exponentials are wavefront reductions; each exponential
+// is computed once and kept in registers until the normalised values are written.
+//
+// Recipe (csarofeen/pytorch issue 2096, first fusion repro): scale, row max, subtract,
+// exp, row sum, divide.  The in-range slot interval of row i is
+// [w - min(w, floor(i/s)), w + min(w_upper, floor((n-1-i)/s))], slot w being the row's
+// own position, so no row is ever empty.
+#include "launch.hpp"
+
+namespace diagmm {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kThreads / 64;
+
+// Element e (0..kVec-1) of a piece held as dwords d0..d3, as float; and the raw bits of
+// a float rounded to the element type.
+template <class T> struct Elem;
+template <> struct Elem<F16> {
+    __device__ __forceinline__ static float get(uint32_t d, int half) {
+        return F16::to_f32(static_cast<uint16_t>(half ? (d >> 16) : (d & 0xffffu)));
+    }
+    __device__ __forceinline__ static uint32_t bits(float x) { return F16::from_f32(x); }
+};
+template <> struct Elem<BF16> {
+    __device__ __forceinline__ static float get(uint32_t d, int half) {
+        return BF16::to_f32(static_cast<uint16_t>(half ? (d >> 16) : (d & 0xffffu)));
+    }
+    __device__ __forceinline__ static uint32_t bits(float x) { return BF16::from_f32(x); }
+};
+template <> struct Elem<F32> {
+    __device__ __forceinline__ static float get(uint32_t d, int) { return __builtin_bit_cast(float, d); }
+    __device__ __forceinline__ static uint32_t bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// P = pieces per lane (the row has at most 64 P pieces).
+template <class T, int P>
+__global__ void __launch_bounds__(kThreads)
+softmax_wave_kernel(const typename T::T* scores, typename T::T* probs, Problem p, float scale,
+                    int64_t nrows) {
+    using ST = typename T::T;
+    constexpr int kVec = 16 / sizeof(ST);
+    const int lane = threadIdx.x & 63;
+    const int64_t row = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= nrows) return;
+    const int64_t i = (row / p.h) % p.n;
+    const int64_t lo_off = i / p.s, hi_off = (p.n - 1 - i) / p.s;
+    const int k_lo = static_cast<int>(p.w - (lo_off < p.w ? lo_off : p.w));
+    const int k_hi = static_cast<int>(p.w + (hi_off < p.wu ? hi_off : p.wu) + 1);
+    const int K = static_cast<int>(p.K);
+    const int64_t g = row * p.K;                       // first element of the row
+    const int sh = static_cast<int>(g & (kVec - 1));
+    const int nc = (sh + K + kVec - 1) / kVec;
+    const ST* src = scores + (g - sh);                 // 16-byte aligned
+    ST* dst = probs + (g - sh);
+
+    // x[q][e]: scaled score of element e of piece c = lane + 64 q (slot c*kVec + e - sh)
+    float x[P][kVec];
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int c = lane + 64 * q;
+        const int base = c * kVec - sh;                // slot of element 0
+        uint32_t dw[4] = {0u, 0u, 0u, 0u};   // the piece as dwords (static indices only)
+        if (c < nc) {
+            if (base >= 0 && base + kVec <= K) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(src + c * kVec);
+                dw[0] = v[0];
+                dw[1] = v[1];
+                dw[2] = v[2];
+                dw[3] = v[3];
+            } else {
+                const int a = base < 0 ? -base : 0;
+                const int b = K - base < kVec ? K - base : kVec;
+                dw[0] = load_part_dword<ST>(src + c * kVec, 0, a, b);
+                dw[1] = load_part_dword<ST>(src + c * kVec, 1, a, b);
+                dw[2] = load_part_dword<ST>(src + c * kVec, 2, a, b);
+                dw[3] = load_part_dword<ST>(src + c * kVec, 3, a, b);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            const int k = base + e;
+            const bool in = c < nc && k >= k_lo && k < k_hi;
+            const uint32_t d = kVec == 8 ? dw[e >> 1] : dw[e];
+            x[q][e] = in ? scale * Elem<T>::get(d, e & 1) : -INFINITY;
+            m = fmaxf(m, x[q][e]);
+        }
+    }
+    m = wave_max(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < P; ++q)
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            x[q][e] = __expf(x[q][e] - m);             // exp(-inf) = +0 for masked slots
+            sum += x[q][e];
+        }
+    sum = wave_sum(sum);
+    const float inv = 1.f / sum;
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int c = lane + 64 * q;
+        if (c >= nc) continue;
+        const int base = c * kVec - sh;
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (kVec == 8)
+                o[j] = Elem<T>::bits(x[q][2 * j] * inv) | (Elem<T>::bits(x[q][2 * j + 1] * inv) << 16);
+            else
+                o[j] = Elem<T>::bits(x[q][j] * inv);
+        }
+        if (base >= 0 && base + kVec <= K) {
+            *reinterpret_cast<u32x4*>(dst + c * kVec) = u32x4{o[0], o[1], o[2], o[3]};
+        } else {
+            const int a = base < 0 ? -base : 0;
+            const int b = K - base < kVec ? K - base : kVec;
+            store_part<ST>(dst + c * kVec, o[0], o[1], o[2], o[3], a, b);
+        }
+    }
+}
+
+template <class T, int P>
+hipError_t launch_p(const void* scores, void* probs, const Problem& p, float scale,
+                    hipStream_t stream) {
+    const int64_t nrows = p.rows() * p.h;
+    const int64_t grid = (nrows + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL((softmax_wave_kernel<T, P>), dim3(static_cast<uint32_t>(grid)),
+                       dim3(kThreads), 0, stream, static_cast<const typename T::T*>(scores),
+                       static_cast<typename T::T*>(probs), p, scale, nrows);
+    return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_t(const void* scores, void* probs, const Problem& p, float scale,
+                    hipStream_t stream) {
+    constexpr int kVec = 16 / sizeof(typename T::T);
+    const int64_t pieces = (p.K + 2 * kVec - 2) / kVec;   // worst-case alignment
+    if (pieces <= 64 * 2) return launch_p<T, 2>(scores, probs, p, scale, stream);
+    if (pieces <= 64 * 4) return launch_p<T, 4>(scores, probs, p, scale, stream);
+    if (pieces <= 64 * 8) return launch_p<T, 8>(scores, probs, p, scale, stream);
+    if (pieces <= 64 * 17) return launch_p<T, 17>(scores, probs, p, scale, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool softmax_wave_supported(const Problem& p, int in_dt, int out_dt) {
+    if (in_dt != out_dt) return false;
+    const int64_t kvec = in_dt == kF32 ? 4 : 8;
+    const int64_t pieces = (p.K + 2 * kvec - 2) / kvec;
+    const int64_t grid = (p.rows() * p.h + kRowsPerBlock - 1) / kRowsPerBlock;
+    return pieces <= 64 * 17 && grid < (int64_t(1) << 31) && p.K < (int64_t(1) << 30);
+}
+
+hipError_t launch_softmax_wave(const void* scores, void* probs, const Problem& p, float scale,
+                               int dt, hipStream_t stream) {
+    switch (dt) {
+    case kF32: return launch_t<F32>(scores, probs, p, scale, stream);
+    case kF16: return launch_t<F16>(scores, probs, p, scale, stream);
+    case kBF16: return launch_t<BF16>(scores, probs, p, scale, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace diagmm

@@ -41,4 +41,19 @@ hipError_t launch_qk_mfma(const void* q, const void* k, void* band, const Proble
                           const QkTilePlan& tp, int in_dt, int out_dt, uint32_t pad,
                           hipStream_t stream);
 
+// pv on MFMA (f16 / bf16 inputs, d in {32, 64, 128}, 16-byte aligned pointers).
+constexpr int kPvRows = 64;
+constexpr int64_t kPvLdsBytes = 160 * 1024;
+
+struct PvTilePlan {
+    TileGrid grid;          // nkb / kb: slot chunks per tile and slots per chunk
+    int64_t lds_bytes = 0;
+    int64_t workgroups = 0;
+    bool ok = false;
+};
+
+PvTilePlan plan_pv_mfma(const Problem& p);
+hipError_t launch_pv_mfma(const void* band, const void* v, void* out, const Problem& p,
+                          const PvTilePlan& tp, int in_dt, int out_dt, hipStream_t stream);
+
 }  // namespace diagmm

@@ -1,0 +1,455 @@
+// diagmm_pv on MFMA with persistent, sliding workgroups.
+//
+//   out[t][c] = sum over in-range slots k of P[t][k] * V[t + k - w][c]
+//
+// (class-local rows t and keys u of one residue class of the dilation, as in the qk
+// kernel).  In dense form out = B V with B[t][u] = P[t][u - t + w] on the band and 0
+// elsewhere; the kernel computes the transposed product out^T = V^T B^T.
+//
+// Tiles and workgroups.  A tile is 64 consecutive rows t0..t0+63 of one residue class of
+// one (batch, head); when the band is wider than a slot chunk (KC slots, set by the LDS
+// budget) the tile is processed chunk by chunk with the accumulators kept in registers.
+// A chunk's slots reach the W = 64 + KC - 1 keys u0 .. u0 + W - 1 (u0 = t0 + k0 - w).
+// One 512-thread workgroup per compute unit walks a contiguous range of whole tiles, chunk
+// by chunk; single-chunk tiles that continue a strip slide the key window by 64.
+//
+// LDS.  V is kept transposed, VT[c][slot], in a ring of key slots, so the MFMA A operand
+// (16 channels x 8 consecutive keys) is one aligned 16-byte read; new rows are scattered
+// into it as they arrive (keys outside the sequence are written as zeros).  The band
+// rows of the current item are copied in as aligned 16-byte pieces of the band tensor
+// (LDS and HBM agree on alignment: row il starts at il * RSP + margin + its offset
+// modulo 8).  The B operand - 8 consecutive keys of one query row, i.e. 8 consecutive
+// band slots of that row starting at an arbitrary slot - is gathered with 2-byte LDS
+// reads; slots outside the chunk or whose key lies outside the sequence read as 0, by
+// index, whatever the band holds there.
+//
+// Compute.  Wave w owns query block rb = w / 2 (16 rows) and channel blocks
+// cb = 2 (w % 2), 2 (w % 2) + 1; for every 32-key chunk of the window that its rows reach
+// it gathers one B operand and issues two v_mfma_f32_16x16x32_{f16,bf16}.  Lane
+// (i = lane % 16, g = lane / 16) accumulates out[16 rb + i][16 cb + 4 g .. +3].
+//
+// Pipelining.  While an item is computed, the band pieces and new V rows of the next
+// item are already loading into registers; they are written to LDS after a barrier.
+#include "launch.hpp"
+#include "tiles.hpp"
+
+namespace diagmm {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <class In> struct Mfma;
+template <> struct Mfma<F16> {
+    using V = f16x8;
+    __device__ __forceinline__ static f32x4 run(V a, V b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<BF16> {
+    using V = bf16x8;
+    __device__ __forceinline__ static f32x4 run(V a, V b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+constexpr int kThreads = 512;
+constexpr int kRows = kPvRows;             // 64 query rows per tile
+constexpr int kMargin = 16;                // band staging lead-in (elements)
+constexpr int kMaxChunk = 513;             // slots per chunk
+constexpr int kMaxWin = kRows + kMaxChunk - 1;
+constexpr int kBandPieces = (kRows * ((kMaxChunk + 14) / 8 + 1) + kThreads - 1) / kThreads;
+
+struct PvArgs {
+    int64_t n, h, K, w, s;
+    TileGrid g;            // nkb = chunks per tile, kb = slots per chunk
+    int32_t rsp;           // band staging row stride (elements, multiple of 8)
+    int32_t ring;          // V ring capacity in key slots (multiple of 8)
+    int32_t ring_off;      // LDS byte offset of the V ring
+    uint32_t nwg;
+};
+
+// One work item = (tile, chunk); items run with the chunk fastest, so a tile's chunks
+// are consecutive and its accumulators stay in registers.
+struct Item {
+    TileId t;
+    int n_r, t0, rows_here, kbeff, u0, W;
+    int64_t k0, row0;
+};
+
+template <class In, int D>
+__global__ void __launch_bounds__(kThreads)
+pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __restrict__ v,
+               void* __restrict__ out_raw, int out_f32, PvArgs a) {
+    using ST = typename In::T;
+    using V = typename Mfma<In>::V;
+    constexpr int kChunks = D / 8;                          // 16-byte pieces per V row
+    constexpr int kPerWinV = (kMaxWin * kChunks + kThreads - 1) / kThreads;
+    constexpr int kPer64V = (kRows * kChunks + kThreads - 1) / kThreads;
+    constexpr int kCB = D / 16;                             // channel blocks
+    static_assert(kCB >= 2 && kCB % 2 == 0, "d must be a multiple of 32");
+    constexpr int kCBPerWave = kCB / 2;
+
+    extern __shared__ __align__(16) unsigned char lds[];
+    ST* pst = reinterpret_cast<ST*>(lds);                   // band staging
+    ST* vt = reinterpret_cast<ST*>(lds + a.ring_off);       // VT[c][slot]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+    const int64_t n = a.n, h = a.h, K = a.K, s = a.s;
+    const int64_t row_step = s * h;
+    const int rsp = a.rsp, ringc = a.ring;
+    const int rb = wave >> 1;                               // this wave's query block
+    const int cb0 = (wave & 1) * kCBPerWave;                // first channel block
+
+    // Whole tiles per workgroup (a tile's chunks share its accumulators), items = chunks.
+    int64_t item, iend;
+    {
+        int64_t tb, te;
+        tile_range(a.g.tiles / a.g.nkb, xcd_rank(blockIdx.x, a.nwg), a.nwg, &tb, &te);
+        item = tb * a.g.nkb;
+        iend = te * a.g.nkb;
+    }
+    // Zero the V ring once: window columns past the current window are read (and
+    // multiplied by exact zeros), so no slot may ever hold a non-finite pattern.
+    for (int x = tid; x < D * ringc / 8; x += kThreads)
+        reinterpret_cast<u32x4*>(vt)[x] = u32x4{0u, 0u, 0u, 0u};
+
+    auto describe = [&](int64_t id, Item* it) {
+        const int64_t nkb = a.g.nkb;
+        const int kc = static_cast<int>(id % nkb);
+        TileId t = decode_tile(TileGrid{a.g.res, a.g.rb, 1, a.g.kb, a.g.tiles / nkb}, h,
+                               static_cast<uint32_t>(id / nkb));
+        t.kb = kc;
+        it->t = t;
+        it->n_r = static_cast<int>(class_len(n, s, t.r));
+        it->t0 = t.tb * kRows;
+        it->rows_here = it->n_r - it->t0 < kRows ? it->n_r - it->t0 : kRows;
+        it->k0 = static_cast<int64_t>(kc) * a.g.kb;
+        it->kbeff = static_cast<int>(K - it->k0 < a.g.kb ? K - it->k0 : a.g.kb);
+        it->u0 = static_cast<int>(it->t0 + it->k0 - a.w);
+        it->W = kRows + it->kbeff - 1;
+        it->row0 = (static_cast<int64_t>(t.bb) * n + t.r) * h + t.hh;
+    };
+
+    // Registers that carry the next item's band pieces and, when its window slides, the
+    // 64 new V rows.
+    u32x4 pb[kBandPieces];
+    u32x4 vb[kPer64V];
+
+    // Band pieces of an item: rows il < rows_here, pieces c < nc(il) of slots [k0, k0+kbeff).
+    auto band_geom = [&](const Item& it, int il, int64_t* g, int* sh, int* nc) {
+        *g = (it.row0 + static_cast<int64_t>(it.t0 + il) * row_step) * K + it.k0;
+        *sh = static_cast<int>(*g & 7);
+        *nc = (*sh + it.kbeff + 7) / 8;
+    };
+    const int ncmax_glob = (7 + a.g.kb + 7) / 8;
+
+    auto load_band = [&](const Item& it) {
+#pragma unroll
+        for (int x = 0; x < kBandPieces; ++x) {
+            const int idx = tid + x * kThreads;
+            const int il = idx / ncmax_glob, c = idx - il * ncmax_glob;
+            if (il < it.rows_here) {
+                int64_t g;
+                int sh, nc;
+                band_geom(it, il, &g, &sh, &nc);
+                if (c < nc) {
+                    const int lo = c * 8 - sh;                 // slot of element 0
+                    const ST* gp = band + (g - sh) + c * 8;
+                    if (lo >= 0 && lo + 8 <= it.kbeff) {
+                        pb[x] = *reinterpret_cast<const u32x4*>(gp);
+                    } else {
+                        const int pa = lo < 0 ? -lo : 0;
+                        const int pe = it.kbeff - lo < 8 ? it.kbeff - lo : 8;
+                        pb[x] = u32x4{load_part_dword<ST>(gp, 0, pa, pe),
+                                      load_part_dword<ST>(gp, 1, pa, pe),
+                                      load_part_dword<ST>(gp, 2, pa, pe),
+                                      load_part_dword<ST>(gp, 3, pa, pe)};
+                    }
+                }
+            }
+        }
+    };
+    auto store_band = [&](const Item& it) {
+#pragma unroll
+        for (int x = 0; x < kBandPieces; ++x) {
+            const int idx = tid + x * kThreads;
+            const int il = idx / ncmax_glob, c = idx - il * ncmax_glob;
+            if (il < it.rows_here) {
+                int64_t g;
+                int sh, nc;
+                band_geom(it, il, &g, &sh, &nc);
+                if (c < nc)
+                    *reinterpret_cast<u32x4*>(pst + il * rsp + kMargin + c * 8) = pb[x];
+            }
+        }
+    };
+    // Scatter one 16-byte piece of V row `slot` (channels ch*8 .. ch*8+7) into VT.
+    auto put_v = [&](int slot, int ch, const u32x4& pc) {
+        const uint32_t d0 = pc[0], d1 = pc[1], d2 = pc[2], d3 = pc[3];
+        uint16_t* base = reinterpret_cast<uint16_t*>(vt) + (ch * 8) * ringc + slot;
+        base[0 * ringc] = static_cast<uint16_t>(d0);
+        base[1 * ringc] = static_cast<uint16_t>(d0 >> 16);
+        base[2 * ringc] = static_cast<uint16_t>(d1);
+        base[3 * ringc] = static_cast<uint16_t>(d1 >> 16);
+        base[4 * ringc] = static_cast<uint16_t>(d2);
+        base[5 * ringc] = static_cast<uint16_t>(d2 >> 16);
+        base[6 * ringc] = static_cast<uint16_t>(d3);
+        base[7 * ringc] = static_cast<uint16_t>(d3 >> 16);
+    };
+    // One 16-byte piece of V for window column x of an item (zeros outside the sequence).
+    auto get_v = [&](const Item& it, int x, int ch) {
+        const int u = it.u0 + x;
+        if (u < 0 || u >= it.n_r) return u32x4{0u, 0u, 0u, 0u};
+        return *reinterpret_cast<const u32x4*>(
+            v + (it.row0 + static_cast<int64_t>(u) * row_step) * D + ch * 8);
+    };
+    // The whole window of an item into ring slots 0..W-1 (synchronous; caller barriers).
+    auto fill_window = [&](const Item& it) {
+        constexpr int kBatch = 9;                           // pieces in flight per thread
+        for (int x0 = 0; x0 < kPerWinV; x0 += kBatch) {
+            u32x4 buf[kBatch];
+#pragma unroll
+            for (int x = 0; x < kBatch; ++x) {
+                const int idx = tid + (x0 + x) * kThreads, rr = idx / kChunks, ch = idx % kChunks;
+                if (rr < it.W) buf[x] = get_v(it, rr, ch);
+            }
+#pragma unroll
+            for (int x = 0; x < kBatch; ++x) {
+                const int idx = tid + (x0 + x) * kThreads, rr = idx / kChunks, ch = idx % kChunks;
+                if (rr < it.W) put_v(rr, ch, buf[x]);
+            }
+        }
+    };
+    // The 64 new keys of a sliding next item (its window columns W-64 .. W-1).
+    auto load_new_v = [&](const Item& nx) {
+#pragma unroll
+        for (int x = 0; x < kPer64V; ++x) {
+            const int idx = tid + x * kThreads, rr = idx / kChunks, ch = idx % kChunks;
+            if (rr < kRows) vb[x] = get_v(nx, nx.W - kRows + rr, ch);
+        }
+    };
+    auto store_new_v = [&](int slot_first) {
+#pragma unroll
+        for (int x = 0; x < kPer64V; ++x) {
+            const int idx = tid + x * kThreads, rr = idx / kChunks, ch = idx % kChunks;
+            if (rr < kRows) {
+                int slot = slot_first + rr;
+                slot = slot < ringc ? slot : slot - ringc;
+                put_v(slot, ch, vb[x]);
+            }
+        }
+    };
+
+    f32x4 acc[kCBPerWave];
+#pragma unroll
+    for (int q = 0; q < kCBPerWave; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // band_ready: the current item's band is staged; v_ready: its key window is in the ring.
+    bool band_ready = false, v_ready = false;
+    int s0 = 0;                                             // ring slot of window column 0
+    Item it;
+    if (item < iend) describe(item, &it);
+    for (; item < iend; ++item) {
+        if (it.t0 >= it.n_r) {                              // empty block of a short class
+            band_ready = v_ready = false;
+            if (item + 1 < iend) describe(item + 1, &it);
+            continue;
+        }
+        if (!band_ready || !v_ready) {
+            if (!band_ready) load_band(it);
+            __syncthreads();                                // previous item done with LDS
+            if (!band_ready) store_band(it);
+            if (!v_ready) {
+                s0 = 0;
+                fill_window(it);
+            }
+            __syncthreads();
+        }
+        // Next item: fetch its band pieces (and new V rows if it slides) during compute.
+        Item nx;
+        bool has_next = item + 1 < iend;
+        if (has_next) {
+            describe(item + 1, &nx);
+            has_next = nx.t0 < nx.n_r;
+        }
+        const bool next_slides = has_next && a.g.nkb == 1 && nx.t.tb == it.t.tb + 1 &&
+                                 nx.t.r == it.t.r && nx.t.hh == it.t.hh && nx.t.bb == it.t.bb;
+        if (has_next) {
+            load_band(nx);
+            if (next_slides) load_new_v(nx);
+        }
+
+        // ---- compute: out^T[c][i] += sum_x VT[c][x] * B[x][i]
+        {
+            const int il = 16 * rb + col;                   // this lane's query row
+            const int x_lo = 16 * rb;                       // window columns this block uses
+            const int x_hi = 16 * rb + 15 + it.kbeff;       // exclusive
+            const int jc_lo = x_lo / 32, jc_hi = (x_hi + 31) / 32;
+            const int srow = il * rsp + kMargin;
+            int64_t gl;
+            int shl, ncl;
+            band_geom(it, il < it.rows_here ? il : 0, &gl, &shl, &ncl);
+            const ST* prow = pst + srow + shl;              // staged slot 0 of this row
+            const bool key_edge = it.u0 < 0 || it.u0 + it.W > it.n_r;
+            for (int jc = jc_lo; jc < jc_hi; ++jc) {
+                const int x0 = 32 * jc + 8 * grp;           // first window column of lane
+                // B operand: B[x0 + e][il] = P[il][x0 + e - il]
+                uint32_t bw[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    uint32_t lohi = 0;
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int e = 2 * e2 + hf;
+                        const int slot = x0 + e - il;
+                        bool ok = slot >= 0 && slot < it.kbeff;
+                        if (key_edge) {
+                            const int u = it.u0 + x0 + e;
+                            ok = ok && u >= 0 && u < it.n_r;
+                        }
+                        const uint32_t val = ok ? static_cast<uint32_t>(
+                                                      __builtin_bit_cast(uint16_t, prow[ok ? slot : 0]))
+                                                : 0u;
+                        lohi |= val << (16 * hf);
+                    }
+                    bw[e2] = lohi;
+                }
+                const V bop = __builtin_bit_cast(V, u32x4{bw[0], bw[1], bw[2], bw[3]});
+                int slot0 = s0 + x0;
+                slot0 = slot0 < ringc ? slot0 : slot0 - ringc;
+#pragma unroll
+                for (int q = 0; q < kCBPerWave; ++q) {
+                    const int c = 16 * (cb0 + q) + col;
+                    const V aop = *reinterpret_cast<const V*>(vt + c * ringc + slot0);
+                    acc[q] = Mfma<In>::run(aop, bop, acc[q]);
+                }
+            }
+        }
+
+        // ---- last chunk of the tile: write the outputs and clear the accumulators
+        const bool tile_done = it.t.kb == a.g.nkb - 1;
+        if (tile_done) {
+            const int il = 16 * rb + col;
+            if (il < it.rows_here) {
+                const int64_t orow = (it.row0 + static_cast<int64_t>(it.t0 + il) * row_step) * D;
+#pragma unroll
+                for (int q = 0; q < kCBPerWave; ++q) {
+                    const int c = 16 * (cb0 + q) + 4 * grp;
+                    if (out_f32) {
+                        float* o = static_cast<float*>(out_raw) + orow + c;
+                        *reinterpret_cast<f32x4*>(o) = acc[q];
+                    } else {
+                        ST* o = static_cast<ST*>(out_raw) + orow + c;
+                        u32x2 pk;
+                        if constexpr (sizeof(ST) == 2 && __is_same(In, F16))
+                            pk = __builtin_bit_cast(u32x2, __builtin_convertvector(acc[q], f16x4));
+                        else
+                            pk = __builtin_bit_cast(u32x2, __builtin_convertvector(acc[q], bf16x4));
+                        *reinterpret_cast<u32x2*>(o) = pk;
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kCBPerWave; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+        __syncthreads();                                    // all LDS reads of this item done
+        if (has_next) {
+            store_band(nx);
+            if (next_slides) {
+                store_new_v(s0 + it.W);                     // slots past the current window
+                s0 += kRows;
+                s0 = s0 < ringc ? s0 : s0 - ringc;
+            }
+            __syncthreads();
+            band_ready = true;
+            v_ready = next_slides;
+            it = nx;
+        } else {
+            band_ready = v_ready = false;
+            if (item + 1 < iend) describe(item + 1, &it);
+        }
+    }
+}
+
+struct PvLayout {
+    int64_t kc = 0, rsp = 0, ring = 0, ring_off = 0, bytes = 0;
+};
+
+PvLayout pv_layout(int64_t kc, int64_t d) {
+    PvLayout l;
+    l.kc = kc;
+    l.rsp = ceil_div(kMargin + kc + 16, 8) * 8;
+    const int64_t need = 2 * kRows + kc - 1;               // window + 64 prefetched keys
+    l.ring = ceil_div(need - 8, 128) * 128 + 8;             // = 8 mod 128 (bank spread)
+    l.ring_off = ceil_div(kRows * l.rsp * 2, 16) * 16;
+    l.bytes = l.ring_off + d * l.ring * 2;
+    return l;
+}
+
+template <class In, int D>
+hipError_t launch_typed(const void* band, const void* v, void* out, bool out_f32,
+                        const Problem& p, const PvTilePlan& tp, hipStream_t stream) {
+    const PvLayout l = pv_layout(tp.grid.kb, D);
+    PvArgs a{p.n, p.h, p.K, p.w, p.s, tp.grid, static_cast<int32_t>(l.rsp),
+             static_cast<int32_t>(l.ring), static_cast<int32_t>(l.ring_off),
+             static_cast<uint32_t>(tp.workgroups)};
+    auto kern = pv_mfma_kernel<In, D>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+        static_cast<int>(kPvLdsBytes));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(tp.workgroups)), dim3(kThreads),
+                       static_cast<size_t>(l.bytes), stream,
+                       static_cast<const typename In::T*>(band),
+                       static_cast<const typename In::T*>(v), out, out_f32 ? 1 : 0, a);
+    return hipGetLastError();
+}
+
+template <class In>
+hipError_t launch_d(const void* band, const void* v, void* out, bool out_f32,
+                    const Problem& p, const PvTilePlan& tp, hipStream_t stream) {
+    switch (p.d) {
+    case 32: return launch_typed<In, 32>(band, v, out, out_f32, p, tp, stream);
+    case 64: return launch_typed<In, 64>(band, v, out, out_f32, p, tp, stream);
+    case 128: return launch_typed<In, 128>(band, v, out, out_f32, p, tp, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+PvTilePlan plan_pv_mfma(const Problem& p) {
+    PvTilePlan tp;
+    int64_t kc = kMaxChunk;
+    while (kc > 16 && pv_layout(kc, p.d).bytes > kPvLdsBytes) --kc;
+    // tiles: (b, h, res, row block) x chunks; TileGrid.nkb counts chunks
+    tp.grid = make_grid(p.b, p.n, p.h, p.K, p.s, kRows, kc);
+    const PvLayout l = pv_layout(tp.grid.kb, p.d);
+    tp.lds_bytes = l.bytes;
+    const int64_t cus = device_cus();
+    tp.workgroups = tp.grid.tiles < cus ? tp.grid.tiles : cus;
+    tp.ok = tp.grid.tiles <= kMaxTiles && ceil_div(p.n, p.s) < (int64_t(1) << 30) &&
+            p.K < (int64_t(1) << 30) && l.bytes <= kPvLdsBytes && tp.workgroups >= 1 &&
+            (p.d == 32 || p.d == 64 || p.d == 128);
+    return tp;
+}
+
+hipError_t launch_pv_mfma(const void* band, const void* v, void* out, const Problem& p,
+                          const PvTilePlan& tp, int in_dt, int out_dt, hipStream_t stream) {
+    const bool f32 = out_dt == kF32;
+    if (in_dt == kF16) return launch_d<F16>(band, v, out, f32, p, tp, stream);
+    if (in_dt == kBF16) return launch_d<BF16>(band, v, out, f32, p, tp, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace diagmm

@@ -56,9 +56,22 @@ Plan plan_qk(const Problem& p, int in_dt, int out_dt) {
 }
 
 Plan plan_pv(const Problem& p, int in_dt, int out_dt) {
-    (void)in_dt;
     (void)out_dt;
-    return simple_plan(p, p.d, "pv_simple");
+    if (force_simple() || !mfma_dtype(in_dt) || !mfma_depth(p.d))
+        return simple_plan(p, p.d, "pv_simple");
+    const PvTilePlan tp = plan_pv_mfma(p);
+    if (!tp.ok) return simple_plan(p, p.d, "pv_simple");
+    Plan pl;
+    pl.family = Family::kPvMfma;
+    pl.kernel = "pv_mfma";
+    pl.rows_per_tile = kPvRows;
+    pl.slots_per_tile = tp.grid.kb;
+    pl.tiles = tp.grid.tiles;
+    pl.workgroups = tp.workgroups;
+    pl.threads = 512;
+    pl.lds_bytes = tp.lds_bytes;
+    pl.residues = tp.grid.res;
+    return pl;
 }
 
 Plan plan_pvT(const Problem& p, int in_dt, int out_dt) {
@@ -101,7 +114,8 @@ hipError_t run_qk(const Plan& plan, const void* q, const void* k, void* band, co
 
 hipError_t run_pv(const Plan& plan, const void* band, const void* v, void* out, const Problem& p,
                   int in_dt, int out_dt, hipStream_t stream) {
-    (void)plan;
+    if (plan.family == Family::kPvMfma && aligned16(band) && aligned16(v) && aligned16(out))
+        return launch_pv_mfma(band, v, out, p, plan_pv_mfma(p), in_dt, out_dt, stream);
     return launch_pv_simple(band, v, out, p, in_dt, out_dt, stream);
 }
 

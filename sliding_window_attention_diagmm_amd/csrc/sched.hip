@@ -75,9 +75,22 @@ Plan plan_pv(const Problem& p, int in_dt, int out_dt) {
 }
 
 Plan plan_pvT(const Problem& p, int in_dt, int out_dt) {
-    (void)in_dt;
     (void)out_dt;
-    return simple_plan(p, p.d, "pvT_simple");
+    if (force_simple() || !mfma_dtype(in_dt) || !mfma_depth(p.d))
+        return simple_plan(p, p.d, "pvT_simple");
+    const PvTilePlan tp = plan_pvt_mfma(p);
+    if (!tp.ok) return simple_plan(p, p.d, "pvT_simple");
+    Plan pl;
+    pl.family = Family::kPvTMfma;
+    pl.kernel = "pvT_mfma";
+    pl.rows_per_tile = kPvTRows;
+    pl.slots_per_tile = tp.grid.kb;
+    pl.tiles = tp.grid.tiles;
+    pl.workgroups = tp.workgroups;
+    pl.threads = 512;
+    pl.lds_bytes = tp.lds_bytes;
+    pl.residues = tp.grid.res;
+    return pl;
 }
 
 Plan plan_softmax(const Problem& p, int in_dt, int out_dt) {
@@ -121,7 +134,8 @@ hipError_t run_pv(const Plan& plan, const void* band, const void* v, void* out, 
 
 hipError_t run_pvT(const Plan& plan, const void* band, const void* x, void* out,
                    const Problem& p, int in_dt, int out_dt, hipStream_t stream) {
-    (void)plan;
+    if (plan.family == Family::kPvTMfma && aligned16(band) && aligned16(x) && aligned16(out))
+        return launch_pvt_mfma(band, x, out, p, plan_pvt_mfma(p), in_dt, out_dt, stream);
     return launch_pvT_simple(band, x, out, p, in_dt, out_dt, stream);
 }
 

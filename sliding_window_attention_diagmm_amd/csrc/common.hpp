@@ -71,6 +71,33 @@ __device__ __forceinline__ uint32_t load_part_dword(const ST* gp, int j, int a, 
     }
 }
 
+// Mask of the elements of dword j that lie in [a, b) (all ones / zeros per element).
+template <class ST>
+__device__ __forceinline__ uint32_t keep_mask(int j, int a, int b) {
+    if constexpr (sizeof(ST) == 4) return (a <= j && j < b) ? 0xffffffffu : 0u;
+    return ((a <= 2 * j && 2 * j < b) ? 0x0000ffffu : 0u) |
+           ((a <= 2 * j + 1 && 2 * j + 1 < b) ? 0xffff0000u : 0u);
+}
+
+typedef uint32_t piece_t __attribute__((ext_vector_type(4)));
+
+// Keep elements [a, b) of a loaded 16-byte piece, zero the others.  Kept apart from the
+// load itself so that a prefetch can issue whole-piece loads and mask them only when the
+// data is consumed: using a loaded value right away would wait for every load in flight.
+template <class ST>
+__device__ __forceinline__ piece_t mask_piece(const piece_t& v, int a, int b) {
+    return piece_t{v[0] & keep_mask<ST>(0, a, b), v[1] & keep_mask<ST>(1, a, b),
+                   v[2] & keep_mask<ST>(2, a, b), v[3] & keep_mask<ST>(3, a, b)};
+}
+
+// Elements [a, b) of a piece read one by one (for a piece that runs past the end of its
+// tensor); the others read as zero.
+template <class ST>
+__device__ __forceinline__ piece_t load_piece_elems(const ST* gp, int a, int b) {
+    return piece_t{load_part_dword<ST>(gp, 0, a, b), load_part_dword<ST>(gp, 1, a, b),
+                   load_part_dword<ST>(gp, 2, a, b), load_part_dword<ST>(gp, 3, a, b)};
+}
+
 // Store elements [a, b) of a piece whose dwords are d0..d3.
 template <class ST>
 __device__ __forceinline__ void store_part(ST* gp, uint32_t d0, uint32_t d1, uint32_t d2,

@@ -18,10 +18,12 @@
 // into it as they arrive (keys outside the sequence are written as zeros).  The band
 // rows of the current item are copied in as aligned 16-byte pieces of the band tensor
 // (LDS and HBM agree on alignment: row il starts at il * RSP + margin + its offset
-// modulo 8).  The B operand - 8 consecutive keys of one query row, i.e. 8 consecutive
-// band slots of that row starting at an arbitrary slot - is gathered with 2-byte LDS
-// reads; slots outside the chunk or whose key lies outside the sequence read as 0, by
-// index, whatever the band holds there.
+// modulo 8).  Pieces are masked as they are written: slots outside the chunk, or whose
+// key lies outside the sequence, are stored as 0 whatever the band holds there, and
+// every position a B read can reach beyond the row's slots (the lead-in margin, zeroed
+// once, and a tail of zero pieces) holds 0 as well.  So the B operand - 8 consecutive
+// keys of one query row, i.e. 8 consecutive band slots of that row starting at an
+// arbitrary slot - is eight unconditional 2-byte LDS reads.
 //
 // Compute.  Wave w owns query block rb = w / 2 (16 rows) and channel blocks
 // cb = 2 (w % 2), 2 (w % 2) + 1; for every 32-key chunk of the window that its rows reach
@@ -60,10 +62,15 @@ template <> struct Mfma<BF16> {
 
 constexpr int kThreads = 512;
 constexpr int kRows = kPvRows;             // 64 query rows per tile
-constexpr int kMargin = 16;                // band staging lead-in (elements)
 constexpr int kMaxChunk = 513;             // slots per chunk
 constexpr int kMaxWin = kRows + kMaxChunk - 1;
-constexpr int kBandPieces = (kRows * ((kMaxChunk + 14) / 8 + 1) + kThreads - 1) / kThreads;
+// Band staging row: B reads of row il reach slots -31 .. KC + 45 (window columns
+// 32 floor(16 rb / 32) .. 32 ceil((16 rb + 15 + KC) / 32) - 1 against il = 16 rb + 0..15),
+// staged at margin + (offset mod 8) + slot.
+constexpr int kMargin = 32;                // zero lead-in (elements)
+constexpr int kSlotTail = 46;              // slots read past the chunk's last one
+__host__ __device__ constexpr int band_pieces(int kc) { return (7 + kc + kSlotTail + 7) / 8; }
+constexpr int kBandPieces = (kRows * band_pieces(kMaxChunk) + kThreads - 1) / kThreads;
 
 struct PvArgs {
     int64_t n, h, K, w, s;
@@ -72,6 +79,7 @@ struct PvArgs {
     int32_t ring;          // V ring capacity in key slots (multiple of 8)
     int32_t ring_off;      // LDS byte offset of the V ring
     uint32_t nwg;
+    int64_t band_elems;    // elements of the band tensor
 };
 
 // One work item = (tile, chunk); items run with the chunk fastest, so a tile's chunks
@@ -106,6 +114,7 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
     const int64_t n = a.n, h = a.h, K = a.K, s = a.s;
     const int64_t row_step = s * h;
     const int rsp = a.rsp, ringc = a.ring;
+    const ST* band_end = band + a.band_elems;               // one past the band tensor
     const int rb = wave >> 1;                               // this wave's query block
     const int cb0 = (wave & 1) * kCBPerWave;                // first channel block
 
@@ -121,6 +130,10 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
     // multiplied by exact zeros), so no slot may ever hold a non-finite pattern.
     for (int x = tid; x < D * ringc / 8; x += kThreads)
         reinterpret_cast<u32x4*>(vt)[x] = u32x4{0u, 0u, 0u, 0u};
+    // The staging lead-in margins are read (as zeros) and never written afterwards.
+    for (int x = tid; x < kRows * (kMargin / 8); x += kThreads)
+        reinterpret_cast<u32x4*>(pst + (x / (kMargin / 8)) * rsp)[x % (kMargin / 8)] =
+            u32x4{0u, 0u, 0u, 0u};
 
     auto describe = [&](int64_t id, Item* it) {
         const int64_t nkb = a.g.nkb;
@@ -150,31 +163,22 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
         *sh = static_cast<int>(*g & 7);
         *nc = (*sh + it.kbeff + 7) / 8;
     };
-    const int ncmax_glob = (7 + a.g.kb + 7) / 8;
+    const int npw = band_pieces(a.g.kb);                    // pieces per staged row
 
+    // Whole pieces are loaded as they lie in the band tensor and masked only when written
+    // to LDS, so the prefetch issues no wait; a piece that runs past the end of the tensor
+    // is read element-wise at that point instead.
     auto load_band = [&](const Item& it) {
 #pragma unroll
         for (int x = 0; x < kBandPieces; ++x) {
             const int idx = tid + x * kThreads;
-            const int il = idx / ncmax_glob, c = idx - il * ncmax_glob;
+            const int il = idx / npw, c = idx - il * npw;
             if (il < it.rows_here) {
                 int64_t g;
                 int sh, nc;
                 band_geom(it, il, &g, &sh, &nc);
-                if (c < nc) {
-                    const int lo = c * 8 - sh;                 // slot of element 0
-                    const ST* gp = band + (g - sh) + c * 8;
-                    if (lo >= 0 && lo + 8 <= it.kbeff) {
-                        pb[x] = *reinterpret_cast<const u32x4*>(gp);
-                    } else {
-                        const int pa = lo < 0 ? -lo : 0;
-                        const int pe = it.kbeff - lo < 8 ? it.kbeff - lo : 8;
-                        pb[x] = u32x4{load_part_dword<ST>(gp, 0, pa, pe),
-                                      load_part_dword<ST>(gp, 1, pa, pe),
-                                      load_part_dword<ST>(gp, 2, pa, pe),
-                                      load_part_dword<ST>(gp, 3, pa, pe)};
-                    }
-                }
+                const ST* gp = band + (g - sh) + c * 8;
+                if (c < nc && gp + 8 <= band_end) pb[x] = *reinterpret_cast<const u32x4*>(gp);
             }
         }
     };
@@ -182,13 +186,30 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
 #pragma unroll
         for (int x = 0; x < kBandPieces; ++x) {
             const int idx = tid + x * kThreads;
-            const int il = idx / ncmax_glob, c = idx - il * ncmax_glob;
+            const int il = idx / npw, c = idx - il * npw;
             if (il < it.rows_here) {
                 int64_t g;
                 int sh, nc;
                 band_geom(it, il, &g, &sh, &nc);
-                if (c < nc)
-                    *reinterpret_cast<u32x4*>(pst + il * rsp + kMargin + c * 8) = pb[x];
+                u32x4 val = u32x4{0u, 0u, 0u, 0u};
+                if (c < nc) {
+                    // kept slots: inside the chunk and with key u0 + il + slot in [0, n_r)
+                    const int key0 = it.u0 + il;
+                    const int va = -key0 > 0 ? -key0 : 0;
+                    const int vb = it.n_r - key0 < it.kbeff ? it.n_r - key0 : it.kbeff;
+                    const int lo = c * 8 - sh;                  // slot of element 0
+                    const int pa = va - lo, pe = vb - lo;
+                    if (pa < 8 && pe > 0 && pa < pe) {
+                        const ST* gp = band + (g - sh) + c * 8;
+                        if (gp + 8 <= band_end) {
+                            val = mask_piece<ST>(pb[x], pa, pe);
+                        } else {
+                            const int lim = static_cast<int>(band_end - gp);
+                            val = load_piece_elems<ST>(gp, pa, pe < lim ? pe : lim);
+                        }
+                    }
+                }
+                *reinterpret_cast<u32x4*>(pst + il * rsp + kMargin + c * 8) = val;
             }
         }
     };
@@ -294,44 +315,40 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
             const int x_lo = 16 * rb;                       // window columns this block uses
             const int x_hi = 16 * rb + 15 + it.kbeff;       // exclusive
             const int jc_lo = x_lo / 32, jc_hi = (x_hi + 31) / 32;
-            const int srow = il * rsp + kMargin;
             int64_t gl;
             int shl, ncl;
             band_geom(it, il < it.rows_here ? il : 0, &gl, &shl, &ncl);
-            const ST* prow = pst + srow + shl;              // staged slot 0 of this row
-            const bool key_edge = it.u0 < 0 || it.u0 + it.W > it.n_r;
-            for (int jc = jc_lo; jc < jc_hi; ++jc) {
-                const int x0 = 32 * jc + 8 * grp;           // first window column of lane
-                // B operand: B[x0 + e][il] = P[il][x0 + e - il]
+            // brow[x] = B[x][il] = P[il][x - il] for every window column x this lane reads
+            const uint16_t* brow =
+                reinterpret_cast<const uint16_t*>(pst + il * rsp + kMargin + shl - il) + 8 * grp;
+            const uint16_t* arow[kCBPerWave];
+#pragma unroll
+            for (int q = 0; q < kCBPerWave; ++q)
+                arow[q] = reinterpret_cast<const uint16_t*>(vt + (16 * (cb0 + q) + col) * ringc);
+            auto fetch = [&](int jc, V* bop, V* aop) {
+                const uint16_t* bp = brow + 32 * jc;
                 uint32_t bw[4];
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    uint32_t lohi = 0;
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const int e = 2 * e2 + hf;
-                        const int slot = x0 + e - il;
-                        bool ok = slot >= 0 && slot < it.kbeff;
-                        if (key_edge) {
-                            const int u = it.u0 + x0 + e;
-                            ok = ok && u >= 0 && u < it.n_r;
-                        }
-                        const uint32_t val = ok ? static_cast<uint32_t>(
-                                                      __builtin_bit_cast(uint16_t, prow[ok ? slot : 0]))
-                                                : 0u;
-                        lohi |= val << (16 * hf);
-                    }
-                    bw[e2] = lohi;
-                }
-                const V bop = __builtin_bit_cast(V, u32x4{bw[0], bw[1], bw[2], bw[3]});
-                int slot0 = s0 + x0;
+                for (int e2 = 0; e2 < 4; ++e2)
+                    bw[e2] = static_cast<uint32_t>(bp[2 * e2]) |
+                             (static_cast<uint32_t>(bp[2 * e2 + 1]) << 16);
+                *bop = __builtin_bit_cast(V, u32x4{bw[0], bw[1], bw[2], bw[3]});
+                int slot0 = s0 + 32 * jc + 8 * grp;             // ring slot of column x0
                 slot0 = slot0 < ringc ? slot0 : slot0 - ringc;
 #pragma unroll
-                for (int q = 0; q < kCBPerWave; ++q) {
-                    const int c = 16 * (cb0 + q) + col;
-                    const V aop = *reinterpret_cast<const V*>(vt + c * ringc + slot0);
-                    acc[q] = Mfma<In>::run(aop, bop, acc[q]);
-                }
+                for (int q = 0; q < kCBPerWave; ++q)
+                    aop[q] = *reinterpret_cast<const V*>(arow[q] + slot0);
+            };
+            V bcur, acur[kCBPerWave];
+            fetch(jc_lo, &bcur, acur);
+            for (int jc = jc_lo; jc < jc_hi; ++jc) {
+                V bnx, anx[kCBPerWave];
+                fetch(jc + 1 < jc_hi ? jc + 1 : jc, &bnx, anx);   // next operands in flight
+#pragma unroll
+                for (int q = 0; q < kCBPerWave; ++q) acc[q] = Mfma<In>::run(acur[q], bcur, acc[q]);
+                bcur = bnx;
+#pragma unroll
+                for (int q = 0; q < kCBPerWave; ++q) acur[q] = anx[q];
             }
         }
 
@@ -388,7 +405,7 @@ struct PvLayout {
 PvLayout pv_layout(int64_t kc, int64_t d) {
     PvLayout l;
     l.kc = kc;
-    l.rsp = ceil_div(kMargin + kc + 16, 8) * 8;
+    l.rsp = kMargin + 8 * band_pieces(static_cast<int>(kc));
     const int64_t need = 2 * kRows + kc - 1;               // window + 64 prefetched keys
     l.ring = ceil_div(need - 8, 128) * 128 + 8;             // = 8 mod 128 (bank spread)
     l.ring_off = ceil_div(kRows * l.rsp * 2, 16) * 16;
@@ -402,7 +419,7 @@ hipError_t launch_typed(const void* band, const void* v, void* out, bool out_f32
     const PvLayout l = pv_layout(tp.grid.kb, D);
     PvArgs a{p.n, p.h, p.K, p.w, p.s, tp.grid, static_cast<int32_t>(l.rsp),
              static_cast<int32_t>(l.ring), static_cast<int32_t>(l.ring_off),
-             static_cast<uint32_t>(tp.workgroups)};
+             static_cast<uint32_t>(tp.workgroups), p.rows() * p.h * p.K};
     auto kern = pv_mfma_kernel<In, D>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -71,6 +71,7 @@ struct PvTArgs {
     int32_t ring;          // X ring capacity in band rows (multiple of 8)
     int32_t ring_off;      // LDS byte offset of the X ring
     uint32_t nwg;
+    int64_t band_elems;
 };
 
 struct Item {
@@ -104,6 +105,7 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
     const int64_t n = a.n, h = a.h, K = a.K, s = a.s;
     const int64_t row_step = s * h;
     const int ringc = a.ring;
+    const ST* band_end = band + a.band_elems;
     const int blk0 = wave * kBPW;
     const bool wave_busy = blk0 < kBlocks;
     const int jb = blk0 / kCB;                              // this wave's 16-row group
@@ -140,46 +142,55 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
     // of which [max(k0, sa), min(k0 + kbeff, sa + 32)) belong to the chunk.  Its 16-byte
     // pieces start at global element gs - sh, gs = (row0 + i * row_step) * K + sa.
     u32x4 sb[kSegPer];
+    // Piece q of this thread: its global address and the element range [a0, b0) that
+    // belongs to the chunk; false for pieces outside the window or the sequence.
+    auto seg_geom = [&](const Item& it, int q, const ST** gp, int* a0, int* b0, int* xr_out) {
+        const int idx = tid + q * kThreads;
+        const int xr = idx / kSegPieces, pc = idx - xr * kSegPieces;
+        *xr_out = xr;
+        if (xr >= it.W) return false;
+        const int i = it.ilo + xr;
+        if (i < 0 || i >= it.n_r) return false;
+        const int64_t sa = static_cast<int64_t>(it.j0) - i + a.w;
+        const int64_t gs = (it.row0 + static_cast<int64_t>(i) * row_step) * K + sa;
+        const int sh = static_cast<int>(gs & 7);
+        const int64_t lo_slot = sa - sh + 8 * pc;          // slot of element 0
+        const int64_t va = it.k0 > sa ? it.k0 : sa;
+        const int64_t vb_ = (it.k0 + it.kbeff) < (sa + kRows) ? (it.k0 + it.kbeff) : (sa + kRows);
+        const int64_t pa = va - lo_slot, pe = vb_ - lo_slot;   // valid [pa, pe)
+        if (pe <= 0 || pa >= 8) return false;
+        *gp = band + (gs - sh) + 8 * pc;
+        *a0 = pa > 0 ? static_cast<int>(pa) : 0;
+        *b0 = pe < 8 ? static_cast<int>(pe) : 8;
+        return true;
+    };
+    // Prefetch whole pieces only; masking (and any piece that runs past the end of the
+    // tensor) waits for store_seg, so the loads stay in flight during compute.
     auto load_seg = [&](const Item& it) {
 #pragma unroll
         for (int q = 0; q < kSegPer; ++q) {
-            const int idx = tid + q * kThreads;
-            const int xr = idx / kSegPieces, pc = idx - xr * kSegPieces;
-            sb[q] = u32x4{0u, 0u, 0u, 0u};
-            if (xr < it.W) {
-                const int i = it.ilo + xr;
-                if (i >= 0 && i < it.n_r) {
-                    const int64_t sa = static_cast<int64_t>(it.j0) - i + a.w;
-                    const int64_t gs = (it.row0 + static_cast<int64_t>(i) * row_step) * K + sa;
-                    const int sh = static_cast<int>(gs & 7);
-                    const int64_t lo_slot = sa - sh + 8 * pc;      // slot of element 0
-                    const int64_t va = it.k0 > sa ? it.k0 : sa;
-                    const int64_t vb_ = (it.k0 + it.kbeff) < (sa + kRows) ? (it.k0 + it.kbeff)
-                                                                         : (sa + kRows);
-                    const int64_t pa = va - lo_slot, pe = vb_ - lo_slot;   // valid [pa, pe)
-                    if (pe > 0 && pa < 8) {
-                        const ST* gp = band + (gs - sh) + 8 * pc;
-                        if (pa <= 0 && pe >= 8) {
-                            sb[q] = *reinterpret_cast<const u32x4*>(gp);
-                        } else {
-                            const int a0 = pa > 0 ? static_cast<int>(pa) : 0;
-                            const int b0 = pe < 8 ? static_cast<int>(pe) : 8;
-                            sb[q] = u32x4{load_part_dword<ST>(gp, 0, a0, b0),
-                                          load_part_dword<ST>(gp, 1, a0, b0),
-                                          load_part_dword<ST>(gp, 2, a0, b0),
-                                          load_part_dword<ST>(gp, 3, a0, b0)};
-                        }
-                    }
-                }
-            }
+            const ST* gp = nullptr;
+            int a0 = 0, b0 = 0, xr = 0;
+            if (seg_geom(it, q, &gp, &a0, &b0, &xr) && gp + 8 <= band_end)
+                sb[q] = *reinterpret_cast<const u32x4*>(gp);
         }
     };
     auto store_seg = [&](const Item& it) {
 #pragma unroll
         for (int q = 0; q < kSegPer; ++q) {
-            const int idx = tid + q * kThreads;
-            const int xr = idx / kSegPieces, pc = idx - xr * kSegPieces;
-            if (xr < it.W) *reinterpret_cast<u32x4*>(seg + xr * kRss + 8 * pc) = sb[q];
+            const ST* gp = nullptr;
+            int a0 = 0, b0 = 0, xr = 0;
+            u32x4 val = u32x4{0u, 0u, 0u, 0u};
+            if (seg_geom(it, q, &gp, &a0, &b0, &xr)) {
+                if (gp + 8 <= band_end) {
+                    val = mask_piece<ST>(sb[q], a0, b0);
+                } else {
+                    const int lim = static_cast<int>(band_end - gp);
+                    val = load_piece_elems<ST>(gp, a0, b0 < lim ? b0 : lim);
+                }
+            }
+            const int pc = tid + q * kThreads - xr * kSegPieces;
+            if (xr < it.W) *reinterpret_cast<u32x4*>(seg + xr * kRss + 8 * pc) = val;
         }
     };
 
@@ -374,7 +385,8 @@ hipError_t launch_typed(const void* band, const void* x, void* out, bool out_f32
                         const Problem& p, const PvTilePlan& tp, hipStream_t stream) {
     const PvTLayout l = pvt_layout(tp.grid.kb, D);
     PvTArgs a{p.n, p.h, p.K, p.w, p.s, tp.grid, static_cast<int32_t>(l.ring),
-              static_cast<int32_t>(l.ring_off), static_cast<uint32_t>(tp.workgroups)};
+              static_cast<int32_t>(l.ring_off), static_cast<uint32_t>(tp.workgroups),
+              p.rows() * p.h * p.K};
     auto kern = pvt_mfma_kernel<In, D>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,

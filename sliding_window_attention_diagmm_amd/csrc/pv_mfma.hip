@@ -16,14 +16,13 @@
 // LDS.  V is kept transposed, VT[c][slot], in a ring of key slots, so the MFMA A operand
 // (16 channels x 8 consecutive keys) is one aligned 16-byte read; new rows are scattered
 // into it as they arrive (keys outside the sequence are written as zeros).  The band
-// rows of the current item are copied in as aligned 16-byte pieces of the band tensor
-// (LDS and HBM agree on alignment: row il starts at il * RSP + margin + its offset
-// modulo 8).  Pieces are masked as they are written: slots outside the chunk, or whose
-// key lies outside the sequence, are stored as 0 whatever the band holds there, and
-// every position a B read can reach beyond the row's slots (the lead-in margin, zeroed
-// once, and a tail of zero pieces) holds 0 as well.  So the B operand - 8 consecutive
-// keys of one query row, i.e. 8 consecutive band slots of that row starting at an
-// arbitrary slot - is eight unconditional 2-byte LDS reads.
+// rows of the current item are staged already skewed into window coordinates,
+// S[il][x] = P[il][x - il] (0 outside the chunk, and where the key lies outside the
+// sequence), so that the B operand - 8 consecutive keys of one query row - is one aligned
+// 16-byte LDS read as well.  The skew is paid in the global loads instead: staged piece
+// (il, x .. x + 7) is the 16 bytes of the band tensor starting at slot x - il of row il,
+// read at 2-byte alignment.  LDS reads at 2-byte alignment are several times slower than
+// aligned ones on this hardware; global loads at that alignment cost little more.
 //
 // Compute.  Wave w owns query block rb = w / 2 (16 rows) and channel blocks
 // cb = 2 (w % 2), 2 (w % 2) + 1; for every 32-key chunk of the window that its rows reach
@@ -64,12 +63,10 @@ constexpr int kThreads = 512;
 constexpr int kRows = kPvRows;             // 64 query rows per tile
 constexpr int kMaxChunk = 513;             // slots per chunk
 constexpr int kMaxWin = kRows + kMaxChunk - 1;
-// Band staging row: B reads of row il reach slots -31 .. KC + 45 (window columns
-// 32 floor(16 rb / 32) .. 32 ceil((16 rb + 15 + KC) / 32) - 1 against il = 16 rb + 0..15),
-// staged at margin + (offset mod 8) + slot.
-constexpr int kMargin = 32;                // zero lead-in (elements)
-constexpr int kSlotTail = 46;              // slots read past the chunk's last one
-__host__ __device__ constexpr int band_pieces(int kc) { return (7 + kc + kSlotTail + 7) / 8; }
+// Staged band row: window columns 0 .. XW - 1, XW = 32 ceil((63 + KC) / 32), which covers
+// every column a B read reaches (block rb reads 32 floor(16 rb / 32) up to
+// 32 ceil((16 rb + 15 + KC) / 32) - 1); 16-byte pieces per row:
+__host__ __device__ constexpr int band_pieces(int kc) { return (63 + kc + 31) / 32 * 4; }
 constexpr int kBandPieces = (kRows * band_pieces(kMaxChunk) + kThreads - 1) / kThreads;
 
 struct PvArgs {
@@ -80,6 +77,8 @@ struct PvArgs {
     int32_t ring_off;      // LDS byte offset of the V ring
     uint32_t nwg;
     int64_t band_elems;    // elements of the band tensor
+    TileDecode dc;         // whole tiles (units) over workgroups, unit -> coordinates
+    Div32 chunks;          // item -> (unit, chunk)
 };
 
 // One work item = (tile, chunk); items run with the chunk fastest, so a tile's chunks
@@ -113,36 +112,31 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
     const int col = lane & 15, grp = lane >> 4;
     const int64_t n = a.n, h = a.h, K = a.K, s = a.s;
     const int64_t row_step = s * h;
+    const int64_t row_k = row_step * K;                     // band elements between rows
     const int rsp = a.rsp, ringc = a.ring;
-    const ST* band_end = band + a.band_elems;               // one past the band tensor
     const int rb = wave >> 1;                               // this wave's query block
     const int cb0 = (wave & 1) * kCBPerWave;                // first channel block
 
     // Whole tiles per workgroup (a tile's chunks share its accumulators), items = chunks.
-    int64_t item, iend;
+    uint32_t item, iend;
     {
-        int64_t tb, te;
-        tile_range(a.g.tiles / a.g.nkb, xcd_rank(blockIdx.x, a.nwg), a.nwg, &tb, &te);
-        item = tb * a.g.nkb;
-        iend = te * a.g.nkb;
+        uint32_t ub, ue;
+        unit_range(a.dc, xcd_rank(blockIdx.x, a.nwg), &ub, &ue);
+        item = ub * a.chunks.d;
+        iend = ue * a.chunks.d;
     }
     // Zero the V ring once: window columns past the current window are read (and
     // multiplied by exact zeros), so no slot may ever hold a non-finite pattern.
     for (int x = tid; x < D * ringc / 8; x += kThreads)
         reinterpret_cast<u32x4*>(vt)[x] = u32x4{0u, 0u, 0u, 0u};
-    // The staging lead-in margins are read (as zeros) and never written afterwards.
-    for (int x = tid; x < kRows * (kMargin / 8); x += kThreads)
-        reinterpret_cast<u32x4*>(pst + (x / (kMargin / 8)) * rsp)[x % (kMargin / 8)] =
-            u32x4{0u, 0u, 0u, 0u};
 
-    auto describe = [&](int64_t id, Item* it) {
-        const int64_t nkb = a.g.nkb;
-        const int kc = static_cast<int>(id % nkb);
-        TileId t = decode_tile(TileGrid{a.g.res, a.g.rb, 1, a.g.kb, a.g.tiles / nkb}, h,
-                               static_cast<uint32_t>(id / nkb));
+    auto describe = [&](uint32_t id, Item* it) {
+        const uint32_t unit = div32(a.chunks, id);
+        const int kc = static_cast<int>(id - unit * a.chunks.d);
+        TileId t = decode_fast(a.dc, unit);
         t.kb = kc;
         it->t = t;
-        it->n_r = static_cast<int>(class_len(n, s, t.r));
+        it->n_r = class_len_fast(a.dc, t.r);
         it->t0 = t.tb * kRows;
         it->rows_here = it->n_r - it->t0 < kRows ? it->n_r - it->t0 : kRows;
         it->k0 = static_cast<int64_t>(kc) * a.g.kb;
@@ -157,60 +151,98 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
     u32x4 pb[kBandPieces];
     u32x4 vb[kPer64V];
 
-    // Band pieces of an item: rows il < rows_here, pieces c < nc(il) of slots [k0, k0+kbeff).
-    auto band_geom = [&](const Item& it, int il, int64_t* g, int* sh, int* nc) {
-        *g = (it.row0 + static_cast<int64_t>(it.t0 + il) * row_step) * K + it.k0;
-        *sh = static_cast<int>(*g & 7);
-        *nc = (*sh + it.kbeff + 7) / 8;
-    };
     const int npw = band_pieces(a.g.kb);                    // pieces per staged row
+    const float inv_npw = 1.0f / static_cast<float>(npw);
+    // Piece x of this thread is (il, q): staged row il, window columns 8q .. 8q+7, i.e.
+    // slots lo .. lo+7 with lo = 8q - il.  idx / npw by a float reciprocal is exact here:
+    // idx < 2^13, so the error is far below the 1/(2 npw) margin around the integers.
+    auto piece_of = [&](int x, int* il, int* lo) {
+        const int idx = tid + x * kThreads;
+        const int r = static_cast<int>((static_cast<float>(idx) + 0.5f) * inv_npw);
+        *il = r;
+        *lo = 8 * (idx - r * npw) - r;
+    };
+    // Slots of row il that take part: inside the chunk, key u0 + il + slot in [0, n_r).
+    auto valid_slots = [&](const Item& it, int il, int* va, int* vb) {
+        const int key0 = it.u0 + il;
+        *va = -key0 > 0 ? -key0 : 0;
+        *vb = it.n_r - key0 < it.kbeff ? it.n_r - key0 : it.kbeff;
+    };
+    // Global element of slot 0 of row 0 of an item, and whether every piece that meets
+    // the chunk (slots -7 .. kbeff + 6 of its rows) lies inside the band tensor.
+    auto item_base = [&](const Item& it, bool* inside) {
+        const int64_t base = (it.row0 + static_cast<int64_t>(it.t0) * row_step) * K + it.k0;
+        *inside = base >= 7 &&
+                  base + (it.rows_here - 1) * row_k + it.kbeff + 7 <= a.band_elems;
+        return base;
+    };
 
-    // Whole pieces are loaded as they lie in the band tensor and masked only when written
-    // to LDS, so the prefetch issues no wait; a piece that runs past the end of the tensor
-    // is read element-wise at that point instead.
+    // Pieces that meet a row's valid slots are loaded whole (2-byte aligned) and staged
+    // raw; pieces that do not are staged as zeros.  The valid slots of a row are one
+    // interval, so at most two staged pieces per row (head and tail) hold stray elements;
+    // clear_strays zeroes those afterwards.  So the prefetch issues no wait and staging is
+    // a handful of ALU operations per piece.  On the first and last tiles of the tensor a
+    // piece may reach past its ends: there, only elements inside the tensor are read, one
+    // by one, when staging.
+    typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+    // il * row_k as one 32 x 32 -> 64-bit multiply (row_k < 2^32 is a plan condition)
+    auto row_off = [&](int il) {
+        return static_cast<int64_t>(static_cast<uint64_t>(il) * static_cast<uint32_t>(row_k));
+    };
     auto load_band = [&](const Item& it) {
+        bool inside;
+        const int64_t base = item_base(it, &inside);
 #pragma unroll
         for (int x = 0; x < kBandPieces; ++x) {
-            const int idx = tid + x * kThreads;
-            const int il = idx / npw, c = idx - il * npw;
-            if (il < it.rows_here) {
-                int64_t g;
-                int sh, nc;
-                band_geom(it, il, &g, &sh, &nc);
-                const ST* gp = band + (g - sh) + c * 8;
-                if (c < nc && gp + 8 <= band_end) pb[x] = *reinterpret_cast<const u32x4*>(gp);
+            int il, lo;
+            piece_of(x, &il, &lo);
+            if (il < it.rows_here && lo + 8 > 0 && lo < it.kbeff) {
+                const int64_t off = base + row_off(il) + lo;
+                if (inside || (off >= 0 && off + 8 <= a.band_elems))
+                    pb[x] = *reinterpret_cast<const u32x4_a2*>(band + off);
             }
         }
     };
     auto store_band = [&](const Item& it) {
+        bool inside;
+        const int64_t base = item_base(it, &inside);
 #pragma unroll
         for (int x = 0; x < kBandPieces; ++x) {
-            const int idx = tid + x * kThreads;
-            const int il = idx / npw, c = idx - il * npw;
+            int il, lo, va, vb;
+            piece_of(x, &il, &lo);
             if (il < it.rows_here) {
-                int64_t g;
-                int sh, nc;
-                band_geom(it, il, &g, &sh, &nc);
+                valid_slots(it, il, &va, &vb);
                 u32x4 val = u32x4{0u, 0u, 0u, 0u};
-                if (c < nc) {
-                    // kept slots: inside the chunk and with key u0 + il + slot in [0, n_r)
-                    const int key0 = it.u0 + il;
-                    const int va = -key0 > 0 ? -key0 : 0;
-                    const int vb = it.n_r - key0 < it.kbeff ? it.n_r - key0 : it.kbeff;
-                    const int lo = c * 8 - sh;                  // slot of element 0
-                    const int pa = va - lo, pe = vb - lo;
-                    if (pa < 8 && pe > 0 && pa < pe) {
-                        const ST* gp = band + (g - sh) + c * 8;
-                        if (gp + 8 <= band_end) {
-                            val = mask_piece<ST>(pb[x], pa, pe);
-                        } else {
-                            const int lim = static_cast<int>(band_end - gp);
-                            val = load_piece_elems<ST>(gp, pa, pe < lim ? pe : lim);
-                        }
+                if (lo + 8 > va && lo < vb) {
+                    const int64_t off = base + row_off(il) + lo;
+                    if (inside || (off >= 0 && off + 8 <= a.band_elems)) {
+                        val = pb[x];
+                    } else {                                // elements [ea, eb) in the tensor
+                        const int ea = off < 0 ? static_cast<int>(-off) : 0;
+                        const int64_t room = a.band_elems - off;
+                        const int eb = room < 8 ? static_cast<int>(room) : 8;
+                        val = load_piece_elems<ST>(band + off, ea, eb);
                     }
                 }
-                *reinterpret_cast<u32x4*>(pst + il * rsp + kMargin + c * 8) = val;
+                *reinterpret_cast<u32x4*>(pst + il * rsp + lo + il) = val;
             }
+        }
+    };
+    // Zero the stray elements of the head and tail pieces of every staged row: window
+    // columns [8 floor(xa / 8), xa) and [xb, 8 ceil(xb / 8)), where [xa, xb) = il + valid
+    // slots.  Task (il, k): k < 8 clears head column 8 floor(xa / 8) + k, k >= 8 tail
+    // column xb + k - 8 (both stay inside the row: xb <= 63 + kbeff < XW).  Runs after the
+    // pieces are written (a barrier in between).
+    auto clear_strays = [&](const Item& it) {
+        for (int task = tid; task < kRows * 16; task += kThreads) {
+            const int il = task >> 4, k = task & 15;
+            if (il >= it.rows_here) continue;
+            int va, vb;
+            valid_slots(it, il, &va, &vb);
+            const int xa = il + va, xb = il + vb;
+            const int x = k < 8 ? (xa & ~7) + k : xb + (k - 8);
+            const bool stray = k < 8 ? x < xa : (x & ~7) == (xb & ~7);
+            if (stray) reinterpret_cast<uint16_t*>(pst)[il * rsp + x] = 0;
         }
     };
     // Scatter one 16-byte piece of V row `slot` (channels ch*8 .. ch*8+7) into VT.
@@ -288,10 +320,14 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
         if (!band_ready || !v_ready) {
             if (!band_ready) load_band(it);
             __syncthreads();                                // previous item done with LDS
-            if (!band_ready) store_band(it);
-            if (!v_ready) {
+            if (!v_ready) {                                 // its loads overlap the band's
                 s0 = 0;
                 fill_window(it);
+            }
+            if (!band_ready) {
+                store_band(it);
+                __syncthreads();
+                clear_strays(it);
             }
             __syncthreads();
         }
@@ -315,41 +351,42 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
             const int x_lo = 16 * rb;                       // window columns this block uses
             const int x_hi = 16 * rb + 15 + it.kbeff;       // exclusive
             const int jc_lo = x_lo / 32, jc_hi = (x_hi + 31) / 32;
-            int64_t gl;
-            int shl, ncl;
-            band_geom(it, il < it.rows_here ? il : 0, &gl, &shl, &ncl);
             // brow[x] = B[x][il] = P[il][x - il] for every window column x this lane reads
-            const uint16_t* brow =
-                reinterpret_cast<const uint16_t*>(pst + il * rsp + kMargin + shl - il) + 8 * grp;
-            const uint16_t* arow[kCBPerWave];
+            const ST* brow = pst + il * rsp + 8 * grp;
+            const uint16_t* arow[kCBPerWave];   // this lane's channel rows of VT
 #pragma unroll
             for (int q = 0; q < kCBPerWave; ++q)
                 arow[q] = reinterpret_cast<const uint16_t*>(vt + (16 * (cb0 + q) + col) * ringc);
             auto fetch = [&](int jc, V* bop, V* aop) {
-                const uint16_t* bp = brow + 32 * jc;
-                uint32_t bw[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2)
-                    bw[e2] = static_cast<uint32_t>(bp[2 * e2]) |
-                             (static_cast<uint32_t>(bp[2 * e2 + 1]) << 16);
-                *bop = __builtin_bit_cast(V, u32x4{bw[0], bw[1], bw[2], bw[3]});
+                *bop = *reinterpret_cast<const V*>(brow + 32 * jc);
                 int slot0 = s0 + 32 * jc + 8 * grp;             // ring slot of column x0
                 slot0 = slot0 < ringc ? slot0 : slot0 - ringc;
 #pragma unroll
                 for (int q = 0; q < kCBPerWave; ++q)
                     aop[q] = *reinterpret_cast<const V*>(arow[q] + slot0);
             };
-            V bcur, acur[kCBPerWave];
-            fetch(jc_lo, &bcur, acur);
-            for (int jc = jc_lo; jc < jc_hi; ++jc) {
-                V bnx, anx[kCBPerWave];
-                fetch(jc + 1 < jc_hi ? jc + 1 : jc, &bnx, anx);   // next operands in flight
+            auto mma = [&](const V& bop, const V* aop) {
 #pragma unroll
-                for (int q = 0; q < kCBPerWave; ++q) acc[q] = Mfma<In>::run(acur[q], bcur, acc[q]);
-                bcur = bnx;
-#pragma unroll
-                for (int q = 0; q < kCBPerWave; ++q) acur[q] = anx[q];
+                for (int q = 0; q < kCBPerWave; ++q) acc[q] = Mfma<In>::run(aop[q], bop, acc[q]);
+            };
+            // Two operand sets in turn: the next chunk's reads are issued before the
+            // current one multiplies.  The empty asm with a memory clobber keeps the
+            // compiler from folding the loop-carried reads back into reads at their use;
+            // the scheduling barrier keeps the reads ahead of the MFMAs.
+            V b0, b1, a0[kCBPerWave], a1[kCBPerWave];
+            fetch(jc_lo, &b0, a0);
+            int jc = jc_lo;
+            for (; jc + 1 < jc_hi; jc += 2) {
+                fetch(jc + 1, &b1, a1);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                mma(b0, a0);
+                fetch(jc + 2 < jc_hi ? jc + 2 : jc + 1, &b0, a0);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                mma(b1, a1);
             }
+            if (jc < jc_hi) mma(b0, a0);
         }
 
         // ---- last chunk of the tile: write the outputs and clear the accumulators
@@ -388,6 +425,8 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
                 s0 = s0 < ringc ? s0 : s0 - ringc;
             }
             __syncthreads();
+            clear_strays(nx);
+            __syncthreads();
             band_ready = true;
             v_ready = next_slides;
             it = nx;
@@ -405,12 +444,20 @@ struct PvLayout {
 PvLayout pv_layout(int64_t kc, int64_t d) {
     PvLayout l;
     l.kc = kc;
-    l.rsp = kMargin + 8 * band_pieces(static_cast<int>(kc));
+    l.rsp = 8 * band_pieces(static_cast<int>(kc)) + 8;    // odd multiple of 16 bytes
     const int64_t need = 2 * kRows + kc - 1;               // window + 64 prefetched keys
     l.ring = ceil_div(need - 8, 128) * 128 + 8;             // = 8 mod 128 (bank spread)
     l.ring_off = ceil_div(kRows * l.rsp * 2, 16) * 16;
     l.bytes = l.ring_off + d * l.ring * 2;
     return l;
+}
+
+// Units are whole tiles (all chunks of one row block), decoded with one chunk per tile.
+TileDecode unit_decode(const PvTilePlan& tp, const Problem& p) {
+    const TileGrid& g = tp.grid;
+    const int64_t units = g.tiles / g.nkb;
+    return make_decode(TileGrid{g.res, g.rb, 1, g.kb, units}, p.h, p.n, p.s, units,
+                       tp.workgroups);
 }
 
 template <class In, int D>
@@ -419,7 +466,8 @@ hipError_t launch_typed(const void* band, const void* v, void* out, bool out_f32
     const PvLayout l = pv_layout(tp.grid.kb, D);
     PvArgs a{p.n, p.h, p.K, p.w, p.s, tp.grid, static_cast<int32_t>(l.rsp),
              static_cast<int32_t>(l.ring), static_cast<int32_t>(l.ring_off),
-             static_cast<uint32_t>(tp.workgroups), p.rows() * p.h * p.K};
+             static_cast<uint32_t>(tp.workgroups), p.rows() * p.h * p.K,
+             unit_decode(tp, p), make_div32(static_cast<uint32_t>(tp.grid.nkb))};
     auto kern = pv_mfma_kernel<In, D>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -457,6 +505,7 @@ PvTilePlan plan_pv_mfma(const Problem& p) {
     tp.workgroups = tp.grid.tiles < cus ? tp.grid.tiles : cus;
     tp.ok = tp.grid.tiles <= kMaxTiles && ceil_div(p.n, p.s) < (int64_t(1) << 30) &&
             p.K < (int64_t(1) << 30) && l.bytes <= kPvLdsBytes && tp.workgroups >= 1 &&
+            p.s * p.h * p.K < (int64_t(1) << 32) &&
             (p.d == 32 || p.d == 64 || p.d == 128);
     return tp;
 }

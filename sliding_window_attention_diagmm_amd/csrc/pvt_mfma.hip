@@ -72,6 +72,8 @@ struct PvTArgs {
     int32_t ring_off;      // LDS byte offset of the X ring
     uint32_t nwg;
     int64_t band_elems;
+    TileDecode dc;         // whole tiles (units) over workgroups, unit -> coordinates
+    Div32 chunks;          // item -> (unit, chunk)
 };
 
 struct Item {
@@ -111,24 +113,23 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
     const int jb = blk0 / kCB;                              // this wave's 16-row group
     const int cb0 = blk0 % kCB;
 
-    int64_t item, iend;
+    uint32_t item, iend;
     {
-        int64_t tb, te;
-        tile_range(a.g.tiles / a.g.nkb, xcd_rank(blockIdx.x, a.nwg), a.nwg, &tb, &te);
-        item = tb * a.g.nkb;
-        iend = te * a.g.nkb;
+        uint32_t ub, ue;
+        unit_range(a.dc, xcd_rank(blockIdx.x, a.nwg), &ub, &ue);
+        item = ub * a.chunks.d;
+        iend = ue * a.chunks.d;
     }
     for (int q = tid; q < D * ringc / 8; q += kThreads)
         reinterpret_cast<u32x4*>(xt)[q] = u32x4{0u, 0u, 0u, 0u};
 
-    auto describe = [&](int64_t id, Item* it) {
-        const int64_t nkb = a.g.nkb;
-        const int kc = static_cast<int>(id % nkb);
-        TileId t = decode_tile(TileGrid{a.g.res, a.g.rb, 1, a.g.kb, a.g.tiles / nkb}, h,
-                               static_cast<uint32_t>(id / nkb));
+    auto describe = [&](uint32_t id, Item* it) {
+        const uint32_t unit = div32(a.chunks, id);
+        const int kc = static_cast<int>(id - unit * a.chunks.d);
+        TileId t = decode_fast(a.dc, unit);
         t.kb = kc;
         it->t = t;
-        it->n_r = static_cast<int>(class_len(n, s, t.r));
+        it->n_r = class_len_fast(a.dc, t.r);
         it->j0 = t.tb * kRows;
         it->rows_here = it->n_r - it->j0 < kRows ? it->n_r - it->j0 : kRows;
         it->k0 = static_cast<int64_t>(kc) * a.g.kb;
@@ -380,13 +381,22 @@ PvTLayout pvt_layout(int64_t kc, int64_t d) {
     return l;
 }
 
+// Units are whole tiles (all chunks of one row block), decoded with one chunk per tile.
+TileDecode unit_decode(const PvTilePlan& tp, const Problem& p) {
+    const TileGrid& g = tp.grid;
+    const int64_t units = g.tiles / g.nkb;
+    return make_decode(TileGrid{g.res, g.rb, 1, g.kb, units}, p.h, p.n, p.s, units,
+                       tp.workgroups);
+}
+
 template <class In, int D>
 hipError_t launch_typed(const void* band, const void* x, void* out, bool out_f32,
                         const Problem& p, const PvTilePlan& tp, hipStream_t stream) {
     const PvTLayout l = pvt_layout(tp.grid.kb, D);
     PvTArgs a{p.n, p.h, p.K, p.w, p.s, tp.grid, static_cast<int32_t>(l.ring),
               static_cast<int32_t>(l.ring_off), static_cast<uint32_t>(tp.workgroups),
-              p.rows() * p.h * p.K};
+              p.rows() * p.h * p.K, unit_decode(tp, p),
+              make_div32(static_cast<uint32_t>(tp.grid.nkb))};
     auto kern = pvt_mfma_kernel<In, D>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -106,6 +106,7 @@ struct QkArgs {
     int32_t q_off;     // LDS byte offset of the query tile
     uint32_t nwg;      // persistent workgroups
     uint32_t pad;      // padding constant, already rounded to the output type
+    TileDecode dc;     // tiles over workgroups, tile -> coordinates
 };
 
 // Byte offset of (row, 16-byte chunk) in a swizzled block of D-element rows.  The chunk
@@ -151,8 +152,8 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
     const int rs = a.rs, ringc = a.ring;
     const P padv = Pack<Out>::splat(a.pad);
 
-    int64_t tile, tend;
-    tile_range(a.g.tiles, xcd_rank(blockIdx.x, a.nwg), a.nwg, &tile, &tend);
+    uint32_t tile, tend;
+    unit_range(a.dc, xcd_rank(blockIdx.x, a.nwg), &tile, &tend);
 
     // Registers carrying the next tile's new key rows and query rows.
     u32x4 kn[kPer64], qn[kPer64];
@@ -163,8 +164,8 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
     const int ebase = col * rs + kMargin + (col & 3) - col + 4 * grp;
 
     for (; tile < tend; ++tile) {
-        const TileId t = decode_tile(a.g, h, static_cast<uint32_t>(tile));
-        const int n_r = static_cast<int>(class_len(n, s, t.r));
+        const TileId t = decode_fast(a.dc, tile);
+        const int n_r = class_len_fast(a.dc, t.r);
         const int t0 = t.tb * kRows;
         if (t0 >= n_r) {           // empty tail block of a shorter residue class
             prefetched = false;
@@ -217,7 +218,7 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
         // Does the next tile continue this strip?  Then fetch its new rows now.
         bool next = false;
         if (tile + 1 < tend) {
-            const TileId tn = decode_tile(a.g, h, static_cast<uint32_t>(tile + 1));
+            const TileId tn = decode_fast(a.dc, tile + 1);
             next = tn.tb == t.tb + 1 && tn.kb == t.kb && tn.r == t.r && tn.hh == t.hh &&
                    tn.bb == t.bb && t0 + kRows < n_r;
         }
@@ -409,7 +410,8 @@ hipError_t launch_typed(const void* q, const void* k, void* band, const Problem&
     const Layout l = layout_for(tp.grid.kb, D, sizeof(typename Out::T));
     QkArgs a{p.n, p.h, p.K, p.w, p.s, tp.grid, static_cast<int32_t>(l.rs),
              static_cast<int32_t>(l.ring), static_cast<int32_t>(l.ring_off),
-             static_cast<int32_t>(l.q_off), static_cast<uint32_t>(tp.workgroups), pad};
+             static_cast<int32_t>(l.q_off), static_cast<uint32_t>(tp.workgroups), pad,
+             make_decode(tp.grid, p.h, p.n, p.s, tp.grid.tiles, tp.workgroups)};
     auto kern = qk_mfma_kernel<In, Out, D>;
     // Once per instantiation (thread-safe static initialisation): allow all of the
     // compute unit's LDS as dynamic LDS.

@@ -89,4 +89,86 @@ __host__ __device__ inline int64_t class_len(int64_t n, int64_t s, int64_t r) {
     return r < n ? (n - r + s - 1) / s : 0;
 }
 
+// Exact n / d for 0 <= n < 2^31 and 1 <= d < 2^31 by one multiply: with
+// 2^(sh-1) < d <= 2^sh, k = 32 + sh and m = floor(2^k / d) + 1, m d = 2^k + e with
+// 0 < e <= d, so n m / 2^k = n / d + n e / (d 2^k) and n e < 2^31 2^sh = 2^(k-1) keeps
+// the excess below 1/d: the floor is unchanged (the round-up method of Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994).
+struct Div32 {
+    uint64_t m;
+    uint32_t d, k;
+};
+
+inline Div32 make_div32(uint32_t d) {
+    uint32_t sh = 0;
+    while ((uint64_t(1) << sh) < d) ++sh;
+    Div32 v;
+    v.d = d;
+    v.k = 32 + sh;
+    v.m = static_cast<uint64_t>((static_cast<unsigned __int128>(1) << v.k) / d) + 1;
+    return v;
+}
+
+__host__ __device__ inline uint32_t div32(const Div32& v, uint32_t n) {
+    const uint64_t lo = static_cast<uint64_t>(n) * static_cast<uint32_t>(v.m);
+    const uint64_t hi = static_cast<uint64_t>(n) * static_cast<uint32_t>(v.m >> 32);
+    // (hi << 32) + lo < 2^64: n < 2^31 and m < 2^33
+    return static_cast<uint32_t>(((hi << 32) + lo) >> v.k);
+}
+
+// Everything a persistent workgroup needs to walk its tiles without a division on the
+// device: reciprocals of the grid extents, the residue class lengths (n = q s + m, so
+// class r has q + (r < m) rows) and a balanced split of `units` (tiles, or whole tiles
+// of several chunks) over the workgroups.
+struct TileDecode {
+    Div32 rb, nkb, res, h;
+    uint32_t cls_q, cls_m;
+    uint32_t unit_base, unit_rem;
+};
+
+inline TileDecode make_decode(const TileGrid& g, int64_t h, int64_t n, int64_t s,
+                              int64_t units, int64_t nwg) {
+    TileDecode t;
+    t.rb = make_div32(static_cast<uint32_t>(g.rb));
+    t.nkb = make_div32(static_cast<uint32_t>(g.nkb));
+    t.res = make_div32(static_cast<uint32_t>(g.res));
+    t.h = make_div32(static_cast<uint32_t>(h));
+    t.cls_q = static_cast<uint32_t>(n / s);
+    t.cls_m = static_cast<uint32_t>(n % s);
+    t.unit_base = static_cast<uint32_t>(units / nwg);
+    t.unit_rem = static_cast<uint32_t>(units % nwg);
+    return t;
+}
+
+// Tile id -> coordinates, as decode_tile (row block fastest).
+__host__ __device__ inline TileId decode_fast(const TileDecode& dc, uint32_t tile) {
+    TileId t;
+    uint32_t x = tile, y;
+    y = div32(dc.rb, x);
+    t.tb = static_cast<int32_t>(x - y * dc.rb.d);
+    x = y;
+    y = div32(dc.nkb, x);
+    t.kb = static_cast<int32_t>(x - y * dc.nkb.d);
+    x = y;
+    y = div32(dc.res, x);
+    t.r = static_cast<int32_t>(x - y * dc.res.d);
+    x = y;
+    y = div32(dc.h, x);
+    t.hh = static_cast<int32_t>(x - y * dc.h.d);
+    t.bb = static_cast<int32_t>(y);
+    return t;
+}
+
+__host__ __device__ inline int class_len_fast(const TileDecode& dc, int r) {
+    return static_cast<int>(dc.cls_q) + (static_cast<uint32_t>(r) < dc.cls_m ? 1 : 0);
+}
+
+// Units [begin, end) of rank `rank`: the first unit_rem ranks take one extra.
+__host__ __device__ inline void unit_range(const TileDecode& dc, uint32_t rank,
+                                           uint32_t* begin, uint32_t* end) {
+    const uint32_t extra = rank < dc.unit_rem ? rank : dc.unit_rem;
+    *begin = rank * dc.unit_base + extra;
+    *end = *begin + dc.unit_base + (rank < dc.unit_rem ? 1u : 0u);
+}
+
 }  // namespace diagmm

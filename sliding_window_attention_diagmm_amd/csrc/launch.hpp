@@ -25,7 +25,7 @@ hipError_t launch_softmax_wave(const void* scores, void* probs, const Problem& p
                                int dt, hipStream_t stream);
 
 // qk on MFMA (f16 / bf16 inputs, d in {32, 64, 128}, 16-byte aligned pointers).
-constexpr int kQkRows = 64;                  // rows per tile
+constexpr int kQkRows = 128;                 // rows per tile
 constexpr int64_t kQkLdsBytes = 160 * 1024;  // one workgroup per compute unit
 
 struct QkTilePlan {

@@ -54,8 +54,8 @@ struct PvTilePlan {
 
 PvTilePlan plan_pv_mfma(const Problem& p);
 
-// pvT on MFMA (same dtypes, depths and alignment as pv); tiles of 32 output rows.
-constexpr int kPvTRows = 32;
+// pvT on MFMA (same dtypes, depths and alignment as pv); tiles of 64 output rows.
+constexpr int kPvTRows = 64;
 PvTilePlan plan_pvt_mfma(const Problem& p);
 hipError_t launch_pvt_mfma(const void* band, const void* x, void* out, const Problem& p,
                            const PvTilePlan& tp, int in_dt, int out_dt, hipStream_t stream);

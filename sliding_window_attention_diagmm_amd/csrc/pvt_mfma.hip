@@ -5,29 +5,35 @@
 // (class-local rows of one residue class of the dilation).  In dense form out = B^T X
 // with B[i][j] = G[i][j - i + w] on the band; the kernel computes out^T = X^T B.
 //
-// Tiles.  A tile is 32 consecutive output rows j0..j0+31 of one residue class of one
+// Tiles.  A tile is 64 consecutive output rows j0..j0+63 of one residue class of one
 // (batch, head), processed per slot chunk [k0, k0 + KC) (one chunk unless the band is
 // wider than the LDS budget allows; the accumulators span the chunks).  The chunk's
-// contributions come from the W = 32 + KC - 1 band rows i = ilo .. ilo + W - 1,
-// ilo = j0 - k0 - KC + 1 + w, and from each such row only the 32 slots
-// [j0 - i + w, j0 + 31 - i + w] (a parallelogram through the band).
+// contributions come from the W = 64 + KC - 1 band rows i = ilo + x, x = 0 .. W-1,
+// ilo = j0 - k0 - KC + 1 + w ("window rows"), and from row x only the 64 slots
+// k0 + KC - 1 - x + j, j = 0..63 (a parallelogram through the band); output column j
+// takes rows x = j .. j + KC - 1.
 //
-// LDS.  X is kept transposed, XT[c][slot], in a ring over band rows (as V is in the pv
-// kernel), sliding by 32 rows per tile.  The parallelogram is staged row by row: the
-// segment of band row i is copied as aligned 16-byte pieces (five pieces cover 32 slots
-// at any alignment) into staging row x = i - ilo, keeping the band tensor's alignment;
-// elements outside the chunk, and rows outside the sequence, are stored as zeros.  For
-// output column j the element of row i sits at segment position j - j0 whatever i is,
-// so the MFMA B operand (8 consecutive band rows, one output column) is a fixed column
-// of 8 staged rows, gathered with 2-byte LDS reads.
+// LDS.  X is kept transposed, XT[c][x], in a ring over window rows (as V is in the pv
+// kernel), sliding by 64 rows per tile.  The parallelogram is staged row-major,
+// S[x][j] = G[ilo + x][k0 + KC - 1 - x + j]: each staged row is one 128-byte row of LDS,
+// filled with aligned 16-byte stores from 16-byte loads of the band tensor taken at
+// 2-byte alignment (the row-dependent skew is paid in the global loads, where it costs
+// little).  Elements outside the chunk, and rows outside the sequence, are stored as 0.
+// 16-byte pieces of a row are XOR-swizzled by row (piece q at q ^ 2 (x mod 4)), so the
+// stores of a row and the transposed reads below are free of bank conflicts.
 //
-// Compute.  The 32 x d output tile is 2 x (d/16) blocks of 16 x 16; each wave owns
-// blocks of one 16-row group jb and, for every 32-row chunk of the window its rows
-// reach, gathers one B operand and issues one v_mfma_f32_16x16x32 per channel block.
-// Lane (j = lane % 16, g = lane / 16) accumulates out[16 jb + j][16 cb + 4 g .. +3].
+// Compute.  The MFMA B operand of lane (j, g) is 8 consecutive window rows of one output
+// column: a column of S.  It is read with two ds_read_b64_tr_b16 (gfx950 transposing LDS
+// reads): in each 16-lane group lane t receives element t mod 4 of the 8-byte chunks read
+// by lanes 4 v + t / 4, v = 0..3, so lanes pointing at rows r + c / 4, columns
+// 4 (c mod 4) hand every lane 4 consecutive rows of its own column.  The 64 x d output
+// tile is 4 x (d/16) blocks of 16 x 16; wave w owns column block jb = w / 2 and half of
+// the channel blocks, and for every 32-row chunk of the window its columns reach issues
+// one v_mfma_f32_16x16x32_{f16,bf16} per channel block.  Lane (j = lane % 16,
+// g = lane / 16) accumulates out[j0 + 16 jb + j][16 cb + 4 g .. +3].
 //
-// Pipelining.  The next tile's segment pieces (and, when the window slides, its 32 new
-// X rows) load into registers while the current tile computes.
+// Pipelining.  The next tile's band pieces (and, when the window slides, its 64 new X
+// rows) load into registers while the current tile computes.
 #include "launch.hpp"
 #include "tiles.hpp"
 
@@ -41,6 +47,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <class In> struct Mfma;
 template <> struct Mfma<F16> {
@@ -57,18 +64,20 @@ template <> struct Mfma<BF16> {
 };
 
 constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
-constexpr int kRows = kPvTRows;                      // 32 output rows per tile
+constexpr int kRows = kPvTRows;                      // 64 output rows per tile
 constexpr int kMaxChunk = 513;
-constexpr int kMaxWin = kRows + kMaxChunk - 1;       // 544 band rows
-constexpr int kSegPieces = (7 + kRows + 7) / 8;      // 16-byte pieces per segment (5)
-constexpr int kRss = kSegPieces * 8;                 // staging row stride (elements)
-constexpr int kSegPer = (kMaxWin * kSegPieces + kThreads - 1) / kThreads;
+constexpr int kMaxWin = kRows + kMaxChunk - 1;       // 576 window rows
+// Staged rows: 0 .. XS - 1, XS = 32 ceil((63 + KC) / 32), every row a B read reaches
+// (column block jb reads rows 32 floor(16 jb / 32) .. 32 ceil((16 jb + 15 + KC) / 32) - 1);
+// rows at or past W are zero.
+__host__ __device__ constexpr int staged_rows(int kc) { return (63 + kc + 31) / 32 * 32; }
+constexpr int kRowBytes = kRows * 2;                 // 128-byte staged rows, 8 pieces
+constexpr int kSegPer = (staged_rows(kMaxChunk) * 8 + kThreads - 1) / kThreads;   // 9
 
 struct PvTArgs {
     int64_t n, h, K, w, s;
     TileGrid g;            // nkb / kb: slot chunks per tile and slots per chunk
-    int32_t ring;          // X ring capacity in band rows (multiple of 8)
+    int32_t ring;          // X ring capacity in window rows (= 8 mod 128)
     int32_t ring_off;      // LDS byte offset of the X ring
     uint32_t nwg;
     int64_t band_elems;
@@ -82,6 +91,9 @@ struct Item {
     int64_t k0, row0;
 };
 
+// Byte offset of piece q of staged row x (pieces XOR-swizzled by row).
+__device__ __forceinline__ int spiece(int x, int q) { return x * kRowBytes + 16 * (q ^ (2 * (x & 3))); }
+
 template <class In, int D>
 __global__ void __launch_bounds__(kThreads)
 pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __restrict__ x,
@@ -90,14 +102,13 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
     using V = typename Mfma<In>::V;
     constexpr int kChunks = D / 8;                          // 16-byte pieces per X row
     constexpr int kPerWinX = (kMaxWin * kChunks + kThreads - 1) / kThreads;
-    constexpr int kPer32X = (kRows * kChunks + kThreads - 1) / kThreads;
+    constexpr int kPer64X = (kRows * kChunks + kThreads - 1) / kThreads;
     constexpr int kCB = D / 16;
-    constexpr int kBlocks = (kRows / 16) * kCB;            // 16x16 output blocks
-    constexpr int kBPW = (kBlocks + kWaves - 1) / kWaves;  // blocks per wave
-    static_assert(kBPW == 1 || kCB % kBPW == 0, "a wave's blocks must share a row group");
+    static_assert(kCB >= 2 && kCB % 2 == 0, "d must be a multiple of 32");
+    constexpr int kCBPerWave = kCB / 2;
 
     extern __shared__ __align__(16) unsigned char lds[];
-    ST* seg = reinterpret_cast<ST*>(lds);                   // [kMaxWin][kRss]
+    unsigned char* seg = lds;                               // S[x][j], swizzled pieces
     ST* xt = reinterpret_cast<ST*>(lds + a.ring_off);       // XT[c][slot]
 
     const int tid = threadIdx.x;
@@ -106,12 +117,10 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
     const int col = lane & 15, grp = lane >> 4;
     const int64_t n = a.n, h = a.h, K = a.K, s = a.s;
     const int64_t row_step = s * h;
+    const int64_t row_k = row_step * K;                     // band elements between rows
     const int ringc = a.ring;
-    const ST* band_end = band + a.band_elems;
-    const int blk0 = wave * kBPW;
-    const bool wave_busy = blk0 < kBlocks;
-    const int jb = blk0 / kCB;                              // this wave's 16-row group
-    const int cb0 = blk0 % kCB;
+    const int jb = wave >> 1;                               // this wave's column block
+    const int cb0 = (wave & 1) * kCBPerWave;                // first channel block
 
     uint32_t item, iend;
     {
@@ -120,6 +129,8 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
         item = ub * a.chunks.d;
         iend = ue * a.chunks.d;
     }
+    // Zero the X ring once: window rows past the current window are read (and multiplied
+    // by exact zeros), so no slot may ever hold a non-finite pattern.
     for (int q = tid; q < D * ringc / 8; q += kThreads)
         reinterpret_cast<u32x4*>(xt)[q] = u32x4{0u, 0u, 0u, 0u};
 
@@ -139,59 +150,92 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
         it->row0 = (static_cast<int64_t>(t.bb) * n + t.r) * h + t.hh;
     };
 
-    // Segment of staging row xr (band row i = ilo + xr): slots [sa, sa + 32), sa = j0 - i + w,
-    // of which [max(k0, sa), min(k0 + kbeff, sa + 32)) belong to the chunk.  Its 16-byte
-    // pieces start at global element gs - sh, gs = (row0 + i * row_step) * K + sa.
+    // Registers carrying the next item's band pieces and, when its window slides, its 64
+    // new X rows.
     u32x4 sb[kSegPer];
-    // Piece q of this thread: its global address and the element range [a0, b0) that
-    // belongs to the chunk; false for pieces outside the window or the sequence.
-    auto seg_geom = [&](const Item& it, int q, const ST** gp, int* a0, int* b0, int* xr_out) {
-        const int idx = tid + q * kThreads;
-        const int xr = idx / kSegPieces, pc = idx - xr * kSegPieces;
-        *xr_out = xr;
-        if (xr >= it.W) return false;
-        const int i = it.ilo + xr;
-        if (i < 0 || i >= it.n_r) return false;
-        const int64_t sa = static_cast<int64_t>(it.j0) - i + a.w;
-        const int64_t gs = (it.row0 + static_cast<int64_t>(i) * row_step) * K + sa;
-        const int sh = static_cast<int>(gs & 7);
-        const int64_t lo_slot = sa - sh + 8 * pc;          // slot of element 0
-        const int64_t va = it.k0 > sa ? it.k0 : sa;
-        const int64_t vb_ = (it.k0 + it.kbeff) < (sa + kRows) ? (it.k0 + it.kbeff) : (sa + kRows);
-        const int64_t pa = va - lo_slot, pe = vb_ - lo_slot;   // valid [pa, pe)
-        if (pe <= 0 || pa >= 8) return false;
-        *gp = band + (gs - sh) + 8 * pc;
-        *a0 = pa > 0 ? static_cast<int>(pa) : 0;
-        *b0 = pe < 8 ? static_cast<int>(pe) : 8;
-        return true;
+    u32x4 xb[kPer64X];
+
+    // Piece p of this thread: staged row x = idx / 8, columns 8 q .. 8 q + 7 (q = idx % 8).
+    // Its elements are band elements E0 + x (row_k - 1) + 8 q + e, E0 = the element of
+    // row ilo at slot k0 + kbeff - 1; row x contributes columns [x - kbeff + 1, x].
+    typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+    auto item_e0 = [&](const Item& it, int* x_lo, int* x_hi, bool* inside) {
+        const int64_t e0 = (it.row0 + static_cast<int64_t>(it.ilo) * row_step) * K + it.k0 +
+                           it.kbeff - 1;
+        // window rows inside the sequence: ilo + x in [0, n_r)
+        *x_lo = -it.ilo > 0 ? -it.ilo : 0;
+        *x_hi = it.n_r - it.ilo < it.W ? it.n_r - it.ilo : it.W;
+        *inside = e0 + static_cast<int64_t>(*x_lo) * (row_k - 1) >= 0 &&
+                  e0 + static_cast<int64_t>(*x_hi - 1) * (row_k - 1) + kRows <= a.band_elems;
+        return e0;
     };
-    // Prefetch whole pieces only; masking (and any piece that runs past the end of the
-    // tensor) waits for store_seg, so the loads stay in flight during compute.
     auto load_seg = [&](const Item& it) {
+        int x_lo, x_hi;
+        bool inside;
+        const int64_t e0 = item_e0(it, &x_lo, &x_hi, &inside);
 #pragma unroll
-        for (int q = 0; q < kSegPer; ++q) {
-            const ST* gp = nullptr;
-            int a0 = 0, b0 = 0, xr = 0;
-            if (seg_geom(it, q, &gp, &a0, &b0, &xr) && gp + 8 <= band_end)
-                sb[q] = *reinterpret_cast<const u32x4*>(gp);
+        for (int p = 0; p < kSegPer; ++p) {
+            const int idx = tid + p * kThreads, xr = idx >> 3, q = idx & 7;
+            if (xr >= x_lo && xr < x_hi && 8 * q + 8 > xr - it.kbeff + 1 && 8 * q <= xr) {
+                const int64_t off = e0 + static_cast<int64_t>(xr) * (row_k - 1) + 8 * q;
+                if (inside || (off >= 0 && off + 8 <= a.band_elems))
+                    sb[p] = *reinterpret_cast<const u32x4_a2*>(band + off);
+            }
         }
     };
     auto store_seg = [&](const Item& it) {
+        int x_lo, x_hi;
+        bool inside;
+        const int64_t e0 = item_e0(it, &x_lo, &x_hi, &inside);
+        const int xs = staged_rows(a.g.kb);
 #pragma unroll
-        for (int q = 0; q < kSegPer; ++q) {
-            const ST* gp = nullptr;
-            int a0 = 0, b0 = 0, xr = 0;
-            u32x4 val = u32x4{0u, 0u, 0u, 0u};
-            if (seg_geom(it, q, &gp, &a0, &b0, &xr)) {
-                if (gp + 8 <= band_end) {
-                    val = mask_piece<ST>(sb[q], a0, b0);
-                } else {
-                    const int lim = static_cast<int>(band_end - gp);
-                    val = load_piece_elems<ST>(gp, a0, b0 < lim ? b0 : lim);
+        for (int p = 0; p < kSegPer; ++p) {
+            const int idx = tid + p * kThreads, xr = idx >> 3, q = idx & 7;
+            if (xr < xs) {
+                u32x4 val = u32x4{0u, 0u, 0u, 0u};
+                if (xr >= x_lo && xr < x_hi && 8 * q + 8 > xr - it.kbeff + 1 && 8 * q <= xr) {
+                    const int64_t off = e0 + static_cast<int64_t>(xr) * (row_k - 1) + 8 * q;
+                    if (inside || (off >= 0 && off + 8 <= a.band_elems)) {
+                        val = sb[p];
+                    } else {                                // elements [ea, eb) in the tensor
+                        const int ea = off < 0 ? static_cast<int>(-off) : 0;
+                        const int64_t room = a.band_elems - off;
+                        const int eb = room < 8 ? static_cast<int>(room) : 8;
+                        val = load_piece_elems<ST>(band + off, ea, eb);
+                    }
                 }
+                *reinterpret_cast<u32x4*>(seg + spiece(xr, q)) = val;
             }
-            const int pc = tid + q * kThreads - xr * kSegPieces;
-            if (xr < it.W) *reinterpret_cast<u32x4*>(seg + xr * kRss + 8 * pc) = val;
+        }
+    };
+    // Row x holds columns [max(0, x - kbeff + 1), min(64, x + 1)); the pieces it stages
+    // whole also carry elements of the neighbouring band rows in HBM on either side of
+    // that interval.  Only rows x < 63 (right end inside the tile) and x >= kbeff (left
+    // end inside) have them: task (r, k) zeroes column k of the right-end piece of row r,
+    // or of the left-end piece of row kbeff + r - 63, where stray.  Runs after the pieces
+    // are written (a barrier in between).
+    auto clear_strays = [&](const Item& it) {
+        int x_lo, x_hi;
+        bool inside;
+        item_e0(it, &x_lo, &x_hi, &inside);
+        for (int task = tid; task < 126 * 8; task += kThreads) {
+            const int r = task >> 3, k = task & 7;
+            const bool right = r < 63;
+            const int xr = right ? r : it.kbeff + r - 63;
+            if (xr < x_lo || xr >= x_hi) continue;
+            int c;
+            bool stray;
+            if (right) {
+                const int je = xr + 1;                      // first column past the row
+                c = (je & ~7) + k;
+                stray = c >= je && je < kRows;
+            } else {
+                const int ja = xr - it.kbeff + 1;           // first column of the row
+                c = (ja & ~7) + k;
+                stray = c < ja;
+            }
+            if (stray && c < kRows)
+                reinterpret_cast<uint16_t*>(seg + spiece(xr, c >> 3))[c & 7] = 0;
         }
     };
 
@@ -207,6 +251,7 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
         base[6 * ringc] = static_cast<uint16_t>(d3);
         base[7 * ringc] = static_cast<uint16_t>(d3 >> 16);
     };
+    // One 16-byte piece of X for window row xr of an item (zeros outside the sequence).
     auto get_x = [&](const Item& it, int xr, int ch) {
         const int i = it.ilo + xr;
         if (i < 0 || i >= it.n_r) return u32x4{0u, 0u, 0u, 0u};
@@ -229,17 +274,16 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
             }
         }
     };
-    u32x4 xb[kPer32X];
     auto load_new_x = [&](const Item& nx) {
 #pragma unroll
-        for (int q = 0; q < kPer32X; ++q) {
+        for (int q = 0; q < kPer64X; ++q) {
             const int idx = tid + q * kThreads, rr = idx / kChunks, ch = idx % kChunks;
             if (rr < kRows) xb[q] = get_x(nx, nx.W - kRows + rr, ch);
         }
     };
     auto store_new_x = [&](int slot_first) {
 #pragma unroll
-        for (int q = 0; q < kPer32X; ++q) {
+        for (int q = 0; q < kPer64X; ++q) {
             const int idx = tid + q * kThreads, rr = idx / kChunks, ch = idx % kChunks;
             if (rr < kRows) {
                 int slot = slot_first + rr;
@@ -249,9 +293,17 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
         }
     };
 
-    f32x4 acc[kBPW];
+    f32x4 acc[kCBPerWave];
 #pragma unroll
-    for (int q = 0; q < kBPW; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < kCBPerWave; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Transposed-read address of this lane for window rows 32 ic + 8 grp + e0 .. +3:
+    // row 32 ic + 8 grp + e0 + col / 4, columns 16 jb + 4 (col mod 4) .. +3 (bytes
+    // 8 (col mod 4) into the block's two pieces 2 jb, 2 jb + 1).  Rows 32 ic + 8 grp + e0
+    // are multiples of 4, so the swizzle depends on col / 4 only.
+    const int tr_row = 8 * grp + (col >> 2);
+    const int tr_off = tr_row * kRowBytes +
+                       16 * ((2 * jb + ((col & 3) >> 1)) ^ (2 * ((col >> 2) & 3))) + 8 * (col & 1);
 
     bool seg_ready = false, x_ready = false;
     int s0 = 0;
@@ -265,11 +317,15 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
         }
         if (!seg_ready || !x_ready) {
             if (!seg_ready) load_seg(it);
-            __syncthreads();
-            if (!seg_ready) store_seg(it);
-            if (!x_ready) {
+            __syncthreads();                                // previous item done with LDS
+            if (!x_ready) {                                 // its loads overlap the band's
                 s0 = 0;
                 fill_window(it);
+            }
+            if (!seg_ready) {
+                store_seg(it);
+                __syncthreads();
+                clear_strays(it);
             }
             __syncthreads();
         }
@@ -287,50 +343,59 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
         }
 
         // ---- compute: out^T[c][j] += sum_x XT[c][x] * B[x][j]
-        if (wave_busy) {
+        {
             const int x_lo = 16 * jb, x_hi = 16 * jb + 15 + it.kbeff;
             const int ic_lo = x_lo / 32, ic_hi = (x_hi + 31) / 32;
-            // shift of staging row xr: (gs mod 8) = (c0 + i * d1) mod 8 with i = ilo + xr
-            const int64_t c0 = (it.row0 * K + it.j0 + a.w) & 7;
-            const int64_t d1 = (row_step * K - 1) & 7;
-            const int jcol = 16 * jb + col;                 // segment position j - j0
-            for (int ic = ic_lo; ic < ic_hi; ++ic) {
-                uint32_t bw[4];
+            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+            const uint16_t* arow[kCBPerWave];               // this lane's channel rows of XT
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    uint32_t lohi = 0;
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const int xr = 32 * ic + 8 * grp + 2 * e2 + hf;
-                        const int i = it.ilo + xr;
-                        const int sh = static_cast<int>((c0 + static_cast<int64_t>(i) * d1) & 7);
-                        const bool ok = xr < it.W;
-                        const uint32_t val = ok ? static_cast<uint32_t>(__builtin_bit_cast(
-                                                      uint16_t, seg[(ok ? xr : 0) * kRss + sh + jcol]))
-                                                : 0u;
-                        lohi |= val << (16 * hf);
-                    }
-                    bw[e2] = lohi;
-                }
-                const V bop = __builtin_bit_cast(V, u32x4{bw[0], bw[1], bw[2], bw[3]});
+            for (int q = 0; q < kCBPerWave; ++q)
+                arow[q] = reinterpret_cast<const uint16_t*>(xt + (16 * (cb0 + q) + col) * ringc);
+            auto fetch = [&](int ic, V* bop, V* aop) {
+                unsigned char* bp = seg + ic * (32 * kRowBytes) + tr_off;
+                // (a C-style cast: the LDS address of a generic pointer into `lds`)
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bp));
+                const s16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bp + 4 * kRowBytes));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                *bop = __builtin_bit_cast(V, u32x4{l2[0], l2[1], h2[0], h2[1]});
                 int slot0 = s0 + 32 * ic + 8 * grp;
                 slot0 = slot0 < ringc ? slot0 : slot0 - ringc;
 #pragma unroll
-                for (int q = 0; q < kBPW; ++q) {
-                    const int c = 16 * (cb0 + q) + col;
-                    const V aop = *reinterpret_cast<const V*>(xt + c * ringc + slot0);
-                    acc[q] = Mfma<In>::run(aop, bop, acc[q]);
-                }
+                for (int q = 0; q < kCBPerWave; ++q)
+                    aop[q] = *reinterpret_cast<const V*>(arow[q] + slot0);
+            };
+            auto mma = [&](const V& bop, const V* aop) {
+#pragma unroll
+                for (int q = 0; q < kCBPerWave; ++q) acc[q] = Mfma<In>::run(aop[q], bop, acc[q]);
+            };
+            // Two operand sets in turn: the next chunk's reads are issued before the
+            // current one multiplies.  The empty asm with a memory clobber keeps the
+            // compiler from folding the loop-carried reads back into reads at their use;
+            // the scheduling barrier keeps the reads ahead of the MFMAs.
+            V b0, b1, a0[kCBPerWave], a1[kCBPerWave];
+            fetch(ic_lo, &b0, a0);
+            int ic = ic_lo;
+            for (; ic + 1 < ic_hi; ic += 2) {
+                fetch(ic + 1, &b1, a1);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                mma(b0, a0);
+                fetch(ic + 2 < ic_hi ? ic + 2 : ic + 1, &b0, a0);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                mma(b1, a1);
             }
+            if (ic < ic_hi) mma(b0, a0);
         }
 
         const bool tile_done = it.t.kb == a.g.nkb - 1;
         if (tile_done) {
             const int jl = 16 * jb + col;
-            if (wave_busy && jl < it.rows_here) {
+            if (jl < it.rows_here) {
                 const int64_t orow = (it.row0 + static_cast<int64_t>(it.j0 + jl) * row_step) * D;
 #pragma unroll
-                for (int q = 0; q < kBPW; ++q) {
+                for (int q = 0; q < kCBPerWave; ++q) {
                     const int c = 16 * (cb0 + q) + 4 * grp;
                     if (out_f32) {
                         *reinterpret_cast<f32x4*>(static_cast<float*>(out_raw) + orow + c) = acc[q];
@@ -345,17 +410,19 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
                 }
             }
 #pragma unroll
-            for (int q = 0; q < kBPW; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < kCBPerWave; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-        __syncthreads();
+        __syncthreads();                                    // all LDS reads of this item done
         if (has_next) {
             store_seg(nx);
             if (next_slides) {
-                store_new_x(s0 + it.W);
+                store_new_x(s0 + it.W);                     // slots past the current window
                 s0 += kRows;
                 s0 = s0 < ringc ? s0 : s0 - ringc;
             }
+            __syncthreads();
+            clear_strays(nx);
             __syncthreads();
             seg_ready = true;
             x_ready = next_slides;
@@ -374,9 +441,9 @@ struct PvTLayout {
 PvTLayout pvt_layout(int64_t kc, int64_t d) {
     PvTLayout l;
     l.kc = kc;
-    const int64_t need = 2 * kRows + kc - 1;               // window + 32 prefetched rows
+    const int64_t need = 2 * kRows + kc - 1;               // window + 64 prefetched rows
     l.ring = ceil_div(need - 8, 128) * 128 + 8;             // = 8 mod 128
-    l.ring_off = ceil_div((kRows + kc - 1) * kRss * 2, 16) * 16;
+    l.ring_off = static_cast<int64_t>(staged_rows(static_cast<int>(kc))) * kRowBytes;
     l.bytes = l.ring_off + d * l.ring * 2;
     return l;
 }

@@ -13,9 +13,13 @@
 // One 512-thread workgroup per compute unit walks a contiguous range of whole tiles, chunk
 // by chunk; single-chunk tiles that continue a strip slide the key window by 64.
 //
-// LDS.  V is kept transposed, VT[c][slot], in a ring of key slots, so the MFMA A operand
-// (16 channels x 8 consecutive keys) is one aligned 16-byte read; new rows are scattered
-// into it as they arrive (keys outside the sequence are written as zeros).  The band
+// LDS.  V is kept row-major in a ring of key slots (keys outside the sequence are
+// written as zeros), each row's 16-byte pieces XOR-swizzled by slot, so new rows go in
+// with aligned 16-byte stores.  The MFMA A operand (16 channels x 8 consecutive keys, a
+// transposed block of V) is read with two ds_read_b64_tr_b16: in each 16-lane group lane
+// t receives element t mod 4 of the 8-byte chunks read by lanes 4 v + t / 4, so lanes
+// pointing at slots r + c / 4, channels 16 cb + 4 (c mod 4) hand lane t keys r .. r + 3 of
+// channel 16 cb + t.  The swizzle keeps the four rows of such a read on distinct banks.  The band
 // rows of the current item are staged already skewed into window coordinates,
 // S[il][x] = P[il][x - il] (0 outside the chunk, and where the key lies outside the
 // sequence), so that the B operand - 8 consecutive keys of one query row - is one aligned
@@ -24,14 +28,15 @@
 // read at 2-byte alignment.  LDS reads at 2-byte alignment are several times slower than
 // aligned ones on this hardware; global loads at that alignment cost little more.
 //
-// Compute.  Wave w owns query block rb = w / 2 (16 rows) and channel blocks
-// cb = 2 (w % 2), 2 (w % 2) + 1; for every 32-key chunk of the window that its rows reach
-// it gathers one B operand and issues two v_mfma_f32_16x16x32_{f16,bf16}.  Lane
-// (i = lane % 16, g = lane / 16) accumulates out[16 rb + i][16 cb + 4 g .. +3].
+// Compute.  Wave w owns query block rb = w / 2 (16 rows) and half of the channel blocks;
+// for every 32-key chunk of the window that its rows reach it reads one B operand and
+// issues one v_mfma_f32_16x16x32_{f16,bf16} per channel block.  Lane (i = lane % 16,
+// g = lane / 16) accumulates out[16 rb + i][16 cb + 4 g .. +3].
 //
 // Pipelining.  While an item is computed, the band pieces and new V rows of the next
 // item are already loading into registers; they are written to LDS after a barrier.
 #include "launch.hpp"
+#include "ring.hpp"
 #include "tiles.hpp"
 
 namespace diagmm {
@@ -104,7 +109,7 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
 
     extern __shared__ __align__(16) unsigned char lds[];
     ST* pst = reinterpret_cast<ST*>(lds);                   // band staging
-    ST* vt = reinterpret_cast<ST*>(lds + a.ring_off);       // VT[c][slot]
+    unsigned char* vr = lds + a.ring_off;                   // V rows by slot, swizzled
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -128,7 +133,7 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
     // Zero the V ring once: window columns past the current window are read (and
     // multiplied by exact zeros), so no slot may ever hold a non-finite pattern.
     for (int x = tid; x < D * ringc / 8; x += kThreads)
-        reinterpret_cast<u32x4*>(vt)[x] = u32x4{0u, 0u, 0u, 0u};
+        reinterpret_cast<u32x4*>(vr)[x] = u32x4{0u, 0u, 0u, 0u};
 
     auto describe = [&](uint32_t id, Item* it) {
         const uint32_t unit = div32(a.chunks, id);
@@ -245,18 +250,9 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
             if (stray) reinterpret_cast<uint16_t*>(pst)[il * rsp + x] = 0;
         }
     };
-    // Scatter one 16-byte piece of V row `slot` (channels ch*8 .. ch*8+7) into VT.
+    // One 16-byte piece of V row `slot` (channels ch*8 .. ch*8+7) into the ring.
     auto put_v = [&](int slot, int ch, const u32x4& pc) {
-        const uint32_t d0 = pc[0], d1 = pc[1], d2 = pc[2], d3 = pc[3];
-        uint16_t* base = reinterpret_cast<uint16_t*>(vt) + (ch * 8) * ringc + slot;
-        base[0 * ringc] = static_cast<uint16_t>(d0);
-        base[1 * ringc] = static_cast<uint16_t>(d0 >> 16);
-        base[2 * ringc] = static_cast<uint16_t>(d1);
-        base[3 * ringc] = static_cast<uint16_t>(d1 >> 16);
-        base[4 * ringc] = static_cast<uint16_t>(d2);
-        base[5 * ringc] = static_cast<uint16_t>(d2 >> 16);
-        base[6 * ringc] = static_cast<uint16_t>(d3);
-        base[7 * ringc] = static_cast<uint16_t>(d3 >> 16);
+        *reinterpret_cast<u32x4*>(vr + ring_piece<D>(slot, ch)) = pc;
     };
     // One 16-byte piece of V for window column x of an item (zeros outside the sequence).
     auto get_v = [&](const Item& it, int x, int ch) {
@@ -353,17 +349,20 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
             const int jc_lo = x_lo / 32, jc_hi = (x_hi + 31) / 32;
             // brow[x] = B[x][il] = P[il][x - il] for every window column x this lane reads
             const ST* brow = pst + il * rsp + 8 * grp;
-            const uint16_t* arow[kCBPerWave];   // this lane's channel rows of VT
+            // A operand of channel block cb: transposed reads of slots r .. r + 3 and
+            // r + 4 .. r + 7, r = ring slot of window column 32 jc + 8 grp (a multiple of
+            // 4, so the four slots of a read never wrap and their swizzle depends on this
+            // lane's position in its group only).
+            int aoff[kCBPerWave];
 #pragma unroll
-            for (int q = 0; q < kCBPerWave; ++q)
-                arow[q] = reinterpret_cast<const uint16_t*>(vt + (16 * (cb0 + q) + col) * ringc);
+            for (int q = 0; q < kCBPerWave; ++q) aoff[q] = tr_lane_off<D>(col, cb0 + q);
             auto fetch = [&](int jc, V* bop, V* aop) {
                 *bop = *reinterpret_cast<const V*>(brow + 32 * jc);
                 int slot0 = s0 + 32 * jc + 8 * grp;             // ring slot of column x0
                 slot0 = slot0 < ringc ? slot0 : slot0 - ringc;
+                const unsigned char* rp = vr + slot0 * (2 * D);
 #pragma unroll
-                for (int q = 0; q < kCBPerWave; ++q)
-                    aop[q] = *reinterpret_cast<const V*>(arow[q] + slot0);
+                for (int q = 0; q < kCBPerWave; ++q) aop[q] = tr_read8<V, D>(rp + aoff[q]);
             };
             auto mma = [&](const V& bop, const V* aop) {
 #pragma unroll

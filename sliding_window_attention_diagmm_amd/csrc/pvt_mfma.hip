@@ -13,8 +13,9 @@
 // k0 + KC - 1 - x + j, j = 0..63 (a parallelogram through the band); output column j
 // takes rows x = j .. j + KC - 1.
 //
-// LDS.  X is kept transposed, XT[c][x], in a ring over window rows (as V is in the pv
-// kernel), sliding by 64 rows per tile.  The parallelogram is staged row-major,
+// LDS.  X is kept row-major in a ring over window rows (as V is in the pv kernel: pieces
+// swizzled by slot, the MFMA A operand read with transposing LDS reads), sliding by 64
+// rows per tile.  The parallelogram is staged row-major,
 // S[x][j] = G[ilo + x][k0 + KC - 1 - x + j]: each staged row is one 128-byte row of LDS,
 // filled with aligned 16-byte stores from 16-byte loads of the band tensor taken at
 // 2-byte alignment (the row-dependent skew is paid in the global loads, where it costs
@@ -35,6 +36,7 @@
 // Pipelining.  The next tile's band pieces (and, when the window slides, its 64 new X
 // rows) load into registers while the current tile computes.
 #include "launch.hpp"
+#include "ring.hpp"
 #include "tiles.hpp"
 
 namespace diagmm {
@@ -47,7 +49,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <class In> struct Mfma;
 template <> struct Mfma<F16> {
@@ -109,7 +110,7 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
 
     extern __shared__ __align__(16) unsigned char lds[];
     unsigned char* seg = lds;                               // S[x][j], swizzled pieces
-    ST* xt = reinterpret_cast<ST*>(lds + a.ring_off);       // XT[c][slot]
+    unsigned char* xr_ = lds + a.ring_off;                  // X rows by slot, swizzled
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -132,7 +133,7 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
     // Zero the X ring once: window rows past the current window are read (and multiplied
     // by exact zeros), so no slot may ever hold a non-finite pattern.
     for (int q = tid; q < D * ringc / 8; q += kThreads)
-        reinterpret_cast<u32x4*>(xt)[q] = u32x4{0u, 0u, 0u, 0u};
+        reinterpret_cast<u32x4*>(xr_)[q] = u32x4{0u, 0u, 0u, 0u};
 
     auto describe = [&](uint32_t id, Item* it) {
         const uint32_t unit = div32(a.chunks, id);
@@ -240,16 +241,7 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
     };
 
     auto put_x = [&](int slot, int ch, const u32x4& pc) {
-        const uint32_t d0 = pc[0], d1 = pc[1], d2 = pc[2], d3 = pc[3];
-        uint16_t* base = reinterpret_cast<uint16_t*>(xt) + (ch * 8) * ringc + slot;
-        base[0 * ringc] = static_cast<uint16_t>(d0);
-        base[1 * ringc] = static_cast<uint16_t>(d0 >> 16);
-        base[2 * ringc] = static_cast<uint16_t>(d1);
-        base[3 * ringc] = static_cast<uint16_t>(d1 >> 16);
-        base[4 * ringc] = static_cast<uint16_t>(d2);
-        base[5 * ringc] = static_cast<uint16_t>(d2 >> 16);
-        base[6 * ringc] = static_cast<uint16_t>(d3);
-        base[7 * ringc] = static_cast<uint16_t>(d3 >> 16);
+        *reinterpret_cast<u32x4*>(xr_ + ring_piece<D>(slot, ch)) = pc;
     };
     // One 16-byte piece of X for window row xr of an item (zeros outside the sequence).
     auto get_x = [&](const Item& it, int xr, int ch) {
@@ -346,11 +338,9 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
         {
             const int x_lo = 16 * jb, x_hi = 16 * jb + 15 + it.kbeff;
             const int ic_lo = x_lo / 32, ic_hi = (x_hi + 31) / 32;
-            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-            const uint16_t* arow[kCBPerWave];               // this lane's channel rows of XT
+            int aoff[kCBPerWave];                           // A operands: transposed reads
 #pragma unroll
-            for (int q = 0; q < kCBPerWave; ++q)
-                arow[q] = reinterpret_cast<const uint16_t*>(xt + (16 * (cb0 + q) + col) * ringc);
+            for (int q = 0; q < kCBPerWave; ++q) aoff[q] = tr_lane_off<D>(col, cb0 + q);
             auto fetch = [&](int ic, V* bop, V* aop) {
                 unsigned char* bp = seg + ic * (32 * kRowBytes) + tr_off;
                 // (a C-style cast: the LDS address of a generic pointer into `lds`)
@@ -359,11 +349,11 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
                     __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bp + 4 * kRowBytes));
                 const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
                 *bop = __builtin_bit_cast(V, u32x4{l2[0], l2[1], h2[0], h2[1]});
-                int slot0 = s0 + 32 * ic + 8 * grp;
+                int slot0 = s0 + 32 * ic + 8 * grp;             // a multiple of 8
                 slot0 = slot0 < ringc ? slot0 : slot0 - ringc;
+                const unsigned char* rp = xr_ + slot0 * (2 * D);
 #pragma unroll
-                for (int q = 0; q < kCBPerWave; ++q)
-                    aop[q] = *reinterpret_cast<const V*>(arow[q] + slot0);
+                for (int q = 0; q < kCBPerWave; ++q) aop[q] = tr_read8<V, D>(rp + aoff[q]);
             };
             auto mma = [&](const V& bop, const V* aop) {
 #pragma unroll

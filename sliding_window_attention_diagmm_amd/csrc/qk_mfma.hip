@@ -7,12 +7,18 @@
 // Tiles are numbered with the row block fastest, so consecutive tiles of one strip slide
 // down the class by 128 rows and share all but 128 of their keys.
 //
-// Workgroups.  One 512-thread workgroup per compute unit walks a contiguous range of
-// tile ids.  It keeps the key window of the current tile in an LDS ring (rows swizzled by
-// 16-byte chunk) and the query tile in one of two LDS buffers; a tile that continues a
-// strip only brings in 128 new key rows and its 128 query rows, fetched into registers at
-// the start of the previous tile and written to LDS at its end.
-//
+// Workgroups.  One workgroup per compute unit walks a contiguous range of tile ids.  It
+// keeps the key window of the current tile in an LDS ring (rows swizzled by 16-byte chunk)
+// and the query tile in one of two LDS buffers.  Its waves have two roles.  Eight compute
+// waves sweep the tile and store the band; they never load from HBM, so nothing makes
+// them wait for their stores to drain (a wave's vector memory counter covers its loads
+// and stores alike, in issue order).  Four load waves bring the next tile's rows into LDS
+// meanwhile: for a tile that continues the strip (same batch, class, head and slot chunk,
+// next row block) its 128 new key rows and its query rows; for one that starts a strip,
+// its whole window, when the ring holds two windows.  Slots outside the current window
+// only ever feed discarded columns of the sweep, so those writes race with nothing that
+// is stored.  A tile that was not prefetched is loaded by all waves before its sweep.
+
 // Alignment.  Band rows are not 16-byte aligned in HBM (row r starts at r K elements),
 // and misaligned stores run at half the bandwidth of aligned ones.  Column x of tile row
 // il sits at element A(il) + x with A(il) = A(0) + il (row stride - 1), so its offset
@@ -95,17 +101,20 @@ template <> struct Pack<F32> {
     __device__ __forceinline__ static P splat(uint32_t pad) { return P{pad, pad, pad, pad}; }
 };
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
+constexpr int kComputeThreads = 512;          // 8 waves: the sweep and every band store
+constexpr int kLoadThreads = 256;             // 4 waves: the global loads of the next tile
+constexpr int kThreads = kComputeThreads + kLoadThreads;
+constexpr int kComputeWaves = kComputeThreads / 64;
 constexpr int kRows = kQkRows;                // 128 = 8 waves x 16 rows
 constexpr int kMaxSlots = 513;
-constexpr int kMaxWindow = kRows + kMaxSlots - 1;
 constexpr int kRingDup = 48;                  // ring rows mirrored past its end
+constexpr int kStagePer = 8;                  // 16-byte chunks per thread per load batch
+                                              // (4 for d = 128, whose sweep needs the registers)
 
 struct QkArgs {
     int64_t n, h, K, w, s;
     TileGrid g;
-    int32_t ring;      // key rows in the LDS ring (2 * kRows + KB - 1, rounded up to 16)
+    int32_t ring;      // key rows in the LDS ring (a multiple of 16, >= 2 kRows + KB - 1)
     int32_t q_off;     // LDS byte offset of the two query tiles
     int32_t p_off;     // LDS byte offset of the parked row-end pieces
     uint32_t nwg;      // persistent workgroups
@@ -113,36 +122,50 @@ struct QkArgs {
     TileDecode dc;     // tiles over workgroups, tile -> coordinates
 };
 
-// Byte offset of (row, 16-byte chunk) in a swizzled block of D-element rows.  The chunk
-// index is XORed with bits 1..3 of the row, so 16 consecutive rows read at one logical
-// chunk land on distinct banks.
+// Byte offset of (row, 16-byte chunk) in a swizzled block of D-element rows.  A 16-byte
+// LDS read is served eight lanes at a time, 128 bytes across all banks; the chunk index
+// is XORed with the row's position among the rows sharing a 128-byte stretch of banks
+// (rows of 128 bytes or more: row mod 8; rows of 64 bytes, two per 128 bytes: row / 2
+// mod 4), so eight consecutive rows read at one logical chunk hit eight distinct 16-byte
+// bank groups.
 template <int D>
 __device__ __forceinline__ int swz(int row, int chunk) {
-    constexpr int kChunks = D / 8;
-    constexpr int kMask = (kChunks < 8 ? kChunks : 8) - 1;
-    return row * (D * 2) + ((chunk ^ ((row >> 1) & kMask)) << 4);
+    constexpr int kShift = D == 32 ? 1 : 0;
+    constexpr int kMask = D == 32 ? 3 : 7;
+    return row * (D * 2) + ((chunk ^ ((row >> kShift) & kMask)) << 4);
 }
 
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Ring rows between the end of a window of W keys and the next multiple of 16.
+__device__ __forceinline__ int align_gap(int W) { return (16 - (W & 15)) & 15; }
+
+// Rows one tile needs in LDS beyond what is already there: nk key rows of a class (keys
+// u_first .., clamped into the class) for ring slots slot_first .., and the tile's query
+// rows (tq0 ..) for a query buffer.
+struct Stage {
+    int64_t row0;      // [b][n][h] row of class row 0 of the tile's (batch, class, head)
+    int u_first, nk, slot_first, tq0, n_r;
+    int qbuf;          // LDS byte offset of the query buffer
+};
+
 template <class In, class Out, int D>
 __global__ void __launch_bounds__(kThreads)
 qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __restrict__ kx,
                typename Out::T* __restrict__ band, QkArgs a) {
     using OT = typename Out::T;
+    using IT = typename In::T;
     using V = typename Mfma<In>::V;
     using P = typename Pack<Out>::P;
     constexpr bool k16 = sizeof(OT) == 2;
     constexpr int kVec = 16 / sizeof(OT);                 // elements per 16-byte piece
     constexpr int kDC = D / 32;
     constexpr int kChunks = D / 8;                        // 16-byte chunks per row
-    constexpr int kRowChunks = kRows * kChunks;           // chunks of a row block
-    constexpr int kPerRows = (kRowChunks + kThreads - 1) / kThreads;
-    constexpr int kPerWin = (kMaxWindow * kChunks + kThreads - 1) / kThreads;
     constexpr int kQBytes = kRows * D * 2;
     constexpr int kBPS = k16 ? 2 : 1;                     // blocks per step
+    constexpr int kPer = D >= 128 ? kStagePer / 2 : kStagePer;
 
     extern __shared__ __align__(16) unsigned char lds[];
     unsigned char* ring = lds;
@@ -150,26 +173,23 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool computes = wave < kComputeWaves;
     const int col = lane & 15, grp = lane >> 4;
-    const int il = wave + 8 * col;                        // this lane's tile row
+    const int cw = wave & (kComputeWaves - 1);            // compute wave index
+    const int il = cw + 8 * col;                          // this lane's tile row
     const int64_t n = a.n, h = a.h, K = a.K, s = a.s;
     const int64_t row_step = s * h;                       // [b][n][h] rows per class row
     const int64_t gstep = row_step * K;                   // band elements per class row
+    const uint32_t row_bytes = static_cast<uint32_t>(row_step * D * 2);   // per class row
     const int ringc = a.ring;
     const P padv = Pack<Out>::splat(a.pad);
     // Column offset of this lane's four (after pairing: eight) columns in a step.
     const int off_g = k16 ? (grp == 1 ? 16 : (grp == 2 ? 8 : (grp == 3 ? 24 : 0))) : 4 * grp;
     // Parked row-end pieces of this wave: [row k][head, tail] x 16 bytes.
-    unsigned char* park = lds + a.p_off + wave * (16 * 2 * 16);
+    unsigned char* park = lds + a.p_off + cw * (16 * 2 * 16);
 
     uint32_t tile, tend;
     unit_range(a.dc, xcd_rank(blockIdx.x, a.nwg), &tile, &tend);
-
-    // Registers carrying the next tile's new key rows and query rows.
-    u32x4 kn[kPerRows], qn[kPerRows];
-    bool prefetched = false;
-    int s0 = 0;                     // ring slot of the current window's first key
-    int qsel = 0;                   // query buffer of the current tile
 
     // Ring rows below kRingDup are written twice, the second time past the ring's end,
     // so that two blocks starting at any row r < ringc (rows r .. r + 16 + 22) are read
@@ -178,266 +198,360 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
         *reinterpret_cast<u32x4*>(ring + swz<D>(slot, ch)) = v;
         if (slot < kRingDup) *reinterpret_cast<u32x4*>(ring + swz<D>(slot + ringc, ch)) = v;
     };
+    // Batch b0 of a Stage moved by NT threads (this one is number gt): kPer 16-byte
+    // chunks per thread, chunk b0 + gt + NT x; the key rows' chunks first, then the query
+    // rows'.  Sources are addressed by 32-bit byte offsets from the strip's first row.
+    // Every entry of buf is loaded (chunks past the end re-read the last one), which keeps
+    // a held batch in one set of registers; only the LDS writes are predicated.
+    auto load_batch = [&](const Stage& sg, int gt, int b0, u32x4* buf, auto nt_c) {
+        constexpr int NT = decltype(nt_c)::value;
+        const int nkc = sg.nk * kChunks;
+        const int total = nkc + kRows * kChunks;
+        const unsigned char* kb8 = reinterpret_cast<const unsigned char*>(kx + sg.row0 * D);
+        const unsigned char* qb8 = reinterpret_cast<const unsigned char*>(q + sg.row0 * D);
+#pragma unroll
+        for (int x = 0; x < kPer; ++x) {
+            int idx = b0 + gt + NT * x;
+            idx = idx < total ? idx : total - 1;
+            const bool isk = idx < nkc;
+            const int j = isk ? idx : idx - nkc;
+            const int rr = j / kChunks, ch = j % kChunks;
+            int u = isk ? sg.u_first + rr : sg.tq0 + rr;
+            u = u < 0 ? 0 : (u < sg.n_r ? u : sg.n_r - 1);
+            const uint32_t off = static_cast<uint32_t>(u) * row_bytes + ch * 16;
+            buf[x] = ld_global16((isk ? kb8 : qb8) + off);
+        }
+    };
+    auto write_batch = [&](const Stage& sg, int gt, int b0, const u32x4* buf, auto nt_c) {
+        constexpr int NT = decltype(nt_c)::value;
+        const int nkc = sg.nk * kChunks;
+        const int total = nkc + kRows * kChunks;
+#pragma unroll
+        for (int x = 0; x < kPer; ++x) {
+            const int idx = b0 + gt + NT * x;
+            if (idx < total) {
+                const bool isk = idx < nkc;
+                const int j = isk ? idx : idx - nkc;
+                const int rr = j / kChunks, ch = j % kChunks;
+                if (isk) {
+                    int slot = sg.slot_first + rr;
+                    slot = slot < ringc ? slot : slot - ringc;
+                    put_ring(slot, ch, buf[x]);
+                } else {
+                    *reinterpret_cast<u32x4*>(lds + sg.qbuf + swz<D>(rr, ch)) = buf[x];
+                }
+            }
+        }
+    };
+    // The batches of a Stage from b0 on, each loaded and then written.
+    auto stage_from = [&](const Stage& sg, int gt, int b0, auto nt_c) {
+        constexpr int NT = decltype(nt_c)::value;
+        const int total = (sg.nk + kRows) * kChunks;
+        for (; b0 < total; b0 += NT * kPer) {
+            u32x4 buf[kPer];
+            load_batch(sg, gt, b0, buf, nt_c);
+            write_batch(sg, gt, b0, buf, nt_c);
+        }
+    };
+
+    // Tile coordinates and extents.
+    struct TInfo {
+        TileId t;
+        int n_r, t0, kbeff, u0, W;
+        int64_t row0;
+        bool ok;                   // not an empty tail block of a shorter residue class
+    };
+    auto info = [&](uint32_t tl) {
+        TInfo f;
+        f.t = decode_fast(a.dc, tl);
+        f.n_r = class_len_fast(a.dc, f.t.r);
+        f.t0 = f.t.tb * kRows;
+        f.ok = f.t0 < f.n_r;
+        const int64_t k0 = static_cast<int64_t>(f.t.kb) * a.g.kb;
+        f.kbeff = static_cast<int>(K - k0 < a.g.kb ? K - k0 : a.g.kb);
+        f.u0 = static_cast<int>(f.t0 + k0 - a.w);
+        f.W = kRows + f.kbeff - 1;
+        f.row0 = (static_cast<int64_t>(f.t.bb) * n + f.t.r) * h + f.t.hh;
+        return f;
+    };
+    // The rows tile nn needs after tile c (window at ring slot s0c).  A tile continuing
+    // c's strip needs 128 new keys, right after c's window; one starting a strip its whole
+    // window, from the first multiple of 16 past c's window (block reads assume windows
+    // start at such ring rows).  They go to the ring while c is swept only if the ring
+    // holds both (at + nk <= ringc).
+    auto link = [&](const TInfo& c, const TInfo& nn, int s0c, int qbuf, bool* cont, int* at) {
+        *cont = nn.t.tb == c.t.tb + 1 && nn.t.kb == c.t.kb && nn.t.r == c.t.r &&
+                nn.t.hh == c.t.hh && nn.t.bb == c.t.bb;
+        *at = *cont ? c.W : c.W + align_gap(c.W);
+        Stage sg;
+        sg.row0 = nn.row0;
+        sg.u_first = *cont ? c.u0 + c.W : nn.u0;
+        sg.nk = *cont ? kRows : nn.W;
+        int sl = s0c + *at;
+        sg.slot_first = sl < ringc ? sl : sl - ringc;
+        sg.tq0 = nn.t0;
+        sg.n_r = nn.n_r;
+        sg.qbuf = qbuf;
+        return sg;
+    };
+
+    bool ready = false;             // the current tile's keys and query rows are in LDS
+    int s0 = 0;                     // ring slot of the current window's first key
+    int qsel = 0;                   // query buffer of the current tile
+
+    // Load waves: the first batch of the rows the tile after next needs, loaded during
+    // this tile and written to LDS during the next one.
+    u32x4 lbuf[kPer];
+    bool lheld = false;
 
     for (; tile < tend; ++tile) {
-        const TileId t = decode_fast(a.dc, tile);
-        const int n_r = class_len_fast(a.dc, t.r);
-        const int t0 = t.tb * kRows;
-        if (t0 >= n_r) {           // empty tail block of a shorter residue class
-            prefetched = false;
+        const TInfo cur = info(tile);
+        if (!cur.ok) {
+            ready = lheld = false;
             continue;
         }
+        const int n_r = cur.n_r, t0 = cur.t0, kbeff = cur.kbeff, u0 = cur.u0, W = cur.W;
         const int rows_here = n_r - t0 < kRows ? n_r - t0 : kRows;
-        const int64_t k0 = static_cast<int64_t>(t.kb) * a.g.kb;
-        const int kbeff = static_cast<int>(K - k0 < a.g.kb ? K - k0 : a.g.kb);
-        const int u0 = static_cast<int>(t0 + k0 - a.w);
-        const int W = kRows + kbeff - 1;
-        const int64_t row0 = (static_cast<int64_t>(t.bb) * n + t.r) * h + t.hh;
-        unsigned char* qlds = lds + a.q_off + qsel * kQBytes;
+        const int64_t k0 = static_cast<int64_t>(cur.t.kb) * a.g.kb;
+        const int64_t row0 = cur.row0;
 
-        if (!prefetched) {
-            // First tile of a strip: the whole key window and the query tile.
+        if (!ready) {
+            // Nothing prefetched: every wave loads the whole key window and the query tile.
             s0 = 0;
-            u32x4 buf[kPerWin];
-#pragma unroll
-            for (int x = 0; x < kPerWin; ++x) {
-                const int idx = tid + x * kThreads, rr = idx / kChunks, ch = idx % kChunks;
-                if (rr < W) {
-                    int u = u0 + rr;
-                    u = u < 0 ? 0 : (u < n_r ? u : n_r - 1);
-                    buf[x] = ld_global16(kx + (row0 + u * row_step) * D + ch * 8);
-                }
-            }
-#pragma unroll
-            for (int x = 0; x < kPerRows; ++x) {
-                const int idx = tid + x * kThreads, rr = idx / kChunks, ch = idx % kChunks;
-                if (idx < kRowChunks) {
-                    int tq = t0 + rr;
-                    tq = tq < n_r ? tq : n_r - 1;
-                    qn[x] = ld_global16(q + (row0 + tq * row_step) * D + ch * 8);
-                }
-            }
-#pragma unroll
-            for (int x = 0; x < kPerWin; ++x) {
-                const int idx = tid + x * kThreads, rr = idx / kChunks, ch = idx % kChunks;
-                if (rr < W) put_ring(rr, ch, buf[x]);
-            }
-#pragma unroll
-            for (int x = 0; x < kPerRows; ++x) {
-                const int idx = tid + x * kThreads, rr = idx / kChunks, ch = idx % kChunks;
-                if (idx < kRowChunks) *reinterpret_cast<u32x4*>(qlds + swz<D>(rr, ch)) = qn[x];
-            }
+            stage_from(Stage{row0, u0, W, 0, t0, n_r, a.q_off + qsel * kQBytes}, tid, 0,
+                       std::integral_constant<int, kThreads>{});
             __syncthreads();
         }
 
-        // Does the next tile continue this strip?  Then fetch its new rows now.
-        bool next = false;
+        // The next tile's rows go to LDS while this one is swept, when the ring holds both.
+        bool pre = false, cont = false;
+        int at = 0;
+        Stage nx{};
+        TInfo nxt{};
+        nxt.ok = false;
         if (tile + 1 < tend) {
-            const TileId tn = decode_fast(a.dc, tile + 1);
-            next = tn.tb == t.tb + 1 && tn.kb == t.kb && tn.r == t.r && tn.hh == t.hh &&
-                   tn.bb == t.bb && t0 + kRows < n_r;
-        }
-        if (next) {
-#pragma unroll
-            for (int x = 0; x < kPerRows; ++x) {
-                const int idx = tid + x * kThreads, rr = idx / kChunks, ch = idx % kChunks;
-                if (idx < kRowChunks) {
-                    int u = u0 + W + rr;
-                    u = u < 0 ? 0 : (u < n_r ? u : n_r - 1);
-                    kn[x] = ld_global16(kx + (row0 + u * row_step) * D + ch * 8);
-                    int tq = t0 + kRows + rr;
-                    tq = tq < n_r ? tq : n_r - 1;
-                    qn[x] = ld_global16(q + (row0 + tq * row_step) * D + ch * 8);
-                }
+            nxt = info(tile + 1);
+            if (nxt.ok) {
+                nx = link(cur, nxt, s0, a.q_off + (qsel ^ 1) * kQBytes, &cont, &at);
+                pre = at + nx.nk <= ringc;
             }
         }
 
-        // B operands: this wave's 16 query rows.
-        V qf[kDC];
-#pragma unroll
-        for (int dc = 0; dc < kDC; ++dc)
-            qf[dc] = *reinterpret_cast<const V*>(qlds + swz<D>(il, 4 * dc + grp));
-
-        // Row il: global element of window column 0 (column x sits at rowA + x); the
-        // wave's rows share rowA mod kVec, and column o starts their pieces.
-        const int64_t rowA = (row0 + static_cast<int64_t>(t0) * row_step) * K + k0 +
-                             static_cast<int64_t>(il) * (gstep - 1);
-        const int o = __builtin_amdgcn_readfirstlane(
-            static_cast<int>((kVec - (rowA & (kVec - 1))) & (kVec - 1)));
-        const bool row_ok = il < rows_here;
-        const bool key_edge = u0 < 0 || u0 + W > n_r;     // window touches a sequence end
-
-        // Blocks: from the one holding the first piece of row `wave` (it starts at the
-        // largest column <= wave that is = o mod kVec, so at least wave - kVec + 1) to the
-        // one holding column wave + 120 + kbeff - 1, the last column of the last row.
-        const int x_first = wave - ((wave - o + kVec) & (kVec - 1));
-        const int jb_lo = (x_first - o) >> 4;             // floor division (may be -1)
-        const int jb_hi = (wave + 119 + kbeff - o) >> 4;
-        const int nsteps = (jb_hi - jb_lo + kBPS) / kBPS;
-        // Ring swizzle of this lane's key row within a block (blocks start at ring rows
-        // that are multiples of 16, so it does not depend on the block).
-        const int krow = o + col;                          // 0 .. 22
-        int roff[kDC];
-#pragma unroll
-        for (int dc = 0; dc < kDC; ++dc) roff[dc] = swz<D>(krow, 4 * dc + grp);
-
-        // Block reads start at ring row (s0 + 16 jb) mod ringc; the step loop advances one
-        // such base by 16 kBPS per step (the second block of a step reads base + 16 ..,
-        // inside the mirrored rows).
-        auto ring_row = [&](int jb) {
-            int r0 = s0 + 16 * jb;
-            return r0 < 0 ? r0 + ringc : (r0 < ringc ? r0 : r0 - ringc);
-        };
-        auto fetch = [&](int base, V* kf) {
-            const unsigned char* rp = ring + base * (2 * D);
-#pragma unroll
-            for (int dc = 0; dc < kDC; ++dc) kf[dc] = *reinterpret_cast<const V*>(rp + roff[dc]);
-        };
-        auto mma = [&](const V* kf) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int dc = 0; dc < kDC; ++dc) acc = Mfma<In>::run(kf[dc], qf[dc], acc);
-            return acc;
-        };
-        // Round four accumulators; on tiles whose window reaches past a sequence end, keys
-        // outside it take the padding constant.
-        auto pack = [&](auto edge, int jb, const f32x4& acc) {
-            P val = Pack<Out>::run(acc);
-            if constexpr (decltype(edge)::value) {
-                // keys of this lane's four columns: u0 + 16 jb + o + 4 grp + v
-                const int ukey = u0 + 16 * jb + o + 4 * grp;
-                bool kok[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) kok[v] = ukey + v >= 0 && ukey + v < n_r;
-                const P pv = padv;
-                if constexpr (!k16) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) val[v] = kok[v] ? val[v] : pv[v];
-                } else {
-                    const uint32_t m0 = (kok[0] ? 0xffffu : 0u) | (kok[1] ? 0xffff0000u : 0u);
-                    const uint32_t m1 = (kok[2] ? 0xffffu : 0u) | (kok[3] ? 0xffff0000u : 0u);
-                    val[0] = (val[0] & m0) | (pv[0] & ~m0);
-                    val[1] = (val[1] & m1) | (pv[1] & ~m1);
+        if (!computes) {
+            const int lt = tid - kComputeThreads;
+            constexpr auto nt = std::integral_constant<int, kLoadThreads>{};
+            if (pre) {
+                if (!lheld) load_batch(nx, lt, 0, lbuf, nt);
+                write_batch(nx, lt, 0, lbuf, nt);
+                stage_from(nx, lt, kLoadThreads * kPer, nt);
+            }
+            lheld = false;
+            if (nxt.ok && tile + 2 < tend) {
+                const TInfo nn = info(tile + 2);
+                if (nn.ok) {
+                    bool c2;
+                    int at2;
+                    const Stage nx2 = link(nxt, nn, 0, 0, &c2, &at2);   // rows only
+                    if (at2 + nx2.nk <= ringc) {
+                        load_batch(nx2, lt, 0, lbuf, nt);
+                        lheld = true;
+                    }
                 }
             }
-            return val;
-        };
-        // Step st: this lane's piece starts at column x0 = 16 (jb_lo + kBPS st) + o + off_g,
-        // i.e. slot x0 - il; whole pieces lie at slots 0 .. kbeff - kVec.
-        const int slot_base = 16 * jb_lo + o + off_g - il;
-        const int full_max = kbeff - kVec;
-        OT* const gbase = band + (rowA + 16 * jb_lo + o + off_g);   // 16-byte aligned
-        // A step holds a row's partial piece only near the ends of the sweep: slot0 >=
-        // 16 kBPS st - 143 (jb_lo >= -1, o >= 0, off_g >= 0, il <= 127) and slot0 <=
-        // 16 kBPS st + 24 (16 jb_lo + o <= x_first <= il), so only steps below st_h or from
-        // st_t on look for them.
-        const int st_h = (143 + 16 * kBPS) / (16 * kBPS);
-        const int st_t = (kbeff - kVec - 24) >= 0 ? (kbeff - kVec - 24) / (16 * kBPS) + 1 : 0;
-        auto finish = [&](auto edge, int st, const f32x4* acc) {
-            const int jb = jb_lo + kBPS * st;
-            u32x4 own;
-            if constexpr (k16) {
-                const P va = pack(edge, jb, acc[0]), vb = pack(edge, jb + 1, acc[1]);
-                const auto sx = __builtin_amdgcn_permlane16_swap(va[0], vb[0], false, false);
-                const auto sy = __builtin_amdgcn_permlane16_swap(va[1], vb[1], false, false);
-                own = u32x4{sx[0], sy[0], sx[1], sy[1]};
-            } else {
-                own = pack(edge, jb, acc[0]);
-            }
-            const int sst = 16 * kBPS * st;
-            const int slot0 = slot_base + sst;
-            if (row_ok && full_max >= 0 &&
-                static_cast<unsigned>(slot0) <= static_cast<unsigned>(full_max))
-                *reinterpret_cast<u32x4*>(gbase + sst) = own;
-            if (st < st_h || st >= st_t) {
-                const bool part = row_ok && slot0 < kbeff && slot0 + kVec > 0 &&
-                                  !(slot0 >= 0 && slot0 <= full_max);
-                if (part)   // head piece (holds slot 0) or tail piece
-                    *reinterpret_cast<u32x4*>(park + (2 * col + (slot0 < 0 ? 0 : 1)) * 16) = own;
-            }
-        };
+        } else {
+            unsigned char* qlds = lds + a.q_off + qsel * kQBytes;
+            // B operands: this wave's 16 query rows.
+            V qf[kDC];
+#pragma unroll
+            for (int dc = 0; dc < kDC; ++dc)
+                qf[dc] = *reinterpret_cast<const V*>(qlds + swz<D>(il, 4 * dc + grp));
 
-        // Software pipeline: the MFMAs of step st + 1 and the key fragment reads of step
-        // st + 2 are issued before step st is finished (past the last step they work on
-        // ring rows nobody stores).  The scheduling barriers keep that order; the empty asm
-        // with a memory clobber keeps the compiler from folding the loop-carried fragment
-        // reads back into reads at their use.
-        auto sweep = [&](auto edge) {
-            V kf[kBPS][kDC];
-            f32x4 acc_cur[kBPS], acc_nx[kBPS];
-            int base = ring_row(jb_lo);                    // block jb_lo + kBPS st
-            auto advance = [&]() {
-                base += 16 * kBPS;
-                base = base < ringc ? base : base - ringc;
+            // Row il: global element of window column 0 (column x sits at rowA + x); the
+            // wave's rows share rowA mod kVec, and column o starts their pieces.
+            const int64_t rowA = (row0 + static_cast<int64_t>(t0) * row_step) * K + k0 +
+                                 static_cast<int64_t>(il) * (gstep - 1);
+            const int o = __builtin_amdgcn_readfirstlane(
+                static_cast<int>((kVec - (rowA & (kVec - 1))) & (kVec - 1)));
+            const bool row_ok = il < rows_here;
+            const bool key_edge = u0 < 0 || u0 + W > n_r;     // window touches a sequence end
+
+            // Blocks: from the one holding the first piece of row `cw` (it starts at the
+            // largest column <= cw that is = o mod kVec, so at least cw - kVec + 1) to the
+            // one holding column cw + 120 + kbeff - 1, the last column of the last row.
+            const int x_first = cw - ((cw - o + kVec) & (kVec - 1));
+            const int jb_lo = (x_first - o) >> 4;             // floor division (may be -1)
+            const int jb_hi = (cw + 119 + kbeff - o) >> 4;
+            const int nsteps = (jb_hi - jb_lo + kBPS) / kBPS;
+            // Ring swizzle of this lane's key row within a block (blocks start at ring rows
+            // that are multiples of 16, so it does not depend on the block).
+            const int krow = o + col;                          // 0 .. 22
+            int roff[kDC];
+#pragma unroll
+            for (int dc = 0; dc < kDC; ++dc) roff[dc] = swz<D>(krow, 4 * dc + grp);
+
+            // Block reads start at ring row (s0 + 16 jb) mod ringc; the step loop advances one
+            // such base by 16 kBPS per step (the second block of a step reads base + 16 ..,
+            // inside the mirrored rows).
+            auto ring_row = [&](int jb) {
+                int r0 = s0 + 16 * jb;
+                return r0 < 0 ? r0 + ringc : (r0 < ringc ? r0 : r0 - ringc);
             };
+            auto fetch = [&](int base, V* kf) {
+                const unsigned char* rp = ring + base * (2 * D);
 #pragma unroll
-            for (int bq = 0; bq < kBPS; ++bq) fetch(base + 16 * bq, kf[bq]);
+                for (int dc = 0; dc < kDC; ++dc) kf[dc] = *reinterpret_cast<const V*>(rp + roff[dc]);
+            };
+            auto mma = [&](const V* kf) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int bq = 0; bq < kBPS; ++bq) acc_cur[bq] = mma(kf[bq]);
-            advance();
+                for (int dc = 0; dc < kDC; ++dc) acc = Mfma<In>::run(kf[dc], qf[dc], acc);
+                return acc;
+            };
+            // Round four accumulators; on tiles whose window reaches past a sequence end, keys
+            // outside it take the padding constant (checked per lane only in blocks that
+            // reach past it: the block's keys are u0 + 16 jb + o .. +15 for the whole wave).
+            auto pack = [&](auto edge, int jb, const f32x4& acc) {
+                P val = Pack<Out>::run(acc);
+                const int ublk = u0 + 16 * jb + o;
+                if (!decltype(edge)::value) return val;
+                if (ublk + 16 <= 0 || ublk >= n_r) return padv;     // whole block outside
+                if (ublk < 0 || ublk + 16 > n_r) {
+                    // keys of this lane's four columns: u0 + 16 jb + o + 4 grp + v
+                    const int ukey = ublk + 4 * grp;
+                    bool kok[4];
 #pragma unroll
-            for (int bq = 0; bq < kBPS; ++bq) fetch(base + 16 * bq, kf[bq]);
-            for (int st = 0; st < nsteps; ++st) {
-                asm volatile("" ::: "memory");
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int v = 0; v < 4; ++v) kok[v] = ukey + v >= 0 && ukey + v < n_r;
+                    const P pv = padv;
+                    if constexpr (!k16) {
 #pragma unroll
-                for (int bq = 0; bq < kBPS; ++bq) acc_nx[bq] = mma(kf[bq]);
-                __builtin_amdgcn_sched_barrier(0);
+                        for (int v = 0; v < 4; ++v) val[v] = kok[v] ? val[v] : pv[v];
+                    } else {
+                        const uint32_t m0 = (kok[0] ? 0xffffu : 0u) | (kok[1] ? 0xffff0000u : 0u);
+                        const uint32_t m1 = (kok[2] ? 0xffffu : 0u) | (kok[3] ? 0xffff0000u : 0u);
+                        val[0] = (val[0] & m0) | (pv[0] & ~m0);
+                        val[1] = (val[1] & m1) | (pv[1] & ~m1);
+                    }
+                }
+                return val;
+            };
+            // Step st: this lane's piece starts at column x0 = 16 (jb_lo + kBPS st) + o + off_g,
+            // i.e. slot x0 - il; whole pieces lie at slots 0 .. kbeff - kVec.
+            const int slot_base = 16 * jb_lo + o + off_g - il;
+            const int full_max = kbeff - kVec;
+            OT* const gbase = band + (rowA + 16 * jb_lo + o + off_g);   // 16-byte aligned
+            // A step holds a row's partial piece only near the ends of the sweep: slot0 >=
+            // 16 kBPS st - 143 (jb_lo >= -1, o >= 0, off_g >= 0, il <= 127) and slot0 <=
+            // 16 kBPS st + 24 (16 jb_lo + o <= x_first <= il), so only steps below st_h or from
+            // st_t on look for them.
+            constexpr int kCS = 16 * kBPS;                   // columns per step
+            const int st_h = (143 + kCS) / kCS;
+            const int st_t = (kbeff - kVec - 24) >= 0 ? (kbeff - kVec - 24) / kCS + 1 : 0;
+            // This lane's partial pieces: the one starting in slots -(kVec - 1) .. -1 (it holds
+            // slot 0) and the one starting in max(0, full_max + 1) .. kbeff - 1 (it holds the
+            // last slot but is not whole).  Its pieces start kCS slots apart, so each range
+            // holds at most one; st_hd / st_tl are their steps (-1: none).
+            auto first_step = [&](int slot) {                // first st with slot0 >= slot
+                const int d = slot - slot_base;
+                return d <= 0 ? 0 : (d + kCS - 1) / kCS;
+            };
+            int st_hd = first_step(-(kVec - 1));
+            if (!row_ok || slot_base + kCS * st_hd > -1) st_hd = -1;
+            const int lo_t = full_max + 1 > 0 ? full_max + 1 : 0;
+            int st_tl = first_step(lo_t);
+            if (!row_ok || slot_base + kCS * st_tl >= kbeff) st_tl = -1;
+            auto finish = [&](auto edge, int st, const f32x4* acc) {
+                const int jb = jb_lo + kBPS * st;
+                u32x4 own;
+                if constexpr (k16) {
+                    const P va = pack(edge, jb, acc[0]), vb = pack(edge, jb + 1, acc[1]);
+                    const auto sx = __builtin_amdgcn_permlane16_swap(va[0], vb[0], false, false);
+                    const auto sy = __builtin_amdgcn_permlane16_swap(va[1], vb[1], false, false);
+                    own = u32x4{sx[0], sy[0], sx[1], sy[1]};
+                } else {
+                    own = pack(edge, jb, acc[0]);
+                }
+                const int sst = 16 * kBPS * st;
+                const int slot0 = slot_base + sst;
+                if (row_ok && full_max >= 0 &&
+                    static_cast<unsigned>(slot0) <= static_cast<unsigned>(full_max))
+                    *reinterpret_cast<u32x4*>(gbase + sst) = own;
+                if (st < st_h || st >= st_t) {
+                    if (st == st_hd || st == st_tl)   // head piece (holds slot 0) or tail piece
+                        *reinterpret_cast<u32x4*>(park + (2 * col + (st == st_tl ? 1 : 0)) * 16) = own;
+                }
+            };
+
+            // Software pipeline: the MFMAs of step st + 1 and the key fragment reads of step
+            // st + 2 are issued before step st is finished; the loop runs steps in pairs, the
+            // accumulators alternating between two sets (an odd count gets one more step,
+            // whose columns no row stores; past the last step the reads work on ring rows
+            // nobody stores).  The scheduling barriers keep that order; the empty asm with a
+            // memory clobber keeps the compiler from folding the loop-carried fragment reads
+            // back into reads at their use.
+            auto sweep = [&](auto edge) {
+                V kf[kBPS][kDC];
+                f32x4 acc_a[kBPS], acc_b[kBPS];
+                int base = ring_row(jb_lo);                    // block jb_lo + kBPS st
+                auto advance = [&]() {
+                    base += 16 * kBPS;
+                    base = base < ringc ? base : base - ringc;
+                };
+                auto mma_fetch = [&](f32x4* acc) {
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int bq = 0; bq < kBPS; ++bq) acc[bq] = mma(kf[bq]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    advance();
+#pragma unroll
+                    for (int bq = 0; bq < kBPS; ++bq) fetch(base + 16 * bq, kf[bq]);
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+#pragma unroll
+                for (int bq = 0; bq < kBPS; ++bq) fetch(base + 16 * bq, kf[bq]);
+#pragma unroll
+                for (int bq = 0; bq < kBPS; ++bq) acc_a[bq] = mma(kf[bq]);
                 advance();
 #pragma unroll
                 for (int bq = 0; bq < kBPS; ++bq) fetch(base + 16 * bq, kf[bq]);
-                __builtin_amdgcn_sched_barrier(0);
-                finish(edge, st, acc_cur);
-#pragma unroll
-                for (int bq = 0; bq < kBPS; ++bq) acc_cur[bq] = acc_nx[bq];
-            }
-        };
-        if (key_edge)
-            sweep(std::true_type{});
-        else
-            sweep(std::false_type{});
+                for (int st = 0; st < nsteps; st += 2) {
+                    mma_fetch(acc_b);
+                    finish(edge, st, acc_a);
+                    mma_fetch(acc_a);
+                    finish(edge, st + 1, acc_b);
+                }
+            };
+            if (key_edge)
+                sweep(std::true_type{});
+            else
+                sweep(std::false_type{});
 
-        // Parked row-end pieces, element by element: lane (k, g), g < 2, takes row k's head
-        // (g = 0) or tail (g = 1) piece.  A row's head piece starts at column x_first + 8 k
-        // (slot -((il - o) mod kVec)); its tail piece holds slot kbeff - 1.  The piece is
-        // read into named scalars before the per-element stores (store_part), which keeps
-        // the element selection out of divergent vector code.
-        if (grp < 2) {
-            const int sh = x_first + 8 * col - il;         // head piece: slot0 in (-kVec, 0]
-            const int xl = il + kbeff - 1;                 // last column of the row
-            const int st_ = xl - ((xl - o + kVec) & (kVec - 1)) - il;   // tail piece slot0
-            const int slot0 = grp ? st_ : sh;
-            // The head piece is parked when it starts before slot 0; the tail piece when it
-            // starts at or after slot 0 and runs past the last slot.
-            const bool parked = row_ok && (grp ? (st_ >= 0 && st_ + kVec > kbeff) : sh < 0);
-            if (parked) {
-                const u32x4 pc = *reinterpret_cast<const u32x4*>(park + (2 * col + grp) * 16);
-                const uint32_t d0 = pc[0], d1 = pc[1], d2 = pc[2], d3 = pc[3];
-                const int pa = slot0 < 0 ? -slot0 : 0;
-                const int pe = kbeff - slot0 < kVec ? kbeff - slot0 : kVec;
-                store_part<OT>(band + (rowA + il + slot0), d0, d1, d2, d3, pa, pe);
-            }
-        }
-
-        // The next tile's new key rows go to ring slots outside the current window (only
-        // columns no row stores are read there), its query rows to the other buffer.
-        if (next) {
-            unsigned char* qnext = lds + a.q_off + (qsel ^ 1) * kQBytes;
-#pragma unroll
-            for (int x = 0; x < kPerRows; ++x) {
-                const int idx = tid + x * kThreads, rr = idx / kChunks, ch = idx % kChunks;
-                if (idx < kRowChunks) {
-                    int slot = s0 + W + rr;
-                    slot = slot < ringc ? slot : slot - ringc;
-                    put_ring(slot, ch, kn[x]);
-                    *reinterpret_cast<u32x4*>(qnext + swz<D>(rr, ch)) = qn[x];
+            // Parked row-end pieces, element by element: lane (k, g), g < 2, takes row k's head
+            // (g = 0) or tail (g = 1) piece.  A row's head piece starts at column x_first + 8 k
+            // (slot -((il - o) mod kVec)); its tail piece holds slot kbeff - 1.  The piece is
+            // read into named scalars before the per-element stores (store_part), which keeps
+            // the element selection out of divergent vector code.
+            if (grp < 2) {
+                const int sh = x_first + 8 * col - il;         // head piece: slot0 in (-kVec, 0]
+                const int xl = il + kbeff - 1;                 // last column of the row
+                const int st_ = xl - ((xl - o + kVec) & (kVec - 1)) - il;   // tail piece slot0
+                const int slot0 = grp ? st_ : sh;
+                // The head piece is parked when it starts before slot 0; the tail piece when it
+                // starts at or after slot 0 and runs past the last slot.
+                const bool parked = row_ok && (grp ? (st_ >= 0 && st_ + kVec > kbeff) : sh < 0);
+                if (parked) {
+                    const u32x4 pc = *reinterpret_cast<const u32x4*>(park + (2 * col + grp) * 16);
+                    const uint32_t d0 = pc[0], d1 = pc[1], d2 = pc[2], d3 = pc[3];
+                    const int pa = slot0 < 0 ? -slot0 : 0;
+                    const int pe = kbeff - slot0 < kVec ? kbeff - slot0 : kVec;
+                    store_part<OT>(band + (rowA + il + slot0), d0, d1, d2, d3, pa, pe);
                 }
             }
         }
-        __syncthreads();
-        prefetched = next;
-        if (next) {
-            s0 += kRows;
+        __syncthreads();                                  // this tile's LDS reads are done
+        ready = pre;
+        if (pre) {
+            s0 += cont ? kRows : at;
             s0 = s0 < ringc ? s0 : s0 - ringc;
             qsel ^= 1;
         }
@@ -449,14 +563,20 @@ struct Layout {
 };
 
 // LDS layout for a chunk of kb slots: the key ring (plus its mirrored rows), two query
-// tiles, the parked row-end pieces.
+// tiles, the parked row-end pieces.  The ring holds two whole windows where that fits, so
+// that a tile starting a new strip is loaded while the one before it is swept, and at
+// least a window plus the kRows keys a continuing tile adds.
 Layout layout_for(int64_t kb, int64_t d) {
+    const int64_t win = kRows + kb - 1;
     Layout l;
-    l.kb = kb;
-    l.ring = ceil_div(2 * kRows + kb - 1, 16) * 16;
-    l.q_off = ceil_div((l.ring + kRingDup) * d * 2, 16) * 16;
-    l.p_off = l.q_off + 2 * kRows * d * 2;
-    l.bytes = l.p_off + kWaves * 16 * 2 * 16;
+    for (const int64_t rows : {2 * ceil_div(win, 16) * 16, win + kRows}) {
+        l.kb = kb;
+        l.ring = ceil_div(rows, 16) * 16;
+        l.q_off = ceil_div((l.ring + kRingDup) * d * 2, 16) * 16;
+        l.p_off = l.q_off + 2 * kRows * d * 2;
+        l.bytes = l.p_off + kComputeWaves * 16 * 2 * 16;
+        if (l.bytes <= kQkLdsBytes) break;
+    }
     return l;
 }
 
@@ -522,7 +642,9 @@ QkTilePlan plan_qk_mfma(const Problem& p, int out_dt) {
     tp.rs = 0;
     tp.lds_bytes = l.bytes;
     tp.workgroups = tp.grid.tiles < cus ? tp.grid.tiles : cus;
+    // (q and k rows of one strip are addressed by 32-bit byte offsets)
     tp.ok = tp.grid.tiles <= kMaxTiles && ceil_div(p.n, p.s) < (int64_t(1) << 30) &&
+            (p.n + p.s) * p.h * p.d * 2 < (int64_t(1) << 32) &&
             p.K < (int64_t(1) << 30) && l.bytes <= kQkLdsBytes && tp.workgroups >= 1;
     return tp;
 }

@@ -39,9 +39,13 @@
 //
 // Store.  For 16-bit outputs two blocks are combined with v_permlane16_swap so that each
 // lane holds 8 consecutive columns, one aligned 16-byte piece; for f32 each block already
-// gives 4 columns = 16 bytes per lane.  Whole pieces go straight to HBM.  The at most two
-// pieces per row that also hold slots of the neighbouring band row in HBM are parked in
-// LDS and written element by element after the sweep.
+// gives 4 columns = 16 bytes per lane.  Whole pieces go straight to HBM through a buffer
+// resource (pieces that are not whole get an out-of-range offset and are dropped).  A
+// lane's at most two pieces that also hold slots of the neighbouring band row in HBM (the
+// row's head and tail) are kept in registers and written element by element after the
+// sweep.  (An optional lane trade, kTradeStores, gives each group of four consecutive
+// lanes one row's 64 consecutive bytes, which the memory pipeline writes as one run; the
+// trade's LDS round trip costs more than it gains here, so it is off.)
 #include <type_traits>
 
 #include "launch.hpp"
@@ -107,16 +111,24 @@ constexpr int kThreads = kComputeThreads + kLoadThreads;
 constexpr int kComputeWaves = kComputeThreads / 64;
 constexpr int kRows = kQkRows;                // 128 = 8 waves x 16 rows
 constexpr int kMaxSlots = 513;
-constexpr int kRingDup = 48;                  // ring rows mirrored past its end
+constexpr int kRingDup = 80;                  // ring rows mirrored past its end
+constexpr bool kTradeStores = false;          // lane trades before band stores
 constexpr int kStagePer = 8;                  // 16-byte chunks per thread per load batch
                                               // (4 for d = 128, whose sweep needs the registers)
+
+// Band stores: raw buffer resource (stride 0, range in bytes; word 3 of the gfx9 buffer
+// descriptor for untyped 32-bit access).  Offsets at or past kBufRange are dropped.
+constexpr int kBufRange = 0x7ffffff0;
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufDrop = static_cast<int>(0x80000000u);
+// Largest tile band span the 32-bit store offsets must cover (checked by the planner).
+constexpr int64_t kMaxTileSpan = (int64_t(1) << 31) - (int64_t(1) << 20);
 
 struct QkArgs {
     int64_t n, h, K, w, s;
     TileGrid g;
     int32_t ring;      // key rows in the LDS ring (a multiple of 16, >= 2 kRows + KB - 1)
     int32_t q_off;     // LDS byte offset of the two query tiles
-    int32_t p_off;     // LDS byte offset of the parked row-end pieces
     uint32_t nwg;      // persistent workgroups
     uint32_t pad;      // padding constant, already rounded to the output type
     TileDecode dc;     // tiles over workgroups, tile -> coordinates
@@ -183,62 +195,60 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
     const uint32_t row_bytes = static_cast<uint32_t>(row_step * D * 2);   // per class row
     const int ringc = a.ring;
     const P padv = Pack<Out>::splat(a.pad);
-    // Column offset of this lane's four (after pairing: eight) columns in a step.
-    const int off_g = k16 ? (grp == 1 ? 16 : (grp == 2 ? 8 : (grp == 3 ? 24 : 0))) : 4 * grp;
-    // Parked row-end pieces of this wave: [row k][head, tail] x 16 bytes.
-    unsigned char* park = lds + a.p_off + cw * (16 * 2 * 16);
 
     uint32_t tile, tend;
     unit_range(a.dc, xcd_rank(blockIdx.x, a.nwg), &tile, &tend);
 
     // Ring rows below kRingDup are written twice, the second time past the ring's end,
-    // so that two blocks starting at any row r < ringc (rows r .. r + 16 + 22) are read
-    // unwrapped.
+    // so that a pair of steps starting at any row r < ringc (rows r .. r + 32 + 16 + 22) is
+    // read unwrapped.
     auto put_ring = [&](int slot, int ch, const u32x4& v) {
         *reinterpret_cast<u32x4*>(ring + swz<D>(slot, ch)) = v;
         if (slot < kRingDup) *reinterpret_cast<u32x4*>(ring + swz<D>(slot + ringc, ch)) = v;
     };
     // Batch b0 of a Stage moved by NT threads (this one is number gt): kPer 16-byte
-    // chunks per thread, chunk b0 + gt + NT x; the key rows' chunks first, then the query
-    // rows'.  Sources are addressed by 32-bit byte offsets from the strip's first row.
-    // Every entry of buf is loaded (chunks past the end re-read the last one), which keeps
-    // a held batch in one set of registers; only the LDS writes are predicated.
+    // chunks per thread, chunk b0 + gt + NT x, i.e. chunk column gt mod kChunks of stage row
+    // (b0 + gt) / kChunks + x NT / kChunks; stage rows are the key rows, then the query
+    // rows.  Sources are addressed by 32-bit byte offsets from the strip's first row.
+    // Every entry of buf is loaded (rows past the end re-read the last one), which keeps a
+    // held batch in one set of registers; only the LDS writes are predicated.
+    constexpr int kChunkShift = D == 32 ? 2 : (D == 64 ? 3 : 4);
     auto load_batch = [&](const Stage& sg, int gt, int b0, u32x4* buf, auto nt_c) {
-        constexpr int NT = decltype(nt_c)::value;
-        const int nkc = sg.nk * kChunks;
-        const int total = nkc + kRows * kChunks;
-        const unsigned char* kb8 = reinterpret_cast<const unsigned char*>(kx + sg.row0 * D);
-        const unsigned char* qb8 = reinterpret_cast<const unsigned char*>(q + sg.row0 * D);
+        constexpr int kRowsX = decltype(nt_c)::value >> kChunkShift;
+        const int ch = gt & (kChunks - 1);
+        const int rr0 = (b0 + gt) >> kChunkShift;
+        const int last = sg.nk + kRows - 1;
+        const int dq = sg.tq0 - sg.nk - sg.u_first;       // query row of stage row rr: rr + dq
+        const unsigned char* kb8 =
+            reinterpret_cast<const unsigned char*>(kx + sg.row0 * D) + ch * 16;
+        const unsigned char* qb8 =
+            reinterpret_cast<const unsigned char*>(q + sg.row0 * D) + ch * 16;
 #pragma unroll
         for (int x = 0; x < kPer; ++x) {
-            int idx = b0 + gt + NT * x;
-            idx = idx < total ? idx : total - 1;
-            const bool isk = idx < nkc;
-            const int j = isk ? idx : idx - nkc;
-            const int rr = j / kChunks, ch = j % kChunks;
-            int u = isk ? sg.u_first + rr : sg.tq0 + rr;
+            int rr = rr0 + kRowsX * x;
+            rr = rr < last ? rr : last;
+            const bool isk = rr < sg.nk;
+            int u = sg.u_first + rr + (isk ? 0 : dq);
             u = u < 0 ? 0 : (u < sg.n_r ? u : sg.n_r - 1);
-            const uint32_t off = static_cast<uint32_t>(u) * row_bytes + ch * 16;
+            const uint32_t off = __umul24(static_cast<uint32_t>(u), row_bytes);
             buf[x] = ld_global16((isk ? kb8 : qb8) + off);
         }
     };
     auto write_batch = [&](const Stage& sg, int gt, int b0, const u32x4* buf, auto nt_c) {
-        constexpr int NT = decltype(nt_c)::value;
-        const int nkc = sg.nk * kChunks;
-        const int total = nkc + kRows * kChunks;
+        constexpr int kRowsX = decltype(nt_c)::value >> kChunkShift;
+        const int ch = gt & (kChunks - 1);
+        const int rr0 = (b0 + gt) >> kChunkShift;
+        const int rows = sg.nk + kRows;
 #pragma unroll
         for (int x = 0; x < kPer; ++x) {
-            const int idx = b0 + gt + NT * x;
-            if (idx < total) {
-                const bool isk = idx < nkc;
-                const int j = isk ? idx : idx - nkc;
-                const int rr = j / kChunks, ch = j % kChunks;
-                if (isk) {
+            const int rr = rr0 + kRowsX * x;
+            if (rr < rows) {
+                if (rr < sg.nk) {
                     int slot = sg.slot_first + rr;
                     slot = slot < ringc ? slot : slot - ringc;
                     put_ring(slot, ch, buf[x]);
                 } else {
-                    *reinterpret_cast<u32x4*>(lds + sg.qbuf + swz<D>(rr, ch)) = buf[x];
+                    *reinterpret_cast<u32x4*>(lds + sg.qbuf + swz<D>(rr - sg.nk, ch)) = buf[x];
                 }
             }
         }
@@ -261,9 +271,26 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
         int64_t row0;
         bool ok;                   // not an empty tail block of a shorter residue class
     };
-    auto info = [&](uint32_t tl) {
+    // Tile ids are walked in order: the next id by carrying through the grid extents.
+    auto next_id = [&](TileId t) {
+        if (++t.tb == static_cast<int>(a.dc.rb.d)) {
+            t.tb = 0;
+            if (++t.kb == static_cast<int>(a.dc.nkb.d)) {
+                t.kb = 0;
+                if (++t.r == static_cast<int>(a.dc.res.d)) {
+                    t.r = 0;
+                    if (++t.hh == static_cast<int>(a.dc.h.d)) {
+                        t.hh = 0;
+                        ++t.bb;
+                    }
+                }
+            }
+        }
+        return t;
+    };
+    auto info = [&](const TileId& id) {
         TInfo f;
-        f.t = decode_fast(a.dc, tl);
+        f.t = id;
         f.n_r = class_len_fast(a.dc, f.t.r);
         f.t0 = f.t.tb * kRows;
         f.ok = f.t0 < f.n_r;
@@ -304,8 +331,20 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
     u32x4 lbuf[kPer];
     bool lheld = false;
 
+    // This tile, the next and the one after (ids past the range decode to unused values).
+    TileId id2 = decode_fast(a.dc, tile);
+    TInfo inf0 = info(id2);
+    id2 = next_id(id2);
+    TInfo inf1 = info(id2);
+    id2 = next_id(id2);
+
     for (; tile < tend; ++tile) {
-        const TInfo cur = info(tile);
+        const TInfo cur = inf0;
+        TInfo nxt = inf1;
+        const TInfo nn = info(id2);
+        id2 = next_id(id2);
+        inf0 = inf1;
+        inf1 = nn;
         if (!cur.ok) {
             ready = lheld = false;
             continue;
@@ -315,26 +354,23 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
         const int64_t k0 = static_cast<int64_t>(cur.t.kb) * a.g.kb;
         const int64_t row0 = cur.row0;
 
-        if (!ready) {
-            // Nothing prefetched: every wave loads the whole key window and the query tile.
-            s0 = 0;
-            stage_from(Stage{row0, u0, W, 0, t0, n_r, a.q_off + qsel * kQBytes}, tid, 0,
-                       std::integral_constant<int, kThreads>{});
-            __syncthreads();
-        }
+        if (!ready) s0 = 0;
 
         // The next tile's rows go to LDS while this one is swept, when the ring holds both.
         bool pre = false, cont = false;
         int at = 0;
         Stage nx{};
-        TInfo nxt{};
-        nxt.ok = false;
-        if (tile + 1 < tend) {
-            nxt = info(tile + 1);
-            if (nxt.ok) {
-                nx = link(cur, nxt, s0, a.q_off + (qsel ^ 1) * kQBytes, &cont, &at);
-                pre = at + nx.nk <= ringc;
-            }
+        if (tile + 1 >= tend) nxt.ok = false;
+        if (nxt.ok) {
+            nx = link(cur, nxt, s0, a.q_off + (qsel ^ 1) * kQBytes, &cont, &at);
+            pre = at + nx.nk <= ringc;
+        }
+
+        if (!ready) {
+            // Nothing prefetched: every wave loads the whole key window and the query tile.
+            stage_from(Stage{row0, u0, W, 0, t0, n_r, a.q_off + qsel * kQBytes}, tid, 0,
+                       std::integral_constant<int, kThreads>{});
+            __syncthreads();
         }
 
         if (!computes) {
@@ -346,16 +382,13 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
                 stage_from(nx, lt, kLoadThreads * kPer, nt);
             }
             lheld = false;
-            if (nxt.ok && tile + 2 < tend) {
-                const TInfo nn = info(tile + 2);
-                if (nn.ok) {
-                    bool c2;
-                    int at2;
-                    const Stage nx2 = link(nxt, nn, 0, 0, &c2, &at2);   // rows only
-                    if (at2 + nx2.nk <= ringc) {
-                        load_batch(nx2, lt, 0, lbuf, nt);
-                        lheld = true;
-                    }
+            if (nxt.ok && tile + 2 < tend && nn.ok) {
+                bool c2;
+                int at2;
+                const Stage nx2 = link(nxt, nn, 0, 0, &c2, &at2);   // rows only
+                if (at2 + nx2.nk <= ringc) {
+                    load_batch(nx2, lt, 0, lbuf, nt);
+                    lheld = true;
                 }
             }
         } else {
@@ -374,6 +407,19 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
                 static_cast<int>((kVec - (rowA & (kVec - 1))) & (kVec - 1)));
             const bool row_ok = il < rows_here;
             const bool key_edge = u0 < 0 || u0 + W > n_r;     // window touches a sequence end
+            // Before a piece is stored, lanes trade pieces (ds_bpermute) so that each group of
+            // four consecutive lanes holds four consecutive pieces of one row, which the memory
+            // pipeline writes as one 64-byte run.  Lane 16 b + 4 a + j then stores row
+            // srow = 4 a + b of the wave's 16 (tile row ils), columns off_s .. of each step.  In
+            // the MFMA layout lane 16 g + c holds row c: for f32 columns 4 g .., for 16-bit
+            // outputs (after pairing two blocks) columns 0, 16, 8, 24 .. for g = 0, 1, 2, 3.
+            const int srow = kTradeStores ? 4 * ((lane >> 2) & 3) + (lane >> 4) : col;
+            const int sj = kTradeStores ? lane & 3 : (k16 ? ((grp & 1) << 1) | (grp >> 1) : grp);
+            const int ils = cw + 8 * srow;
+            const bool row_ok_s = ils < rows_here;
+            const int off_s = k16 ? 8 * sj : 4 * sj;
+            const int src_g = k16 ? (((sj & 1) << 1) | (sj >> 1)) : sj;   // holds off_s ..
+            const int bp_addr = (16 * src_g + srow) * 4;
 
             // Blocks: from the one holding the first piece of row `cw` (it starts at the
             // largest column <= cw that is = o mod kVec, so at least cw - kVec + 1) to the
@@ -434,14 +480,27 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
                 }
                 return val;
             };
-            // Step st: this lane's piece starts at column x0 = 16 (jb_lo + kBPS st) + o + off_g,
-            // i.e. slot x0 - il; whole pieces lie at slots 0 .. kbeff - kVec.
-            const int slot_base = 16 * jb_lo + o + off_g - il;
+            // Step st: the piece this lane stores starts at column x0 = 16 (jb_lo + kBPS st) + o
+            // + off_s, i.e. slot x0 - ils; whole pieces lie at slots 0 .. kbeff - kVec.
+            const int slot_base = 16 * jb_lo + o + off_s - ils;
             const int full_max = kbeff - kVec;
-            OT* const gbase = band + (rowA + 16 * jb_lo + o + off_g);   // 16-byte aligned
+            // Whole pieces are stored through a buffer resource based at the tile's band
+            // origin: this lane's piece of step st sits (ils (gstep - 1) + 16 jb_lo + o + off_s
+            // + kCS st) elements past it, a 16-byte aligned spot.  Pieces that are not whole
+            // (or rows past the class) get an offset beyond the resource's range, whose stores
+            // the hardware drops: no branch, no exec mask.
+            const bool any_full = row_ok_s && full_max >= 0;
+            const int sb_full = any_full ? slot_base : -(1 << 30);
+            const unsigned fm_full = any_full ? static_cast<unsigned>(full_max) : 0u;
+            const int lane_off = static_cast<int>(
+                (static_cast<int64_t>(ils) * (gstep - 1) + 16 * jb_lo + o + off_s) *
+                static_cast<int64_t>(sizeof(OT)));
+            const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+                band + ((row0 + static_cast<int64_t>(t0) * row_step) * K + k0), 0, kBufRange,
+                kBufWord3);
             // A step holds a row's partial piece only near the ends of the sweep: slot0 >=
-            // 16 kBPS st - 143 (jb_lo >= -1, o >= 0, off_g >= 0, il <= 127) and slot0 <=
-            // 16 kBPS st + 24 (16 jb_lo + o <= x_first <= il), so only steps below st_h or from
+            // 16 kBPS st - 143 (jb_lo >= -1, o >= 0, off_s >= 0, ils <= 127) and slot0 <=
+            // 16 kBPS st + 24 (16 jb_lo + o <= x_first <= ils), so only steps below st_h or from
             // st_t on look for them.
             constexpr int kCS = 16 * kBPS;                   // columns per step
             const int st_h = (143 + kCS) / kCS;
@@ -455,11 +514,13 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
                 return d <= 0 ? 0 : (d + kCS - 1) / kCS;
             };
             int st_hd = first_step(-(kVec - 1));
-            if (!row_ok || slot_base + kCS * st_hd > -1) st_hd = -1;
+            if (!row_ok_s || slot_base + kCS * st_hd > -1) st_hd = -1;
             const int lo_t = full_max + 1 > 0 ? full_max + 1 : 0;
             int st_tl = first_step(lo_t);
-            if (!row_ok || slot_base + kCS * st_tl >= kbeff) st_tl = -1;
-            auto finish = [&](auto edge, int st, const f32x4* acc) {
+            if (!row_ok_s || slot_base + kCS * st_tl >= kbeff) st_tl = -1;
+            // Step st's piece in the store layout: rounded (and padded), paired into 16-byte
+            // pieces for 16-bit outputs, then traded between lanes.
+            auto gather_ = [&](auto edge, int st, const f32x4* acc) {
                 const int jb = jb_lo + kBPS * st;
                 u32x4 own;
                 if constexpr (k16) {
@@ -470,24 +531,57 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
                 } else {
                     own = pack(edge, jb, acc[0]);
                 }
+                if constexpr (!kTradeStores) return own;
+                u32x4 pc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    pc[i] = static_cast<uint32_t>(
+                        __builtin_amdgcn_ds_bpermute(bp_addr, static_cast<int>(own[i])));
+                return pc;
+            };
+            // Steps whose keys all lie inside the class: ub + kCS st .. + kCS - 1 in [0, n_r);
+            // on tiles touching a sequence end, those skip the per-block padding checks.
+            const int ub = u0 + 16 * jb_lo + o;
+            const int st_in_lo = ub >= 0 ? 0 : (kCS - 1 - ub) / kCS;
+            int st_in_n = n_r - kCS - ub >= 0 ? (n_r - kCS - ub) / kCS + 1 - st_in_lo : 0;
+            st_in_n = st_in_n > 0 ? st_in_n : 0;
+            auto gather = [&](auto edge, int st, const f32x4* acc) {
+                if constexpr (decltype(edge)::value) {
+                    if (static_cast<unsigned>(st - st_in_lo) < static_cast<unsigned>(st_in_n))
+                        return gather_(std::false_type{}, st, acc);
+                }
+                return gather_(edge, st, acc);
+            };
+            // Store step st's piece: whole pieces to HBM, the row's partial ones to LDS.
+            // The lane's partial pieces are kept in registers (head steps all come before
+            // st_h, tail steps from st_t on) and stored element by element after the sweep.
+            u32x4 hpc = {0u, 0u, 0u, 0u}, tpc = {0u, 0u, 0u, 0u};
+            auto put = [&](int st, const u32x4& pc) {
                 const int sst = 16 * kBPS * st;
-                const int slot0 = slot_base + sst;
-                if (row_ok && full_max >= 0 &&
-                    static_cast<unsigned>(slot0) <= static_cast<unsigned>(full_max))
-                    *reinterpret_cast<u32x4*>(gbase + sst) = own;
-                if (st < st_h || st >= st_t) {
-                    if (st == st_hd || st == st_tl)   // head piece (holds slot 0) or tail piece
-                        *reinterpret_cast<u32x4*>(park + (2 * col + (st == st_tl ? 1 : 0)) * 16) = own;
+                const bool whole = static_cast<unsigned>(sb_full + sst) <= fm_full;
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    pc, brs, whole ? lane_off + sst * static_cast<int>(sizeof(OT)) : kBufDrop,
+                    0, 0);
+                if (st < st_h) {
+                    const bool mine = st == st_hd;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) hpc[i] = mine ? pc[i] : hpc[i];
+                }
+                if (st >= st_t) {   // (the two ranges overlap when kbeff is small)
+                    const bool mine = st == st_tl;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) tpc[i] = mine ? pc[i] : tpc[i];
                 }
             };
 
-            // Software pipeline: the MFMAs of step st + 1 and the key fragment reads of step
-            // st + 2 are issued before step st is finished; the loop runs steps in pairs, the
-            // accumulators alternating between two sets (an odd count gets one more step,
-            // whose columns no row stores; past the last step the reads work on ring rows
-            // nobody stores).  The scheduling barriers keep that order; the empty asm with a
-            // memory clobber keeps the compiler from folding the loop-carried fragment reads
-            // back into reads at their use.
+            // Software pipeline, per step st: the MFMAs of step st + 1, the lane trades of
+            // step st, the key fragment reads of step st + 2 (issued after the trades, so that
+            // waiting for the trades leaves them in flight), then step st's stores.  The loop
+            // runs steps in pairs, the accumulators alternating between two sets (an odd count
+            // gets one more step, whose columns no row stores; past the last step the reads
+            // work on ring rows nobody stores).  The scheduling barriers keep that order; the
+            // empty asm with a memory clobber keeps the compiler from folding the loop-carried
+            // fragment reads back into reads at their use.
             auto sweep = [&](auto edge) {
                 V kf[kBPS][kDC];
                 f32x4 acc_a[kBPS], acc_b[kBPS];
@@ -496,16 +590,22 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
                     base += 16 * kBPS;
                     base = base < ringc ? base : base - ringc;
                 };
-                auto mma_fetch = [&](f32x4* acc) {
+                // The first step of a pair reads up to 70 rows past a base below ringc (inside
+                // the mirrored rows), so only the second one wraps.
+                auto step = [&](f32x4* acc_out, const f32x4* acc_in, int st, bool wrap) {
                     asm volatile("" ::: "memory");
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int bq = 0; bq < kBPS; ++bq) acc[bq] = mma(kf[bq]);
+                    for (int bq = 0; bq < kBPS; ++bq) acc_out[bq] = mma(kf[bq]);
                     __builtin_amdgcn_sched_barrier(0);
-                    advance();
+                    const u32x4 pc = gather(edge, st, acc_in);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (wrap) advance();
+                    else base += 16 * kBPS;
 #pragma unroll
                     for (int bq = 0; bq < kBPS; ++bq) fetch(base + 16 * bq, kf[bq]);
                     __builtin_amdgcn_sched_barrier(0);
+                    put(st, pc);
                 };
 #pragma unroll
                 for (int bq = 0; bq < kBPS; ++bq) fetch(base + 16 * bq, kf[bq]);
@@ -515,10 +615,8 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
 #pragma unroll
                 for (int bq = 0; bq < kBPS; ++bq) fetch(base + 16 * bq, kf[bq]);
                 for (int st = 0; st < nsteps; st += 2) {
-                    mma_fetch(acc_b);
-                    finish(edge, st, acc_a);
-                    mma_fetch(acc_a);
-                    finish(edge, st + 1, acc_b);
+                    step(acc_b, acc_a, st, false);
+                    step(acc_a, acc_b, st + 1, true);
                 }
             };
             if (key_edge)
@@ -526,27 +624,27 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
             else
                 sweep(std::false_type{});
 
-            // Parked row-end pieces, element by element: lane (k, g), g < 2, takes row k's head
-            // (g = 0) or tail (g = 1) piece.  A row's head piece starts at column x_first + 8 k
-            // (slot -((il - o) mod kVec)); its tail piece holds slot kbeff - 1.  The piece is
-            // read into named scalars before the per-element stores (store_part), which keeps
-            // the element selection out of divergent vector code.
-            if (grp < 2) {
-                const int sh = x_first + 8 * col - il;         // head piece: slot0 in (-kVec, 0]
-                const int xl = il + kbeff - 1;                 // last column of the row
-                const int st_ = xl - ((xl - o + kVec) & (kVec - 1)) - il;   // tail piece slot0
-                const int slot0 = grp ? st_ : sh;
-                // The head piece is parked when it starts before slot 0; the tail piece when it
-                // starts at or after slot 0 and runs past the last slot.
-                const bool parked = row_ok && (grp ? (st_ >= 0 && st_ + kVec > kbeff) : sh < 0);
-                if (parked) {
-                    const u32x4 pc = *reinterpret_cast<const u32x4*>(park + (2 * col + grp) * 16);
-                    const uint32_t d0 = pc[0], d1 = pc[1], d2 = pc[2], d3 = pc[3];
-                    const int pa = slot0 < 0 ? -slot0 : 0;
-                    const int pe = kbeff - slot0 < kVec ? kbeff - slot0 : kVec;
-                    store_part<OT>(band + (rowA + il + slot0), d0, d1, d2, d3, pa, pe);
+            // Partial pieces, element by element: slots inside 0 .. kbeff - 1 only; the other
+            // elements (and pieces the lane does not hold) get out-of-range offsets.
+            auto put_part = [&](int st, const u32x4& pc) {
+                const int slot0 = slot_base + kCS * st;
+                const int e_lo = st < 0 ? kVec : (slot0 < 0 ? -slot0 : 0);
+                const int e_hi = kbeff - slot0 < kVec ? kbeff - slot0 : kVec;
+                const int off0 = lane_off + kCS * st * static_cast<int>(sizeof(OT));
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) {
+                    const int off = e >= e_lo && e < e_hi
+                                        ? off0 + e * static_cast<int>(sizeof(OT)) : kBufDrop;
+                    if constexpr (k16)
+                        __builtin_amdgcn_raw_buffer_store_b16(
+                            static_cast<unsigned short>(pc[e >> 1] >> (16 * (e & 1))), brs, off,
+                            0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b32(pc[e], brs, off, 0, 0);
                 }
-            }
+            };
+            if (st_hd >= 0) put_part(st_hd, hpc);
+            if (st_tl >= 0) put_part(st_tl, tpc);
         }
         __syncthreads();                                  // this tile's LDS reads are done
         ready = pre;
@@ -559,11 +657,11 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
 }
 
 struct Layout {
-    int64_t kb = 0, ring = 0, q_off = 0, p_off = 0, bytes = 0;
+    int64_t kb = 0, ring = 0, q_off = 0, bytes = 0;
 };
 
-// LDS layout for a chunk of kb slots: the key ring (plus its mirrored rows), two query
-// tiles, the parked row-end pieces.  The ring holds two whole windows where that fits, so
+// LDS layout for a chunk of kb slots: the key ring (plus its mirrored rows) and two query
+// tiles.  The ring holds two whole windows where that fits, so
 // that a tile starting a new strip is loaded while the one before it is swept, and at
 // least a window plus the kRows keys a continuing tile adds.
 Layout layout_for(int64_t kb, int64_t d) {
@@ -573,8 +671,7 @@ Layout layout_for(int64_t kb, int64_t d) {
         l.kb = kb;
         l.ring = ceil_div(rows, 16) * 16;
         l.q_off = ceil_div((l.ring + kRingDup) * d * 2, 16) * 16;
-        l.p_off = l.q_off + 2 * kRows * d * 2;
-        l.bytes = l.p_off + kComputeWaves * 16 * 2 * 16;
+        l.bytes = l.q_off + 2 * kRows * d * 2;
         if (l.bytes <= kQkLdsBytes) break;
     }
     return l;
@@ -585,7 +682,7 @@ hipError_t launch_typed(const void* q, const void* k, void* band, const Problem&
                         const QkTilePlan& tp, uint32_t pad, hipStream_t stream) {
     const Layout l = layout_for(tp.grid.kb, D);
     QkArgs a{p.n, p.h, p.K, p.w, p.s, tp.grid, static_cast<int32_t>(l.ring),
-             static_cast<int32_t>(l.q_off), static_cast<int32_t>(l.p_off),
+             static_cast<int32_t>(l.q_off),
              static_cast<uint32_t>(tp.workgroups), pad,
              make_decode(tp.grid, p.h, p.n, p.s, tp.grid.tiles, tp.workgroups)};
     auto kern = qk_mfma_kernel<In, Out, D>;
@@ -617,8 +714,8 @@ hipError_t launch_d(const void* q, const void* k, void* band, const Problem& p,
 }  // namespace
 
 QkTilePlan plan_qk_mfma(const Problem& p, int out_dt) {
-    (void)out_dt;
     QkTilePlan tp;
+    const int64_t out_bytes = out_dt == kF32 ? 4 : 2;
     // The widest chunk (at most 513 slots) whose ring + query tiles fit in LDS ...
     int64_t max_slots = kMaxSlots;
     while (max_slots > 16 && layout_for(max_slots, p.d).bytes > kQkLdsBytes) --max_slots;
@@ -645,6 +742,9 @@ QkTilePlan plan_qk_mfma(const Problem& p, int out_dt) {
     // (q and k rows of one strip are addressed by 32-bit byte offsets)
     tp.ok = tp.grid.tiles <= kMaxTiles && ceil_div(p.n, p.s) < (int64_t(1) << 30) &&
             (p.n + p.s) * p.h * p.d * 2 < (int64_t(1) << 32) &&
+            kRows * p.s * p.h * p.K * out_bytes < kMaxTileSpan &&   // band store offsets
+            p.s * p.h * p.d * 2 < (int64_t(1) << 24) &&             // 24-bit row offsets
+            ceil_div(p.n, p.s) < (int64_t(1) << 24) &&
             p.K < (int64_t(1) << 30) && l.bytes <= kQkLdsBytes && tp.workgroups >= 1;
     return tp;
 }

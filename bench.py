@@ -17,8 +17,10 @@ before the timed region; R rotating buffer sets (> 256 MB in total) keep one ste
 operands out of the Infinity Cache of the previous steps.  The value is the whole
 step's algorithmic HBM bytes per second (each input read once, each output written
 once; pv / pvT / softmax read only in-range band slots); useful TFLOP/s (2*d per
-in-range slot of qk, pv, pvT) is reported beside it.  The roofline object is for the
-qk kernel at dilation 0, timed with HIP events on the stream it runs on.
+in-range slot of qk, pv, pvT) is reported beside it.  Per-kernel times come from the
+library's kernel timers: HIP events recorded at each kernel's own start and end on the
+stream it runs on, for every launch of the timed steps.  The roofline object is for the
+qk kernel at dilation 0.
 """
 from __future__ import annotations
 
@@ -237,16 +239,11 @@ def main():
         return
 
     ops = [(dil, op) for dil in DILATIONS for op in ("qk", "softmax", "pv", "pvT")]
-    events = {key: [] for key in ops}
 
-    def step(t, record):
+    def step(t):
         for dil in DILATIONS:
             S = t[f"S{dil}"]
             for op in ("qk", "softmax", "pv", "pvT"):
-                if record:
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
                 if op == "qk":
                     dm.diagmm_qk(t["q"], t["k"], W, WU, dil, 0.0, out=S)
                 elif op == "softmax":
@@ -255,24 +252,32 @@ def main():
                     dm.diagmm_pv(S, t["v"], W, WU, dil, out=t[f"O{dil}"])
                 else:
                     dm.diagmm_pvT(S, t["do"], W, WU, dil, out=t[f"X{dil}"])
-                if record:
-                    e1.record(stream)
-                    events[(dil, op)].append((e0, e1))
 
     for i in range(args.warmup):
-        step(sets[i % len(sets)], False)
+        step(sets[i % len(sets)])
     torch.cuda.synchronize()
+    # Per-kernel times: the library's kernel timers record HIP events at each kernel's own
+    # start and end on the stream it runs on, for every launch of the timed steps.
+    dm.diagmm_timing_begin(args.steps * len(ops))
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % len(sets)], True)
+        step(sets[i % len(sets)])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    dm.diagmm_timing_end()
+    recs = dm.diagmm_timing_read()
+    assert len(recs) == args.steps * len(ops), (len(recs), args.steps * len(ops))
+    kernel_ms = {key: [] for key in ops}
+    for i, (name, ms) in enumerate(recs):
+        key = ops[i % len(ops)]
+        assert name == key[1], (i, name, key)
+        kernel_ms[key].append(ms)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     per_op = {}
     step_bytes = step_flops = 0
     for (dil, op) in ops:
-        ms = sum(a.elapsed_time(b_) for a, b_ in events[(dil, op)]) / len(events[(dil, op)])
+        ms = sum(kernel_ms[(dil, op)]) / len(kernel_ms[(dil, op)])
         c = op_costs(dil)[op]
         step_bytes += c["bytes"]
         step_flops += c["flops"]

@@ -154,6 +154,25 @@ diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d
                             int64_t w_upper, int64_t dilation, diagmm_dtype_t in_dtype,
                             diagmm_dtype_t out_dtype, diagmm_plan_t* plan);
 
+/*
+ * Kernel timers, a measurement aid for benchmarks (not part of the method).  Between
+ * diagmm_timing_begin(capacity) and diagmm_timing_end(), each of the next `capacity`
+ * kernel launches by this library records a pair of HIP events at the kernel's own start
+ * and end on the stream it is launched on (hipExtLaunchKernel), tagged with the entry
+ * point (the diagmm_plan modes: 0 qk, 1 pv, 2 pvT, 3 banded softmax); further launches
+ * run untimed.  One session at a time, process-wide, on one device (the events are made
+ * on the device current at diagmm_timing_begin; launches on another device are not to be
+ * timed).  diagmm_timing_read waits for the recorded kernels and writes, for the first
+ * min(max, count) launches in launch order, the entry point tag (ops[i]) and the kernel
+ * time in milliseconds (ms[i]); *count receives the number of launches recorded.  The
+ * arrays are host memory owned by the caller.  Errors: DIAGMM_ERR_SHAPE for capacity
+ * outside 1 .. 2^20, DIAGMM_ERR_NULL for a null count (or null arrays with max > 0),
+ * DIAGMM_ERR_HIP if an event call fails.
+ */
+diagmm_status_t diagmm_timing_begin(int64_t capacity);
+diagmm_status_t diagmm_timing_end(void);
+diagmm_status_t diagmm_timing_read(int64_t max, int32_t* ops, double* ms, int64_t* count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,7 @@ import os
 import torch
 
 __all__ = ["diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax", "diagmm_plan",
+           "diagmm_timing_begin", "diagmm_timing_end", "diagmm_timing_read",
            "diagmm_abi_version", "library_path", "load", "DiagmmError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +80,13 @@ def load() -> ctypes.CDLL:
     lib.diagmm_abi_version.restype = ci
     lib.diagmm_plan.argtypes = [ci] + [i64] * 7 + [ci, ci, ctypes.POINTER(_Plan)]
     lib.diagmm_plan.restype = ci
+    lib.diagmm_timing_begin.argtypes = [i64]
+    lib.diagmm_timing_begin.restype = ci
+    lib.diagmm_timing_end.argtypes = []
+    lib.diagmm_timing_end.restype = ci
+    lib.diagmm_timing_read.argtypes = [i64, ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    lib.diagmm_timing_read.restype = ci
     _lib = lib
     return lib
 
@@ -216,3 +224,36 @@ def diagmm_plan(mode, b, n, h, d, w, w_upper=None, dilation=0, in_dtype=torch.fl
             "slots_per_tile": pl.slots_per_tile, "tiles": pl.tiles,
             "workgroups": pl.workgroups, "threads": pl.threads, "lds_bytes": pl.lds_bytes,
             "residues": pl.residues}
+
+
+def diagmm_timing_begin(capacity: int) -> None:
+    """Start recording kernel start/end events for the next ``capacity`` launches."""
+    lib = load()
+    st = lib.diagmm_timing_begin(int(capacity))
+    if st:
+        _raise(lib, st)
+
+
+def diagmm_timing_end() -> None:
+    """Stop recording (launches after this run untimed)."""
+    lib = load()
+    st = lib.diagmm_timing_end()
+    if st:
+        _raise(lib, st)
+
+
+def diagmm_timing_read() -> list:
+    """Waits for the timed kernels; returns [(mode name, kernel ms), ...] in launch order."""
+    lib = load()
+    count = ctypes.c_int64(0)
+    st = lib.diagmm_timing_read(0, None, None, ctypes.byref(count))
+    if st:
+        _raise(lib, st)
+    n = count.value
+    ops = (ctypes.c_int32 * max(n, 1))()
+    ms = (ctypes.c_double * max(n, 1))()
+    st = lib.diagmm_timing_read(n, ops, ms, ctypes.byref(count))
+    if st:
+        _raise(lib, st)
+    names = {v: k for k, v in MODES.items()}
+    return [(names.get(ops[i], str(ops[i])), ms[i]) for i in range(n)]

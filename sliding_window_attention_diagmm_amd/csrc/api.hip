@@ -174,6 +174,7 @@ diagmm_status_t diagmm_qk(const void* q, const void* k, void* band, int64_t b, i
         return fail(DIAGMM_ERR_ALIAS, "diagmm_qk: band overlaps q or k");
     const uint32_t pad = pad_bits(padding_value, out_dtype);
     const Plan plan = plan_qk(p, in_dtype, out_dtype);
+    timing_set_op(kOpQk);
     return launched("diagmm_qk", run_qk(plan, q, k, band, p, in_dtype, out_dtype, pad,
                                         static_cast<hipStream_t>(stream)));
 }
@@ -195,6 +196,7 @@ static diagmm_status_t pv_like(const char* fn, int mode, const void* band, const
         return fail(DIAGMM_ERR_ALIAS, "%s: output overlaps an input", fn);
     const Plan plan = mode == 1 ? plan_pv(p, in_dtype, out_dtype) : plan_pvT(p, in_dtype, out_dtype);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    timing_set_op(mode == 1 ? kOpPv : kOpPvT);
     return launched(fn, mode == 1 ? run_pv(plan, band, x, out, p, in_dtype, out_dtype, s)
                                   : run_pvT(plan, band, x, out, p, in_dtype, out_dtype, s));
 }
@@ -233,6 +235,7 @@ diagmm_status_t diagmm_banded_softmax(const void* scores, void* probs, int64_t b
         return fail(DIAGMM_ERR_ALIAS, "diagmm_banded_softmax: probs overlaps scores (only "
                     "exact in-place with equal dtypes is allowed)");
     const Plan plan = plan_softmax(p, in_dtype, out_dtype);
+    timing_set_op(kOpSoftmax);
     return launched("diagmm_banded_softmax",
                     run_softmax(plan, scores, probs, p, scale, in_dtype, out_dtype,
                                 static_cast<hipStream_t>(stream)));

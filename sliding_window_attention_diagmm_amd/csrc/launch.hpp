@@ -4,6 +4,7 @@
 
 #include "common.hpp"
 #include "tiles.hpp"
+#include "timing.hpp"
 
 namespace diagmm {
 

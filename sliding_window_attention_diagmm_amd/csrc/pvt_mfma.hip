@@ -459,7 +459,7 @@ hipError_t launch_typed(const void* band, const void* x, void* out, bool out_f32
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
         static_cast<int>(kPvLdsBytes));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(tp.workgroups)), dim3(kThreads),
+    launch_kernel(kern, dim3(static_cast<uint32_t>(tp.workgroups)), dim3(kThreads),
                        static_cast<size_t>(l.bytes), stream,
                        static_cast<const typename In::T*>(band),
                        static_cast<const typename In::T*>(x), out, out_f32 ? 1 : 0, a);

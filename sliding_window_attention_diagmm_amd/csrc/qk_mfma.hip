@@ -692,7 +692,7 @@ hipError_t launch_typed(const void* q, const void* k, void* band, const Problem&
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
         static_cast<int>(kQkLdsBytes));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(tp.workgroups)), dim3(kThreads),
+    launch_kernel(kern, dim3(static_cast<uint32_t>(tp.workgroups)), dim3(kThreads),
                        static_cast<size_t>(l.bytes), stream,
                        static_cast<const typename In::T*>(q),
                        static_cast<const typename In::T*>(k),

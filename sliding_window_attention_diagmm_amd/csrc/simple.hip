@@ -161,7 +161,7 @@ hipError_t launch_qk_simple(const void* q, const void* k, void* band, const Prob
         typename Out::T padv;
         if constexpr (Out::code == kF32) padv = __builtin_bit_cast(float, pad);
         else padv = static_cast<uint16_t>(pad);
-        hipLaunchKernelGGL((qk_simple_kernel<In, Out>), dim3(blocks_for(total)), dim3(kThreads),
+        launch_kernel((qk_simple_kernel<In, Out>), dim3(blocks_for(total)), dim3(kThreads),
                            0, stream, static_cast<const typename In::T*>(q),
                            static_cast<const typename In::T*>(k),
                            static_cast<typename Out::T*>(band), p, padv, total);
@@ -175,7 +175,7 @@ hipError_t launch_pv_simple(const void* band, const void* v, void* out, const Pr
     return dispatch(in_dt, out_dt, [&](auto in, auto o) {
         using In = decltype(in);
         using Out = decltype(o);
-        hipLaunchKernelGGL((pv_simple_kernel<In, Out>), dim3(blocks_for(total)), dim3(kThreads),
+        launch_kernel((pv_simple_kernel<In, Out>), dim3(blocks_for(total)), dim3(kThreads),
                            0, stream, static_cast<const typename In::T*>(band),
                            static_cast<const typename In::T*>(v),
                            static_cast<typename Out::T*>(out), p, total);
@@ -189,7 +189,7 @@ hipError_t launch_pvT_simple(const void* band, const void* x, void* out, const P
     return dispatch(in_dt, out_dt, [&](auto in, auto o) {
         using In = decltype(in);
         using Out = decltype(o);
-        hipLaunchKernelGGL((pvT_simple_kernel<In, Out>), dim3(blocks_for(total)),
+        launch_kernel((pvT_simple_kernel<In, Out>), dim3(blocks_for(total)),
                            dim3(kThreads), 0, stream, static_cast<const typename In::T*>(band),
                            static_cast<const typename In::T*>(x),
                            static_cast<typename Out::T*>(out), p, total);
@@ -204,7 +204,7 @@ hipError_t launch_softmax_rows(const void* scores, void* probs, const Problem& p
     return dispatch(in_dt, out_dt, [&](auto in, auto o) {
         using In = decltype(in);
         using Out = decltype(o);
-        hipLaunchKernelGGL((softmax_rows_kernel<In, Out>), dim3(grid), dim3(kThreads), 0, stream,
+        launch_kernel((softmax_rows_kernel<In, Out>), dim3(grid), dim3(kThreads), 0, stream,
                            static_cast<const typename In::T*>(scores),
                            static_cast<typename Out::T*>(probs), p, scale, nrows);
         return hipGetLastError();

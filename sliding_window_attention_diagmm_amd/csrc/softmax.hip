@@ -277,7 +277,7 @@ hipError_t launch_g(const void* scores, void* probs, const Problem& p, float sca
     const int64_t nrows = p.rows() * p.h;
     const int64_t per_block = kRowsPerBlock * (64 / L);
     const int64_t grid = (nrows + per_block - 1) / per_block;
-    hipLaunchKernelGGL((softmax_group_kernel<T, L>), dim3(static_cast<uint32_t>(grid)),
+    launch_kernel((softmax_group_kernel<T, L>), dim3(static_cast<uint32_t>(grid)),
                        dim3(kThreads), 0, stream, static_cast<const typename T::T*>(scores),
                        static_cast<typename T::T*>(probs), p, scale, nrows,
                        RowDiv{make_div32(static_cast<uint32_t>(p.h)),
@@ -291,7 +291,7 @@ hipError_t launch_p(const void* scores, void* probs, const Problem& p, float sca
                     hipStream_t stream) {
     const int64_t nrows = p.rows() * p.h;
     const int64_t grid = (nrows + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL((softmax_wave_kernel<T, P>), dim3(static_cast<uint32_t>(grid)),
+    launch_kernel((softmax_wave_kernel<T, P>), dim3(static_cast<uint32_t>(grid)),
                        dim3(kThreads), 0, stream, static_cast<const typename T::T*>(scores),
                        static_cast<typename T::T*>(probs), p, scale, nrows,
                        RowDiv{make_div32(static_cast<uint32_t>(p.h)),

@@ -51,7 +51,7 @@ def check_close(gpu: torch.Tensor, ref64: torch.Tensor, in_dtype, what: str, mas
         tol = torch.maximum(tol, out_ulp(r, gpu.dtype))
     bad = diff > tol
     assert not bad.any(), (f"{what}: {int(bad.sum())} elements out of tolerance, worst "
-                           f"{diff.max().item():.3e} (ref {r[diff.argmax()].item():.4g})")
+                           f"{diff.max().item():.3e} (ref {r.flatten()[diff.argmax()].item():.4g})")
     return diff.max().item()
 
 

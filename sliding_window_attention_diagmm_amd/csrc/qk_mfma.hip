@@ -114,7 +114,7 @@ constexpr int kMaxSlots = 513;
 constexpr int kRingDup = 80;                  // ring rows mirrored past its end
 constexpr bool kTradeStores = false;          // lane trades before band stores
 constexpr int kStagePer = 8;                  // 16-byte chunks per thread per load batch
-                                              // (4 for d = 128, whose sweep needs the registers)
+                                              // (2 for d = 128, whose sweep needs the registers)
 
 // Band stores: raw buffer resource (stride 0, range in bytes; word 3 of the gfx9 buffer
 // descriptor for untyped 32-bit access).  Offsets at or past kBufRange are dropped.
@@ -177,7 +177,7 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
     constexpr int kChunks = D / 8;                        // 16-byte chunks per row
     constexpr int kQBytes = kRows * D * 2;
     constexpr int kBPS = k16 ? 2 : 1;                     // blocks per step
-    constexpr int kPer = D >= 128 ? kStagePer / 2 : kStagePer;
+    constexpr int kPer = D >= 128 ? kStagePer / 4 : kStagePer;
 
     extern __shared__ __align__(16) unsigned char lds[];
     unsigned char* ring = lds;
@@ -626,22 +626,41 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
 
             // Partial pieces, element by element: slots inside 0 .. kbeff - 1 only; the other
             // elements (and pieces the lane does not hold) get out-of-range offsets.
+            // The valid elements form one stretch, bytes [a, b) of the 16-byte piece; it
+            // goes out as aligned 2-, 4-, 8-, 4- and 2-byte stores taken greedily from the
+            // left (at most three of them apply to a row end, and since a wave's rows share
+            // their alignment, all lanes holding such a piece need the same ones).
             auto put_part = [&](int st, const u32x4& pc) {
                 const int slot0 = slot_base + kCS * st;
-                const int e_lo = st < 0 ? kVec : (slot0 < 0 ? -slot0 : 0);
+                const int e_lo = slot0 < 0 ? -slot0 : 0;
                 const int e_hi = kbeff - slot0 < kVec ? kbeff - slot0 : kVec;
-                const int off0 = lane_off + kCS * st * static_cast<int>(sizeof(OT));
-#pragma unroll
-                for (int e = 0; e < kVec; ++e) {
-                    const int off = e >= e_lo && e < e_hi
-                                        ? off0 + e * static_cast<int>(sizeof(OT)) : kBufDrop;
-                    if constexpr (k16)
-                        __builtin_amdgcn_raw_buffer_store_b16(
-                            static_cast<unsigned short>(pc[e >> 1] >> (16 * (e & 1))), brs, off,
-                            0, 0);
-                    else
-                        __builtin_amdgcn_raw_buffer_store_b32(pc[e], brs, off, 0, 0);
+                constexpr int esz = static_cast<int>(sizeof(OT));
+                int a = e_lo * esz;
+                const int b = e_hi * esz;
+                const int off0 = lane_off + kCS * st * esz;
+                auto word = [&](int byte) { return pc[byte >> 2]; };
+                if ((a & 3) == 2 && a + 2 <= b) {
+                    __builtin_amdgcn_raw_buffer_store_b16(
+                        static_cast<unsigned short>(word(a) >> 16), brs, off0 + a, 0, 0);
+                    a += 2;
                 }
+                if ((a & 7) == 4 && a + 4 <= b) {
+                    __builtin_amdgcn_raw_buffer_store_b32(word(a), brs, off0 + a, 0, 0);
+                    a += 4;
+                }
+                if (a + 8 <= b) {
+                    const u32x2 dw = (a & 8) ? u32x2{pc[2], pc[3]} : u32x2{pc[0], pc[1]};
+                    __builtin_amdgcn_raw_buffer_store_b64(dw, brs, off0 + a, 0, 0);
+                    a += 8;
+                }
+                if (a + 4 <= b) {
+                    __builtin_amdgcn_raw_buffer_store_b32(word(a), brs, off0 + a, 0, 0);
+                    a += 4;
+                }
+                if (a + 2 <= b)
+                    __builtin_amdgcn_raw_buffer_store_b16(
+                        static_cast<unsigned short>(word(a) >> (8 * (a & 2))), brs, off0 + a,
+                        0, 0);
             };
             if (st_hd >= 0) put_part(st_hd, hpc);
             if (st_tl >= 0) put_part(st_tl, tpc);

@@ -157,15 +157,24 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
     u32x4 vb[kPer64V];
 
     const int npw = band_pieces(a.g.kb);                    // pieces per staged row
-    const float inv_npw = 1.0f / static_cast<float>(npw);
     // Piece x of this thread is (il, q): staged row il, window columns 8q .. 8q+7, i.e.
-    // slots lo .. lo+7 with lo = 8q - il.  idx / npw by a float reciprocal is exact here:
-    // idx < 2^13, so the error is far below the 1/(2 npw) margin around the integers.
+    // slots lo .. lo+7 with lo = 8q - il, for idx = tid + x kThreads = il npw + q (the
+    // same for every item, so worked out once).  idx / npw by a float reciprocal is exact
+    // here: idx < 2^13, so the error is far below the 1/(2 npw) margin around the integers.
+    int pil[kBandPieces], plo[kBandPieces];
+    {
+        const float inv_npw = 1.0f / static_cast<float>(npw);
+#pragma unroll
+        for (int x = 0; x < kBandPieces; ++x) {
+            const int idx = tid + x * kThreads;
+            const int r = static_cast<int>((static_cast<float>(idx) + 0.5f) * inv_npw);
+            pil[x] = r;
+            plo[x] = 8 * (idx - r * npw) - r;
+        }
+    }
     auto piece_of = [&](int x, int* il, int* lo) {
-        const int idx = tid + x * kThreads;
-        const int r = static_cast<int>((static_cast<float>(idx) + 0.5f) * inv_npw);
-        *il = r;
-        *lo = 8 * (idx - r * npw) - r;
+        *il = pil[x];
+        *lo = plo[x];
     };
     // Slots of row il that take part: inside the chunk, key u0 + il + slot in [0, n_r).
     auto valid_slots = [&](const Item& it, int il, int* va, int* vb) {
@@ -217,6 +226,7 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
             piece_of(x, &il, &lo);
             if (il < it.rows_here) {
                 valid_slots(it, il, &va, &vb);
+                if (va >= vb) va = vb = 1 << 30;            // no valid slot: all zeros
                 u32x4 val = u32x4{0u, 0u, 0u, 0u};
                 if (lo + 8 > va && lo < vb) {
                     const int64_t off = base + row_off(il) + lo;
@@ -233,22 +243,24 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
             }
         }
     };
-    // Zero the stray elements of the head and tail pieces of every staged row: window
-    // columns [8 floor(xa / 8), xa) and [xb, 8 ceil(xb / 8)), where [xa, xb) = il + valid
-    // slots.  Task (il, k): k < 8 clears head column 8 floor(xa / 8) + k, k >= 8 tail
-    // column xb + k - 8 (both stay inside the row: xb <= 63 + kbeff < XW).  Runs after the
+    // Mask the head and tail pieces of every staged row to its valid window columns
+    // [xa, xb) = il + valid slots: one 16-byte read-modify-write per piece (thread 2 il
+    // the head piece, 2 il + 1 the tail piece unless it is the head piece too).  A row with
+    // no valid slot has all its pieces staged as zeros (store_band).  Runs after the
     // pieces are written (a barrier in between).
     auto clear_strays = [&](const Item& it) {
-        for (int task = tid; task < kRows * 16; task += kThreads) {
-            const int il = task >> 4, k = task & 15;
-            if (il >= it.rows_here) continue;
-            int va, vb;
-            valid_slots(it, il, &va, &vb);
-            const int xa = il + va, xb = il + vb;
-            const int x = k < 8 ? (xa & ~7) + k : xb + (k - 8);
-            const bool stray = k < 8 ? x < xa : (x & ~7) == (xb & ~7);
-            if (stray) reinterpret_cast<uint16_t*>(pst)[il * rsp + x] = 0;
-        }
+        if (tid >= 2 * kRows) return;
+        const int il = tid >> 1, tail = tid & 1;
+        if (il >= it.rows_here) return;
+        int va, vb;
+        valid_slots(it, il, &va, &vb);
+        const int xa = il + va, xb = il + vb;
+        if (xa >= xb) return;
+        const int ph = xa & ~7, pt = (xb - 1) & ~7;
+        if (tail && pt == ph) return;
+        const int pc = tail ? pt : ph;
+        u32x4* pp = reinterpret_cast<u32x4*>(pst + il * rsp + pc);
+        *pp = mask_piece<ST>(*pp, xa - pc, xb - pc);
     };
     // One 16-byte piece of V row `slot` (channels ch*8 .. ch*8+7) into the ring.
     auto put_v = [&](int slot, int ch, const u32x4& pc) {

@@ -2,6 +2,7 @@
 // band-tile scheduler's choice of kernel, and error reporting.  Declarations and the
 // contract of every entry point are in include/diagmm.h.
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 
@@ -96,7 +97,14 @@ int device_cus() {
             cus = 256;
         cached[dev] = cus;
     }
-    return cached[dev];
+    // DIAGMM_MAX_WORKGROUPS=m caps the persistent grids at m workgroups (a testing switch:
+    // on a small grid each workgroup walks many tiles, strip changes included).
+    int cus = cached[dev];
+    if (const char* e = std::getenv("DIAGMM_MAX_WORKGROUPS")) {
+        const int m = std::atoi(e);
+        if (m >= 1 && m < cus) cus = m;
+    }
+    return cus;
 }
 
 // Round-to-nearest-even of a float into the 16-bit types, on the host.

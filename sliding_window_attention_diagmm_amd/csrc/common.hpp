@@ -129,7 +129,8 @@ struct Problem {
     __host__ __device__ int64_t rows() const { return b * n; }
 };
 
-// Compute units of the current device (cached per device; 256 on MI355X).
+// Persistent workgroups per launch: the compute units of the current device (cached per
+// device; 256 on MI355X), capped by DIAGMM_MAX_WORKGROUPS when that is set.
 int device_cus();
 
 // Host-side rounding of the padding constant to the output type (nearest even),

@@ -121,6 +121,17 @@ __device__ __forceinline__ void store_part(ST* gp, uint32_t d0, uint32_t d1, uin
     }
 }
 
+// Wait until every vector memory operation of this wave has completed (s_waitcnt with
+// vmcnt 0 and the other counters left at their maxima: expcnt 7, lgkmcnt 15).
+//
+// The compiler's wait insertion tracks loads per register, and a load whose value is
+// only used under a condition it cannot match to the load's own stays "pending" on the
+// other path.  A later write of the same register anywhere downstream - an LDS read in a
+// compute loop, say - then gets a full vmcnt(0), which also waits for loads issued just
+// before (a prefetch meant to overlap that loop).  Calling this where such loads are
+// known to be consumed clears them from the tracking at no cost.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ------------------------------------------------------------------ problem descriptor
 
 struct Problem {

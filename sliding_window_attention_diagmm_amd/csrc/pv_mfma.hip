@@ -289,23 +289,34 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
                 if (rr < it.W) put_v(rr, ch, buf[x]);
             }
         }
+        wait_vmem_all();    // every batch is consumed: keep the loads off later waits
     };
-    // The 64 new keys of a sliding next item (its window columns W-64 .. W-1).
+    // The 64 new rows of a sliding next item (its window columns W-64 .. W-1).  Rows past
+    // the sequence are read at the nearest row inside it and zeroed when staged, so the
+    // prefetch writes its registers with loads alone: no wait is due between it and the
+    // staging after the next barrier.
+    auto new_row = [&](const Item& nx, int rr) {
+        const int i = nx.u0 + nx.W - kRows + rr;
+        return i < 0 ? 0 : (i < nx.n_r ? i : nx.n_r - 1);
+    };
     auto load_new_v = [&](const Item& nx) {
 #pragma unroll
         for (int x = 0; x < kPer64V; ++x) {
             const int idx = tid + x * kThreads, rr = idx / kChunks, ch = idx % kChunks;
-            if (rr < kRows) vb[x] = get_v(nx, nx.W - kRows + rr, ch);
+            if (rr < kRows)
+                vb[x] = *reinterpret_cast<const u32x4*>(
+                    v + (nx.row0 + static_cast<int64_t>(new_row(nx, rr)) * row_step) * D + ch * 8);
         }
     };
-    auto store_new_v = [&](int slot_first) {
+    auto store_new_v = [&](const Item& nx, int slot_first) {
 #pragma unroll
         for (int x = 0; x < kPer64V; ++x) {
             const int idx = tid + x * kThreads, rr = idx / kChunks, ch = idx % kChunks;
             if (rr < kRows) {
+                const int i = nx.u0 + nx.W - kRows + rr;
                 int slot = slot_first + rr;
                 slot = slot < ringc ? slot : slot - ringc;
-                put_v(slot, ch, vb[x]);
+                put_v(slot, ch, i >= 0 && i < nx.n_r ? vb[x] : u32x4{0u, 0u, 0u, 0u});
             }
         }
     };
@@ -349,8 +360,8 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
         const bool next_slides = has_next && a.g.nkb == 1 && nx.t.tb == it.t.tb + 1 &&
                                  nx.t.r == it.t.r && nx.t.hh == it.t.hh && nx.t.bb == it.t.bb;
         if (has_next) {
-            load_band(nx);
             if (next_slides) load_new_v(nx);
+            load_band(nx);
         }
 
         // ---- compute: out^T[c][i] += sum_x VT[c][x] * B[x][i]
@@ -431,7 +442,7 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
         if (has_next) {
             store_band(nx);
             if (next_slides) {
-                store_new_v(s0 + it.W);                     // slots past the current window
+                store_new_v(nx, s0 + it.W);                 // slots past the current window
                 s0 += kRows;
                 s0 = s0 < ringc ? s0 : s0 - ringc;
             }

@@ -265,22 +265,34 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
                 if (rr < it.W) put_x(rr, ch, buf[q]);
             }
         }
+        wait_vmem_all();    // every batch is consumed: keep the loads off later waits
+    };
+    // The 64 new rows of a sliding next item (its window columns W-64 .. W-1).  Rows past
+    // the sequence are read at the nearest row inside it and zeroed when staged, so the
+    // prefetch writes its registers with loads alone: no wait is due between it and the
+    // staging after the next barrier.
+    auto new_row = [&](const Item& nx, int rr) {
+        const int i = nx.ilo + nx.W - kRows + rr;
+        return i < 0 ? 0 : (i < nx.n_r ? i : nx.n_r - 1);
     };
     auto load_new_x = [&](const Item& nx) {
 #pragma unroll
         for (int q = 0; q < kPer64X; ++q) {
             const int idx = tid + q * kThreads, rr = idx / kChunks, ch = idx % kChunks;
-            if (rr < kRows) xb[q] = get_x(nx, nx.W - kRows + rr, ch);
+            if (rr < kRows)
+                xb[q] = *reinterpret_cast<const u32x4*>(
+                    x + (nx.row0 + static_cast<int64_t>(new_row(nx, rr)) * row_step) * D + ch * 8);
         }
     };
-    auto store_new_x = [&](int slot_first) {
+    auto store_new_x = [&](const Item& nx, int slot_first) {
 #pragma unroll
         for (int q = 0; q < kPer64X; ++q) {
             const int idx = tid + q * kThreads, rr = idx / kChunks, ch = idx % kChunks;
             if (rr < kRows) {
+                const int i = nx.ilo + nx.W - kRows + rr;
                 int slot = slot_first + rr;
                 slot = slot < ringc ? slot : slot - ringc;
-                put_x(slot, ch, xb[q]);
+                put_x(slot, ch, i >= 0 && i < nx.n_r ? xb[q] : u32x4{0u, 0u, 0u, 0u});
             }
         }
     };
@@ -330,8 +342,8 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
         const bool next_slides = has_next && a.g.nkb == 1 && nx.t.tb == it.t.tb + 1 &&
                                  nx.t.r == it.t.r && nx.t.hh == it.t.hh && nx.t.bb == it.t.bb;
         if (has_next) {
-            load_seg(nx);
             if (next_slides) load_new_x(nx);
+            load_seg(nx);
         }
 
         // ---- compute: out^T[c][j] += sum_x XT[c][x] * B[x][j]
@@ -407,7 +419,7 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
         if (has_next) {
             store_seg(nx);
             if (next_slides) {
-                store_new_x(s0 + it.W);                     // slots past the current window
+                store_new_x(nx, s0 + it.W);                 // slots past the current window
                 s0 += kRows;
                 s0 = s0 < ringc ? s0 : s0 - ringc;
             }

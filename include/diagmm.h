@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DIAGMM_ABI_VERSION 1
+#define DIAGMM_ABI_VERSION 2
 
 typedef enum {
     DIAGMM_F32 = 0,
@@ -148,6 +148,10 @@ typedef struct {
     int64_t threads;        /* threads per workgroup */
     int64_t lds_bytes;      /* LDS per workgroup */
     int64_t residues;       /* residue classes the rows are split into (s) */
+    int64_t strip_workgroups; /* pv, pvT: workgroups given to each strip (the row blocks of
+                                 one residue class of one (batch, head)) when the tiles are
+                                 split strip by strip; 0 when they are balanced over all
+                                 workgroups at once */
 } diagmm_plan_t;
 
 diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,

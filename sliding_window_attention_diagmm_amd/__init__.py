@@ -46,7 +46,8 @@ class _Plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_char * 48), ("rows_per_tile", ctypes.c_int64),
                 ("slots_per_tile", ctypes.c_int64), ("tiles", ctypes.c_int64),
                 ("workgroups", ctypes.c_int64), ("threads", ctypes.c_int64),
-                ("lds_bytes", ctypes.c_int64), ("residues", ctypes.c_int64)]
+                ("lds_bytes", ctypes.c_int64), ("residues", ctypes.c_int64),
+                ("strip_workgroups", ctypes.c_int64)]
 
 
 _lib = None
@@ -223,7 +224,7 @@ def diagmm_plan(mode, b, n, h, d, w, w_upper=None, dilation=0, in_dtype=torch.fl
     return {"kernel": pl.kernel.decode(), "rows_per_tile": pl.rows_per_tile,
             "slots_per_tile": pl.slots_per_tile, "tiles": pl.tiles,
             "workgroups": pl.workgroups, "threads": pl.threads, "lds_bytes": pl.lds_bytes,
-            "residues": pl.residues}
+            "residues": pl.residues, "strip_workgroups": pl.strip_workgroups}
 
 
 def diagmm_timing_begin(capacity: int) -> None:

@@ -50,6 +50,7 @@ struct PvTilePlan {
     TileGrid grid;          // nkb / kb: slot chunks per tile and slots per chunk
     int64_t lds_bytes = 0;
     int64_t workgroups = 0;
+    int64_t strip_wgs = 0;  // workgroups per strip with the strip split, 0 = flat split
     bool ok = false;
 };
 

@@ -478,8 +478,10 @@ PvLayout pv_layout(int64_t kc, int64_t d) {
 TileDecode unit_decode(const PvTilePlan& tp, const Problem& p) {
     const TileGrid& g = tp.grid;
     const int64_t units = g.tiles / g.nkb;
-    return make_decode(TileGrid{g.res, g.rb, 1, g.kb, units}, p.h, p.n, p.s, units,
-                       tp.workgroups);
+    TileDecode dc = make_decode(TileGrid{g.res, g.rb, 1, g.kb, units}, p.h, p.n, p.s, units,
+                                tp.workgroups);
+    if (tp.strip_wgs > 0) set_strip_split(&dc, units / g.rb, g.rb, tp.strip_wgs);
+    return dc;
 }
 
 template <class In, int D>
@@ -525,6 +527,12 @@ PvTilePlan plan_pv_mfma(const Problem& p) {
     tp.lds_bytes = l.bytes;
     const int64_t cus = device_cus();
     tp.workgroups = tp.grid.tiles < cus ? tp.grid.tiles : cus;
+    // A strip: the row blocks (whole tiles) of one residue class of one (batch, head).
+    const int64_t per_strip = tp.grid.rb;
+    if (per_strip > 0 && tp.grid.nkb > 0)
+        tp.strip_wgs = pick_strip_split(tp.grid.tiles / tp.grid.nkb / per_strip, per_strip,
+                                        kRows, ceil_div(p.n, p.s) - (per_strip - 1) * kRows,
+                                        tp.workgroups);
     tp.ok = tp.grid.tiles <= kMaxTiles && ceil_div(p.n, p.s) < (int64_t(1) << 30) &&
             p.K < (int64_t(1) << 30) && l.bytes <= kPvLdsBytes && tp.workgroups >= 1 &&
             p.s * p.h * p.K < (int64_t(1) << 32) &&

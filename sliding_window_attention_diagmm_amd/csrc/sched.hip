@@ -71,6 +71,7 @@ Plan plan_pv(const Problem& p, int in_dt, int out_dt) {
     pl.threads = 512;
     pl.lds_bytes = tp.lds_bytes;
     pl.residues = tp.grid.res;
+    pl.strip_wgs = tp.strip_wgs;
     return pl;
 }
 
@@ -90,6 +91,7 @@ Plan plan_pvT(const Problem& p, int in_dt, int out_dt) {
     pl.threads = 512;
     pl.lds_bytes = tp.lds_bytes;
     pl.residues = tp.grid.res;
+    pl.strip_wgs = tp.strip_wgs;
     return pl;
 }
 

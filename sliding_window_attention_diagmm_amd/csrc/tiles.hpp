@@ -124,6 +124,12 @@ struct TileDecode {
     Div32 rb, nkb, res, h;
     uint32_t cls_q, cls_m;
     uint32_t unit_base, unit_rem;
+    // Strip split, used when strip_wgs > 0: the units form strip_count strips of
+    // strip_units consecutive ids, and workgroup rank strip * strip_wgs + j takes units of
+    // that strip only.  Its first strip_wgs - strip_rem workgroups take strip_q units each
+    // and the others one more, so the longer ranges sit at the end of the strip, where its
+    // last (possibly short) unit is.  Ranks past the strips get nothing.
+    uint32_t strip_wgs, strip_count, strip_units, strip_q, strip_rem;
 };
 
 inline TileDecode make_decode(const TileGrid& g, int64_t h, int64_t n, int64_t s,
@@ -137,7 +143,37 @@ inline TileDecode make_decode(const TileGrid& g, int64_t h, int64_t n, int64_t s
     t.cls_m = static_cast<uint32_t>(n % s);
     t.unit_base = static_cast<uint32_t>(units / nwg);
     t.unit_rem = static_cast<uint32_t>(units % nwg);
+    t.strip_wgs = t.strip_count = t.strip_units = t.strip_q = t.strip_rem = 0;
     return t;
+}
+
+// Workgroups per strip for the strip split, or 0 for the flat one (units balanced over all
+// workgroups to +-1), whichever leaves the busiest workgroup less work.  Strips hold
+// `per_strip` units of `unit_rows` rows, the last one `last_rows` rows (a ragged class
+// end); a full unit counts 1 and the short one a quarter (its fixed costs: a pass over its
+// band rows, the start and end of a tile) plus its share of rows.  The flat split counts
+// every unit as full, and is kept unless the strip split saves at least a quarter.
+inline int64_t pick_strip_split(int64_t strips, int64_t per_strip, int64_t unit_rows,
+                                int64_t last_rows, int64_t nwg) {
+    if (strips < 1 || per_strip < 1 || nwg < 1) return 0;
+    const int64_t g = nwg / strips;
+    if (g < 2 || g > per_strip) return 0;
+    const double flat = static_cast<double>(ceil_div(strips * per_strip, nwg));
+    const int64_t q = per_strip / g, rem = per_strip % g;
+    double last = 0.25 + static_cast<double>(last_rows) / static_cast<double>(unit_rows);
+    last = last < 1.0 ? last : 1.0;
+    const double split = rem == 0 ? static_cast<double>(q)
+                       : rem == 1 ? static_cast<double>(q) + last
+                                  : static_cast<double>(q + 1);
+    return split + 0.25 <= flat ? g : 0;
+}
+
+inline void set_strip_split(TileDecode* t, int64_t strips, int64_t per_strip, int64_t g) {
+    t->strip_wgs = static_cast<uint32_t>(g);
+    t->strip_count = static_cast<uint32_t>(strips);
+    t->strip_units = static_cast<uint32_t>(per_strip);
+    t->strip_q = static_cast<uint32_t>(per_strip / g);
+    t->strip_rem = static_cast<uint32_t>(per_strip % g);
 }
 
 // Tile id -> coordinates, as decode_tile (row block fastest).
@@ -163,9 +199,22 @@ __host__ __device__ inline int class_len_fast(const TileDecode& dc, int r) {
     return static_cast<int>(dc.cls_q) + (static_cast<uint32_t>(r) < dc.cls_m ? 1 : 0);
 }
 
-// Units [begin, end) of rank `rank`: the first unit_rem ranks take one extra.
+// Units [begin, end) of rank `rank`: with the strip split as set out at TileDecode, else
+// balanced over all ranks (the first unit_rem ranks take one extra).
 __host__ __device__ inline void unit_range(const TileDecode& dc, uint32_t rank,
                                            uint32_t* begin, uint32_t* end) {
+    if (dc.strip_wgs != 0) {
+        const uint32_t strip = rank / dc.strip_wgs, j = rank - strip * dc.strip_wgs;
+        if (strip >= dc.strip_count) {
+            *begin = *end = 0;
+            return;
+        }
+        const uint32_t lo = dc.strip_wgs - dc.strip_rem;      // ranges of strip_q units
+        *begin = strip * dc.strip_units +
+                 (j < lo ? j * dc.strip_q : lo * dc.strip_q + (j - lo) * (dc.strip_q + 1));
+        *end = *begin + dc.strip_q + (j < lo ? 0u : 1u);
+        return;
+    }
     const uint32_t extra = rank < dc.unit_rem ? rank : dc.unit_rem;
     *begin = rank * dc.unit_base + extra;
     *end = *begin + dc.unit_base + (rank < dc.unit_rem ? 1u : 0u);

@@ -22,6 +22,10 @@ CASES = [
     (2, 1100, 2, 64, 128, 40, 2, "bf16", "f32", 5),
     (1, 1500, 2, 32, 200, 200, 0, "f16", "f16", 3),
     (1, 900, 2, 128, 96, 96, 1, "bf16", "bf16", 7),
+    # the strip split for pv and pvT: 7 workgroups per strip of 8 row blocks (2 of 44 idle),
+    # and 2 per strip of 5 row blocks (ragged last blocks of 8 and 19 rows)
+    (1, 1366, 2, 64, 200, 200, 3, "f16", "f16", 44),
+    (2, 1100, 1, 64, 96, 30, 4, "bf16", "f32", 16),
 ]
 
 
@@ -35,6 +39,31 @@ def test_grid_cap_shapes_the_plan(monkeypatch):
     for mode in ("qk", "pv", "pvT"):
         pl = dm.diagmm_plan(mode, 1, 2048, 3, 64, 256, 256, 0, torch.float16)
         assert pl["workgroups"] <= 8 and pl["tiles"] >= 4 * pl["workgroups"], (mode, pl)
+
+
+def test_strip_split_choice(monkeypatch):
+    """pv and pvT split the tiles strip by strip where that shortens the busiest
+    workgroup's list: at n=4096, h=12, w=256, dilation 3 a strip (one residue class of one
+    head) has 21 full row blocks and one of 22 rows, so 7 workgroups per strip take 3 or
+    3 + the short one, against 4 full ones for 24 workgroups of the flat split."""
+    monkeypatch.delenv("DIAGMM_MAX_WORKGROUPS", raising=False)
+    for mode in ("pv", "pvT"):
+        pl = dm.diagmm_plan(mode, 1, 4096, 12, 64, 256, 256, 3, torch.float16)
+        if pl["workgroups"] == 256:
+            assert pl["strip_workgroups"] == 7, pl
+        for args in ((1, 4096, 12, 64, 256, 256, 0), (12, 4096, 12, 64, 256, 0, 0),
+                     (1, 32768, 12, 64, 4096, 4096, 0)):
+            assert dm.diagmm_plan(mode, *args, torch.float16)["strip_workgroups"] == 0
+    monkeypatch.setenv("DIAGMM_MAX_WORKGROUPS", "44")
+    for mode in ("pv", "pvT"):
+        assert dm.diagmm_plan(mode, 1, 1366, 2, 64, 200, 200, 3,
+                              torch.float16)["strip_workgroups"] == 7
+    monkeypatch.setenv("DIAGMM_MAX_WORKGROUPS", "16")
+    for mode in ("pv", "pvT"):
+        assert dm.diagmm_plan(mode, 2, 1100, 1, 64, 96, 30, 4,
+                              torch.bfloat16)["strip_workgroups"] == 2
+    assert dm.diagmm_plan("qk", 2, 1100, 1, 64, 96, 30, 4,
+                          torch.bfloat16)["strip_workgroups"] == 0
 
 
 @pytest.mark.gpu

@@ -155,12 +155,13 @@ __device__ __forceinline__ u32x4 ld_global16(const void* p) {
 __device__ __forceinline__ int align_gap(int W) { return (16 - (W & 15)) & 15; }
 
 // Rows one tile needs in LDS beyond what is already there: nk key rows of a class (keys
-// u_first .., clamped into the class) for ring slots slot_first .., and the tile's query
-// rows (tq0 ..) for a query buffer.
+// u_first .., clamped into the class) for ring slots slot_first .., and nq of the tile's
+// query rows (tq0 ..; all kRows of them, or none) for a query buffer.
 struct Stage {
     int64_t row0;      // [b][n][h] row of class row 0 of the tile's (batch, class, head)
     int u_first, nk, slot_first, tq0, n_r;
     int qbuf;          // LDS byte offset of the query buffer
+    int nq;
 };
 
 template <class In, class Out, int D>
@@ -217,7 +218,7 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
         constexpr int kRowsX = decltype(nt_c)::value >> kChunkShift;
         const int ch = gt & (kChunks - 1);
         const int rr0 = (b0 + gt) >> kChunkShift;
-        const int last = sg.nk + kRows - 1;
+        const int last = sg.nk + sg.nq - 1;
         const int dq = sg.tq0 - sg.nk - sg.u_first;       // query row of stage row rr: rr + dq
         const unsigned char* kb8 =
             reinterpret_cast<const unsigned char*>(kx + sg.row0 * D) + ch * 16;
@@ -238,7 +239,7 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
         constexpr int kRowsX = decltype(nt_c)::value >> kChunkShift;
         const int ch = gt & (kChunks - 1);
         const int rr0 = (b0 + gt) >> kChunkShift;
-        const int rows = sg.nk + kRows;
+        const int rows = sg.nk + sg.nq;
 #pragma unroll
         for (int x = 0; x < kPer; ++x) {
             const int rr = rr0 + kRowsX * x;
@@ -256,7 +257,7 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
     // The batches of a Stage from b0 on, each loaded and then written.
     auto stage_from = [&](const Stage& sg, int gt, int b0, auto nt_c) {
         constexpr int NT = decltype(nt_c)::value;
-        const int total = (sg.nk + kRows) * kChunks;
+        const int total = (sg.nk + sg.nq) * kChunks;
         for (; b0 < total; b0 += NT * kPer) {
             u32x4 buf[kPer];
             load_batch(sg, gt, b0, buf, nt_c);
@@ -304,27 +305,57 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
     // The rows tile nn needs after tile c (window at ring slot s0c).  A tile continuing
     // c's strip needs 128 new keys, right after c's window; one starting a strip its whole
     // window, from the first multiple of 16 past c's window (block reads assume windows
-    // start at such ring rows).  They go to the ring while c is swept only if the ring
-    // holds both (at + nk <= ringc).
-    auto link = [&](const TInfo& c, const TInfo& nn, int s0c, int qbuf, bool* cont, int* at) {
+    // start at such ring rows), less the first `skip` keys when those were written earlier.
+    // They go to the ring while c is swept only if the ring holds both (*fits: at + the
+    // keys nn adds <= ringc).
+    auto link = [&](const TInfo& c, const TInfo& nn, int s0c, int qbuf, int skip, bool* cont,
+                    int* at, bool* fits) {
         *cont = nn.t.tb == c.t.tb + 1 && nn.t.kb == c.t.kb && nn.t.r == c.t.r &&
                 nn.t.hh == c.t.hh && nn.t.bb == c.t.bb;
         *at = *cont ? c.W : c.W + align_gap(c.W);
+        const int add = *cont ? kRows : nn.W;
+        *fits = *at + add <= ringc;
+        skip = *cont ? 0 : skip;
         Stage sg;
         sg.row0 = nn.row0;
-        sg.u_first = *cont ? c.u0 + c.W : nn.u0;
-        sg.nk = *cont ? kRows : nn.W;
-        int sl = s0c + *at;
+        sg.u_first = *cont ? c.u0 + c.W : nn.u0 + skip;
+        sg.nk = add - skip;
+        int sl = s0c + *at + skip;
         sg.slot_first = sl < ringc ? sl : sl - ringc;
         sg.tq0 = nn.t0;
         sg.n_r = nn.n_r;
         sg.qbuf = qbuf;
+        sg.nq = kRows;
+        return sg;
+    };
+    // The first e keys of the window of a tile x that starts a strip, as key rows only, for
+    // ring slots from slot0 (the slot of x's window) on.
+    auto early_stage = [&](const TInfo& x, int slot0, int e) {
+        Stage sg;
+        sg.row0 = x.row0;
+        sg.u_first = x.u0;
+        sg.nk = e;
+        sg.slot_first = slot0 < ringc ? slot0 : slot0 - ringc;
+        sg.tq0 = x.t0;
+        sg.n_r = x.n_r;
+        sg.qbuf = 0;
+        sg.nq = 0;
         return sg;
     };
 
     bool ready = false;             // the current tile's keys and query rows are in LDS
     int s0 = 0;                     // ring slot of the current window's first key
     int qsel = 0;                   // query buffer of the current tile
+    // A tile that starts a strip needs a whole window, three times the keys a continuing
+    // tile adds.  When it comes two tiles after one that its predecessor continues, the
+    // first keys of its window are written while that earlier tile is swept, into ring
+    // rows neither window being swept then holds; the rest, with its query rows, then
+    // comes one tile early like a continuing tile's rows.  (A workgroup whose range
+    // crosses into a second strip would otherwise load that window within one tile and
+    // finish last.)  early_tile / early_n: the tile whose first early_n keys are written.
+    uint32_t early_tile = ~0u;
+    int early_n = 0;
+    constexpr int kEarlyCap = kLoadThreads * kPer / kChunks;   // key rows of one load batch
 
     // Load waves: the first batch of the rows the tile after next needs, loaded during
     // this tile and written to LDS during the next one.
@@ -361,15 +392,55 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
         int at = 0;
         Stage nx{};
         if (tile + 1 >= tend) nxt.ok = false;
+        const int qnext = a.q_off + (qsel ^ 1) * kQBytes;
         if (nxt.ok) {
-            nx = link(cur, nxt, s0, a.q_off + (qsel ^ 1) * kQBytes, &cont, &at);
-            pre = at + nx.nk <= ringc;
+            link(cur, nxt, s0, qnext, 0, &cont, &at, &pre);
+            // A cold tile followed by a strip start: the first keys of the next window are
+            // loaded with this tile's rows (they go past this window, at + e <= ringc).
+            if (!ready && pre && !cont) {
+                const int e = min(min(nxt.W, ringc - at), kEarlyCap);
+                early_tile = tile + 1;
+                early_n = e;
+            }
+            nx = link(cur, nxt, s0, qnext, early_tile == tile + 1 ? early_n : 0, &cont, &at,
+                      &pre);
+        }
+        // The tile after next starts a strip and the next one continues this one: the first
+        // e2 keys of its window go to ring rows from s0 + kRows + at2 (its window's slot)
+        // while this tile is swept.  This tile's window lies kRows before the next one's, so
+        // rows up to ringc - kRows past the next window's slot are free.
+        int e2 = 0, slot2 = 0;
+        if (pre && cont && tile + 2 < tend && nn.ok && early_tile != tile + 2) {
+            bool c2, fit2;
+            int at2;
+            link(nxt, nn, 0, 0, 0, &c2, &at2, &fit2);
+            if (!c2 && fit2) {
+                e2 = min(min(nn.W, ringc - kRows - at2), kEarlyCap);
+                slot2 = s0 + kRows + at2;
+                slot2 = slot2 < ringc ? slot2 : slot2 - ringc;
+                if (e2 > 0) {
+                    early_tile = tile + 2;
+                    early_n = e2;
+                }
+            }
         }
 
         if (!ready) {
-            // Nothing prefetched: every wave loads the whole key window and the query tile.
-            stage_from(Stage{row0, u0, W, 0, t0, n_r, a.q_off + qsel * kQBytes}, tid, 0,
-                       std::integral_constant<int, kThreads>{});
+            // Nothing prefetched: every wave loads the whole key window and the query tile,
+            // or, when the early keys of the next strip's window come too, the compute waves
+            // the window and query tile and the load waves those keys.
+            const Stage cold{row0, u0, W, 0, t0, n_r, a.q_off + qsel * kQBytes, kRows};
+            const bool e1 = early_tile == tile + 1;
+            if (!e1 && e2 <= 0) {
+                stage_from(cold, tid, 0, std::integral_constant<int, kThreads>{});
+            } else if (computes) {
+                stage_from(cold, tid, 0, std::integral_constant<int, kComputeThreads>{});
+            } else {
+                const int lt = tid - kComputeThreads;
+                constexpr auto nt = std::integral_constant<int, kLoadThreads>{};
+                stage_from(e1 ? early_stage(nxt, s0 + at, early_n) : early_stage(nn, slot2, e2),
+                           lt, 0, nt);
+            }
             __syncthreads();
         }
 
@@ -381,12 +452,14 @@ qk_mfma_kernel(const typename In::T* __restrict__ q, const typename In::T* __res
                 write_batch(nx, lt, 0, lbuf, nt);
                 stage_from(nx, lt, kLoadThreads * kPer, nt);
             }
+            if (ready && e2 > 0) stage_from(early_stage(nn, slot2, e2), lt, 0, nt);
             lheld = false;
             if (nxt.ok && tile + 2 < tend && nn.ok) {
-                bool c2;
+                bool c2, fit2;
                 int at2;
-                const Stage nx2 = link(nxt, nn, 0, 0, &c2, &at2);   // rows only
-                if (at2 + nx2.nk <= ringc) {
+                const Stage nx2 = link(nxt, nn, 0, 0, early_tile == tile + 2 ? early_n : 0,
+                                       &c2, &at2, &fit2);   // rows only
+                if (fit2) {
                     load_batch(nx2, lt, 0, lbuf, nt);
                     lheld = true;
                 }

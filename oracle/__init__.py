@@ -17,7 +17,10 @@ posts 1, 3, 5 and 6): with stride ``s = max(dilation, 1)`` and ``K = w + w_upper
 * ``pvT``: out[b,j,h,:] = sum over (i,k) with i+(k-w)s = j of band[b,i,h,k] * X[b,i,h,:]
   (backward function with transpose_t1 = 1);
 * ``softmax``: per band row, scale, mask out-of-range slots to -inf, max, exp, sum,
-  divide (attention softmax of the first fusion repro on csarofeen/pytorch issue 2096).
+  divide (attention softmax of the first fusion repro on csarofeen/pytorch issue 2096);
+* ``softmax_bwd``: the derivative of that softmax with respect to the stored scores,
+  scale * P * (dP - sum(P * dP)) per row over in-range slots, 0 elsewhere (not printed
+  on the pages; the chain rule through the recipe above).
 """
 from __future__ import annotations
 
@@ -62,6 +65,7 @@ def _load():
             lib.oracle_pv.argtypes = [vp, vp, vp] + [i64] * 7 + [ci, ci, vp, i64, ci]
             lib.oracle_pvT.argtypes = [vp, vp, vp] + [i64] * 7 + [ci, ci, vp, i64, ci]
             lib.oracle_softmax.argtypes = [vp, vp] + [i64] * 6 + [cd, ci, ci, vp, i64, ci]
+            lib.oracle_softmax_bwd.argtypes = [vp, vp, vp] + [i64] * 6 + [cd, ci, ci, vp, i64, ci]
             for f in (lib.oracle_qk, lib.oracle_pv, lib.oracle_pvT, lib.oracle_softmax):
                 f.restype = ci
             lib.oracle_convert.argtypes = [vp, vp, i64, ci]
@@ -173,6 +177,36 @@ def softmax(scores, w, w_upper, dilation=0, scale=1.0, out_dtype=None, n=None, r
                             threads or default_threads())
     if st:
         raise ValueError(f"oracle.softmax: bad arguments ({st})")
+    return out
+
+
+def softmax_bwd(probs, dprobs, w, w_upper, dilation=0, scale=1.0, out_dtype=None, n=None,
+                rows=None, threads=None):
+    """Gradient of the banded softmax with respect to its stored scores, given its
+    probabilities ``probs`` and the gradient ``dprobs`` with respect to them (both band
+    tensors [b, n, h, K] of one dtype, or packed [len(rows), h, K] with ``n`` given)."""
+    lib = _load()
+    p = _check(probs, "probs")
+    dp = _check(dprobs, "dprobs")
+    if dp.dtype != p.dtype or dp.shape != p.shape:
+        raise ValueError("oracle.softmax_bwd: probs and dprobs differ in dtype or shape")
+    out_dtype = out_dtype or p.dtype
+    rt, rp, nr = _rows(rows)
+    if rt is None:
+        b, n, h, K = p.shape
+    else:
+        if n is None:
+            raise ValueError("oracle.softmax_bwd: n is required with a row list")
+        b = 1
+        _, h, K = p.shape
+    if K != w + w_upper + 1:
+        raise ValueError("oracle.softmax_bwd: band width mismatch")
+    out = torch.empty(p.shape, dtype=out_dtype)
+    st = lib.oracle_softmax_bwd(_ptr(p), _ptr(dp), _ptr(out), b, n, h, w, w_upper, dilation,
+                                float(scale), _CODE[p.dtype], _CODE[out_dtype], rp, nr,
+                                threads or default_threads())
+    if st:
+        raise ValueError(f"oracle.softmax_bwd: bad arguments ({st})")
     return out
 
 

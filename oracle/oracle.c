@@ -31,6 +31,10 @@
  *     holds; the banded softmax masks them to -inf, so their probability is 0;
  *   - dense layout [b][n][h][d], band layout [b][n][h][K], both contiguous.
  *
+ * The banded softmax backward is not printed on the pages: it is the derivative of the
+ * softmax recipe above with respect to the stored scores, the operation that feeds
+ * the two backward functions of post 6 the band gradient they multiply.
+ *
  * Arithmetic: every element is widened exactly to double, products and sums are
  * formed in double, and the result is rounded once, to nearest-even, to the output
  * type (OR_F64 keeps the unrounded double, for tolerance checks).
@@ -301,6 +305,46 @@ int oracle_softmax(const void* scores, void* probs, int64_t b, int64_t n, int64_
                 double p = 0.0;
                 if (j >= 0 && j < n) p = exp(scale * or_load(scores, row + k, in_dt) - m) / sum;
                 or_store(probs, row + k, out_dt, p);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ softmax backward
+ * Per (bb, i, hh) row, with P the probabilities of the banded softmax above and dP the
+ * gradient of a loss with respect to them: the gradient with respect to the stored
+ * scores S is, by the chain rule through x_k = scale * S[k] and P = softmax(x),
+ *     dS_k = scale * P_k * (dP_k - sum_m P_m dP_m)      for in-range slots k, m,
+ *     dS_k = 0                                           for out-of-range slots,
+ * out-of-range slots of P and dP never entering the sum (they are masked by index, as
+ * in the forward softmax, whatever they hold). */
+int oracle_softmax_bwd(const void* probs, const void* dprobs, void* dscores, int64_t b,
+                       int64_t n, int64_t h, int64_t w, int64_t wu, int64_t dil, double scale,
+                       int in_dt, int out_dt, const int64_t* rows, int64_t nrows, int nthreads)
+{
+    int bad = or_check(b, n, h, 1, w, wu, dil, in_dt, out_dt);
+    if (bad) return bad;
+    const int64_t K = w + wu + 1, s = or_stride(dil);
+    if (!rows) nrows = b * n;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = or_row(rows, r) % n;
+        for (int64_t hh = 0; hh < h; ++hh) {
+            const int64_t row = (r * h + hh) * K;
+            double dot = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t j = i + (k - w) * s;
+                if (j < 0 || j >= n) continue;
+                dot += or_load(probs, row + k, in_dt) * or_load(dprobs, row + k, in_dt);
+            }
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t j = i + (k - w) * s;
+                double g = 0.0;
+                if (j >= 0 && j < n)
+                    g = scale * or_load(probs, row + k, in_dt) *
+                        (or_load(dprobs, row + k, in_dt) - dot);
+                or_store(dscores, row + k, out_dt, g);
             }
         }
     }

@@ -423,6 +423,100 @@ def test_softmax_invariants_fp16():
     assert torch.allclose(U, torch.where(inr[:, :, :1], 1.0 / cnt, 0.0), rtol=1e-15, atol=0)
 
 
+# ---------------------------------------------------- softmax backward pins
+# The gradient of the banded softmax with respect to its stored scores is not printed
+# on the pages; it is the chain rule through their softmax recipe.  Three independent
+# pins: torch autograd through a dense -inf-masked softmax (a library routine), central
+# finite differences through the forward oracle itself, and closed forms.
+
+def test_softmax_bwd_matches_torch_autograd_on_masked_dense_rows():
+    n, w, wu, d = 23, 3, 5, 6
+    for dil in (0, 2):
+        s = max(dil, 1)
+        g = datagen.rng(41 + dil)
+        S = datagen.normal(g, (1, n, 1, w + wu + 1), "f32").double()
+        dP = datagen.normal(g, (1, n, 1, w + wu + 1), "f32").double()
+        P = oracle.softmax(S, w, wu, dil, scale=0.3, out_dtype=torch.float64)
+        dS = oracle.softmax_bwd(P, dP, w, wu, dil, scale=0.3, out_dtype=torch.float64)
+        mask = torch.from_numpy(_selected(n, w, wu, s))
+        for i in range(n):
+            cols = torch.nonzero(mask[i]).flatten()            # keys of the in-range slots
+            ks = (cols - i) // s + w                           # their slots
+            x = torch.full((n,), float("-inf"), dtype=torch.float64)
+            sv = S[0, i, 0, ks].clone().requires_grad_(True)
+            x = x.index_put((cols,), 0.3 * sv)
+            pr = torch.softmax(x, -1)
+            (gs,) = torch.autograd.grad((pr[cols] * dP[0, i, 0, ks]).sum(), sv)
+            np.testing.assert_allclose(dS[0, i, 0, ks].numpy(), gs.numpy(), rtol=1e-12,
+                                       atol=1e-14)
+            out = torch.ones(w + wu + 1, dtype=torch.bool)
+            out[ks] = False
+            assert torch.all(dS[0, i, 0, out] == 0)
+
+
+def test_softmax_bwd_matches_central_differences_of_the_forward_oracle():
+    n, w, wu, dil, h = 17, 4, 2, 3, 2
+    K = w + wu + 1
+    g = datagen.rng(47)
+    S = datagen.normal(g, (1, n, h, K), "f32").double()
+    dP = datagen.normal(g, (1, n, h, K), "f32").double()
+    P = oracle.softmax(S, w, wu, dil, scale=0.5, out_dtype=torch.float64)
+    dS = oracle.softmax_bwd(P, dP, w, wu, dil, scale=0.5, out_dtype=torch.float64)
+    eps = 1e-6
+    ones = torch.ones(1, n, 1, 1)
+    inr = (oracle.qk(ones, ones, w, wu, dil, padding=0.0) == 1)[0, :, 0]
+    for i in range(0, n, 3):
+        for hh in range(h):
+            for k in range(K):
+                Sp, Sm = S.clone(), S.clone()
+                Sp[0, i, hh, k] += eps
+                Sm[0, i, hh, k] -= eps
+                Lp = (oracle.softmax(Sp, w, wu, dil, scale=0.5, out_dtype=torch.float64) * dP).sum()
+                Lm = (oracle.softmax(Sm, w, wu, dil, scale=0.5, out_dtype=torch.float64) * dP).sum()
+                fd = ((Lp - Lm) / (2 * eps)).item()
+                assert abs(dS[0, i, hh, k].item() - fd) <= 1e-7, (i, hh, k)
+                if not inr[i, k]:
+                    assert dS[0, i, hh, k].item() == 0.0 and fd == 0.0
+
+
+def test_softmax_bwd_closed_forms():
+    n, w, wu = 40, 6, 6
+    K = w + wu + 1
+    g = datagen.rng(53)
+    S = datagen.normal(g, (2, n, 3, K), "f32").double()
+    P = oracle.softmax(S, w, wu, 0, scale=0.25, out_dtype=torch.float64)
+    ones = torch.ones(1, n, 1, 1)
+    inr = (oracle.qk(ones, ones, w, wu, padding=0.0) == 1).expand_as(P)
+    # a gradient constant over the row's in-range slots (out-of-range slots hold
+    # anything, NaN included) leaves the scores' gradient exactly zero in double
+    dP = torch.where(inr, torch.full_like(P, 0.75), torch.full_like(P, float("nan")))
+    dS = oracle.softmax_bwd(P, dP, w, wu, 0, scale=0.25, out_dtype=torch.float64)
+    assert torch.all(dS.abs() <= 1e-16)
+    # each row of the gradient sums to zero (the softmax is shift invariant)
+    dP = datagen.normal(g, (2, n, 3, K), "f32").double()
+    dS = oracle.softmax_bwd(P, dP, w, wu, 0, scale=0.25, out_dtype=torch.float64)
+    assert torch.all(dS.sum(-1).abs() <= 1e-15)
+    # a one-hot probability row has a zero gradient, and a two-point row is
+    # scale * p (1 - p) (dP_a - dP_b) on its first point
+    P1 = torch.zeros_like(P)
+    P1[..., w] = 1.0
+    assert torch.all(oracle.softmax_bwd(P1, dP, w, wu, 0, scale=0.25,
+                                        out_dtype=torch.float64) == 0)
+    P2 = torch.zeros_like(P)
+    P2[..., w] = 0.375
+    P2[..., w + 1] = 0.625
+    dS2 = oracle.softmax_bwd(P2, dP, w, wu, 0, scale=0.25, out_dtype=torch.float64)
+    want = 0.25 * 0.375 * 0.625 * (dP[..., w] - dP[..., w + 1])
+    inner = inr[..., w + 1]                                   # rows where slot w+1 exists
+    assert torch.allclose(dS2[..., w][inner], want[inner], rtol=1e-15, atol=0)
+    # one rounding: a 16-bit output is the double value rounded once
+    Ph = oracle.convert(P, torch.float16)
+    dPh = oracle.convert(dP, torch.float16)
+    d64 = oracle.softmax_bwd(Ph, dPh, w, wu, 0, scale=0.25, out_dtype=torch.float64)
+    d16 = oracle.softmax_bwd(Ph, dPh, w, wu, 0, scale=0.25)
+    assert torch.equal(d16, oracle.convert(d64, torch.float16))
+
+
 # ------------------------------------------------------------ row sampling
 
 def test_row_list_equals_full_computation():

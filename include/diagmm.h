@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DIAGMM_ABI_VERSION 2
+#define DIAGMM_ABI_VERSION 3
 
 typedef enum {
     DIAGMM_F32 = 0,
@@ -122,6 +122,26 @@ diagmm_status_t diagmm_banded_softmax(const void* scores, void* probs, int64_t b
                                       int64_t dilation, float scale, diagmm_dtype_t in_dtype,
                                       diagmm_dtype_t out_dtype, void* stream);
 
+/*
+ * diagmm_banded_softmax_backward - gradient of diagmm_banded_softmax with respect to its
+ * stored scores, given its output probs and the gradient dprobs of a loss with respect
+ * to probs (the chain rule through the issue 2096 recipe; the pages print only the
+ * forward, and say the kernel's two backward functions of post 6 multiply a band
+ * gradient, the one this call produces):
+ *   dscores[bb,i,hh,k] = scale * probs[k] * (dprobs[k] - sum_m probs[m] * dprobs[m])
+ * over the row's in-range slots k, m; out-of-range slots of dscores become exactly +0,
+ * and out-of-range slots of probs and dprobs are never read into the sum (any value,
+ * NaN included, is ignored).  probs, dprobs and dscores are band tensors [b][n][h][K]
+ * of one dtype (f32, f16 or bf16; accumulation in f32, the result rounded to nearest
+ * even).  dscores may be the same pointer as probs or as dprobs (in place); any other
+ * overlap with them is DIAGMM_ERR_ALIAS.  Errors as for the other calls.
+ */
+diagmm_status_t diagmm_banded_softmax_backward(const void* probs, const void* dprobs,
+                                               void* dscores, int64_t b, int64_t n,
+                                               int64_t h, int64_t w, int64_t w_upper,
+                                               int64_t dilation, float scale,
+                                               diagmm_dtype_t dtype, void* stream);
+
 /* Static text for a status code. */
 const char* diagmm_status_string(diagmm_status_t status);
 
@@ -136,7 +156,8 @@ int diagmm_abi_version(void);
  * call with these arguments is cut into workgroups: which kernel runs, the tile shape
  * (rows per tile, slots per tile), how many tiles and workgroups, the LDS bytes per
  * workgroup, and how many residue classes the dilation splits the rows into.
- * mode: 0 = qk, 1 = pv, 2 = pvT, 3 = banded softmax.  Returns DIAGMM_ERR_SHAPE /
+ * mode: 0 = qk, 1 = pv, 2 = pvT, 3 = banded softmax, 4 = banded softmax backward
+ * (planned for 16-byte aligned tensors; out_dtype must equal in_dtype).  Returns DIAGMM_ERR_SHAPE /
  * DIAGMM_ERR_DTYPE for invalid arguments, as the compute calls would.
  */
 typedef struct {
@@ -163,7 +184,7 @@ diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d
  * diagmm_timing_begin(capacity) and diagmm_timing_end(), each of the next `capacity`
  * kernel launches by this library records a pair of HIP events at the kernel's own start
  * and end on the stream it is launched on (hipExtLaunchKernel), tagged with the entry
- * point (the diagmm_plan modes: 0 qk, 1 pv, 2 pvT, 3 banded softmax); further launches
+ * point (the diagmm_plan modes: 0 qk, 1 pv, 2 pvT, 3 banded softmax, 4 its backward); further launches
  * run untimed.  One session at a time, process-wide, on one device (the events are made
  * on the device current at diagmm_timing_begin; launches on another device are not to be
  * timed).  diagmm_timing_read waits for the recorded kernels and writes, for the first

@@ -23,7 +23,8 @@ import os
 
 import torch
 
-__all__ = ["diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax", "diagmm_plan",
+__all__ = ["diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax",
+           "diagmm_banded_softmax_backward", "diagmm_plan",
            "diagmm_timing_begin", "diagmm_timing_end", "diagmm_timing_read",
            "diagmm_abi_version", "library_path", "load", "DiagmmError"]
 
@@ -31,7 +32,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdiagmm.so")
 
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-MODES = {"qk": 0, "pv": 1, "pvT": 2, "softmax": 3}
+MODES = {"qk": 0, "pv": 1, "pvT": 2, "softmax": 3, "softmax_bwd": 4}
 
 
 class DiagmmError(RuntimeError):
@@ -73,6 +74,8 @@ def load() -> ctypes.CDLL:
         fn.restype = ci
     lib.diagmm_banded_softmax.argtypes = [vp, vp] + [i64] * 6 + [f32, ci, ci, vp]
     lib.diagmm_banded_softmax.restype = ci
+    lib.diagmm_banded_softmax_backward.argtypes = [vp, vp, vp] + [i64] * 6 + [f32, ci, vp]
+    lib.diagmm_banded_softmax_backward.restype = ci
     lib.diagmm_status_string.argtypes = [ci]
     lib.diagmm_status_string.restype = ctypes.c_char_p
     lib.diagmm_last_error.argtypes = []
@@ -205,6 +208,29 @@ def diagmm_banded_softmax(scores, w, w_upper=None, dilation=0, scale=1.0, out_dt
         res = _out(out, s.shape, out_dtype, s.device)
     st = lib.diagmm_banded_softmax(s.data_ptr(), res.data_ptr(), b, n, h, w, w_upper, dilation,
                                    float(scale), _DT[s.dtype], _DT[out_dtype], _stream(s.device))
+    if st:
+        _raise(lib, st)
+    return res
+
+
+def diagmm_banded_softmax_backward(probs, dprobs, w, w_upper=None, dilation=0, scale=1.0,
+                                   out=None):
+    """Gradient of ``diagmm_banded_softmax`` with respect to its scores, from its output
+    ``probs`` and the gradient ``dprobs`` with respect to it: per band row,
+    ``scale * probs * (dprobs - sum(probs * dprobs))`` over the in-range slots, exactly 0
+    elsewhere.  ``out`` may be ``probs`` or ``dprobs`` itself (in place)."""
+    lib = load()
+    w, w_upper, dilation = _window(w, w_upper, dilation)
+    p, dp = _dense(probs, "probs"), _dense(dprobs, "dprobs")
+    if p.shape != dp.shape or p.dtype != dp.dtype or p.device != dp.device:
+        raise ValueError("probs and dprobs must have the same shape, dtype and device")
+    b, n, h, K = p.shape
+    if K != w + w_upper + 1:
+        raise ValueError(f"probs last dim {K} != w + w_upper + 1 = {w + w_upper + 1}")
+    res = out if out is p or out is dp else _out(out, p.shape, p.dtype, p.device)
+    st = lib.diagmm_banded_softmax_backward(p.data_ptr(), dp.data_ptr(), res.data_ptr(), b, n,
+                                            h, w, w_upper, dilation, float(scale),
+                                            _DT[p.dtype], _stream(p.device))
     if st:
         _raise(lib, st)
     return res

@@ -1,0 +1,59 @@
+"""Banded (sliding-window) attention with its gradient, composed from the libdiagmm calls.
+
+TVM Discuss, "Developing a faster schedule for Longformer's kernel", post 6: the kernel
+serves one forward function and two backward functions told apart by ``transpose_t1``;
+with the banded softmax between them (csarofeen/pytorch issue 2096, first fusion repro)
+they give attention over a (dilated) sliding window and its gradients:
+
+    forward:   S = qk(Q, K)        P = softmax(scale * S)       O = pv(P, V)
+    backward:  dP = qk(dO, V)      dV = pvT(P, dO)
+               dS = softmax_backward(P, dP)                    (scale included)
+               dQ = pv(dS, K)      dK = pvT(dS, Q)
+
+Every step runs in the library's kernels; this module only orders the calls, keeps P
+for the backward pass and hands torch's autograd the results.  Tensors are contiguous
+``[b, n, h, d]`` on the GPU in one dtype (f32, f16 or bf16); gradients come back in it.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (diagmm_banded_softmax, diagmm_banded_softmax_backward, diagmm_pv, diagmm_pvT,
+               diagmm_qk)
+
+
+class BandedAttention(torch.autograd.Function):
+    """O = softmax_band(scale * Q K^T) V over the window (w, w_upper, dilation)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, w, w_upper, dilation, scale):
+        band = diagmm_qk(q, k, w, w_upper, dilation, 0.0)
+        probs = diagmm_banded_softmax(band, w, w_upper, dilation, scale, inplace=True)
+        out = diagmm_pv(probs, v, w, w_upper, dilation)
+        ctx.save_for_backward(q, k, v, probs)
+        ctx.window = (w, w_upper, dilation, scale)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, probs = ctx.saved_tensors
+        w, w_upper, dilation, scale = ctx.window
+        dout = dout.contiguous()
+        dprobs = diagmm_qk(dout, v, w, w_upper, dilation, 0.0)
+        dv = diagmm_pvT(probs, dout, w, w_upper, dilation)
+        dscores = diagmm_banded_softmax_backward(probs, dprobs, w, w_upper, dilation, scale,
+                                                 out=dprobs)
+        dq = diagmm_pv(dscores, k, w, w_upper, dilation)
+        dk = diagmm_pvT(dscores, q, w, w_upper, dilation)
+        return dq, dk, dv, None, None, None, None
+
+
+def banded_attention(q, k, v, w, w_upper=None, dilation=0, scale=None):
+    """Sliding-window attention of ``q`` over ``k``/``v`` ([b, n, h, d] each): slot kk of
+    row i attends key i + (kk - w) * max(dilation, 1) for kk in 0 .. w + w_upper; keys
+    outside the sequence are masked.  ``scale`` defaults to 1 / sqrt(d)."""
+    if w_upper is None:
+        w_upper = w
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    return BandedAttention.apply(q, k, v, int(w), int(w_upper), int(dilation), float(scale))

@@ -249,16 +249,58 @@ diagmm_status_t diagmm_banded_softmax(const void* scores, void* probs, int64_t b
                                 static_cast<hipStream_t>(stream)));
 }
 
+diagmm_status_t diagmm_banded_softmax_backward(const void* probs, const void* dprobs,
+                                               void* dscores, int64_t b, int64_t n,
+                                               int64_t h, int64_t w, int64_t w_upper,
+                                               int64_t dilation, float scale,
+                                               diagmm_dtype_t dtype, void* stream) {
+    const char* fn = "diagmm_banded_softmax_backward";
+    Problem p;
+    int64_t de, be;
+    diagmm_status_t st = check_common(fn, b, n, h, 1, w, w_upper, dilation, dtype, dtype, &p,
+                                      &de, &be);
+    if (st != DIAGMM_OK) return st;
+    if (p.rows() * p.h == 0) return ok();
+    if (!probs || !dprobs || !dscores) return fail(DIAGMM_ERR_NULL, "%s: null pointer", fn);
+    const int64_t bytes = be * static_cast<int64_t>(elem_size(dtype));
+    for (const void* in : {probs, dprobs})
+        if (dscores != in && overlaps(dscores, bytes, in, bytes))
+            return fail(DIAGMM_ERR_ALIAS, "%s: dscores overlaps probs or dprobs (only the "
+                        "exact same pointer, in place, is allowed)", fn);
+    if (!softmax_bwd_supported(p))
+        return fail(DIAGMM_ERR_UNSUPPORTED, "%s: more than 2^31 rows or 2^30 slots", fn);
+    const bool fast = !force_simple() && softmax_bwd_fast(p, dtype, probs, dprobs, dscores);
+    timing_set_op(kOpSoftmaxBwd);
+    return launched(fn, launch_softmax_bwd(probs, dprobs, dscores, p, scale, dtype, fast,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,
                             int64_t w_upper, int64_t dilation, diagmm_dtype_t in_dtype,
                             diagmm_dtype_t out_dtype, diagmm_plan_t* out) {
     if (!out) return fail(DIAGMM_ERR_NULL, "diagmm_plan: null plan pointer");
-    if (mode < 0 || mode > 3) return fail(DIAGMM_ERR_UNSUPPORTED, "diagmm_plan: mode %d", mode);
+    if (mode < 0 || mode > 4) return fail(DIAGMM_ERR_UNSUPPORTED, "diagmm_plan: mode %d", mode);
     Problem p;
     int64_t de, be;
-    diagmm_status_t st = check_common("diagmm_plan", b, n, h, mode == 3 ? 1 : d, w, w_upper,
+    diagmm_status_t st = check_common("diagmm_plan", b, n, h, mode >= 3 ? 1 : d, w, w_upper,
                                       dilation, in_dtype, out_dtype, &p, &de, &be);
     if (st != DIAGMM_OK) return st;
+    if (mode == 4) {
+        if (out_dtype != in_dtype)
+            return fail(DIAGMM_ERR_DTYPE, "diagmm_plan: the softmax backward has one dtype");
+        const void* al = reinterpret_cast<const void*>(uintptr_t(256));   // aligned tensors
+        const bool fast = !force_simple() && softmax_bwd_fast(p, in_dtype, al, al, al);
+        std::memset(out, 0, sizeof *out);
+        std::snprintf(out->kernel, sizeof out->kernel, "%s",
+                      softmax_bwd_kernel_name(p, in_dtype, fast));
+        out->rows_per_tile = 1;
+        out->slots_per_tile = p.K;
+        out->tiles = p.rows() * p.h;
+        out->workgroups = softmax_bwd_workgroups(p, in_dtype, fast);
+        out->threads = 256;
+        out->residues = 1;
+        return ok();
+    }
     Plan plan = mode == 0 ? plan_qk(p, in_dtype, out_dtype)
               : mode == 1 ? plan_pv(p, in_dtype, out_dtype)
               : mode == 2 ? plan_pvT(p, in_dtype, out_dtype)

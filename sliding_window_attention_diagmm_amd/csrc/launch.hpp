@@ -25,6 +25,20 @@ bool softmax_wave_supported(const Problem& p, int in_dt, int out_dt);
 hipError_t launch_softmax_wave(const void* scores, void* probs, const Problem& p, float scale,
                                int dt, hipStream_t stream);
 
+// DIAGMM_KERNEL=simple: the general kernels only (debugging and comparison switch).
+bool force_simple();
+
+// Banded softmax backward (one dtype for probs, dprobs and dscores): the group / wave
+// kernel when `fast` (softmax_bwd_fast), else one workgroup per row.
+bool softmax_bwd_supported(const Problem& p);
+int64_t softmax_bwd_workgroups(const Problem& p, int dt, bool fast);
+bool softmax_bwd_fast(const Problem& p, int dt, const void* probs, const void* dprobs,
+                      const void* dscores);
+const char* softmax_bwd_kernel_name(const Problem& p, int dt, bool fast);
+hipError_t launch_softmax_bwd(const void* probs, const void* dprobs, void* dscores,
+                              const Problem& p, float scale, int dt, bool fast,
+                              hipStream_t stream);
+
 // qk on MFMA (f16 / bf16 inputs, d in {32, 64, 128}, 16-byte aligned pointers).
 constexpr int kQkRows = 128;                 // rows per tile
 constexpr int64_t kQkLdsBytes = 160 * 1024;  // one workgroup per compute unit

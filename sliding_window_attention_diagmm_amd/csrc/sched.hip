@@ -7,14 +7,14 @@
 
 namespace diagmm {
 
-namespace {
-
 // DIAGMM_KERNEL=simple forces the element-per-thread kernels (a debugging and
 // comparison switch; the default picks the tiled kernels where they apply).
 bool force_simple() {
     const char* e = std::getenv("DIAGMM_KERNEL");
     return e && std::strcmp(e, "simple") == 0;
 }
+
+namespace {
 
 Plan simple_plan(const Problem& p, int64_t cols, const char* name) {
     Plan pl;

@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for want in ("diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax",
-                 "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
+                 "diagmm_banded_softmax_backward", "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
                  "diagmm_plan"):
         assert want in names
 
@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dm.diagmm_abi_version() == 2
+    assert dm.diagmm_abi_version() == 3
     seen = set()
     for st in range(7):
         s = lib.diagmm_status_string(st).decode()
@@ -86,6 +86,15 @@ def test_validation_errors_are_reported_without_launching(lib):
     assert sm(FAKE, FAKE + 2, 1, 8, 1, 2, 2, 0, 1.0, 1, 1, None) == ERR_ALIAS
     assert sm(FAKE, FAKE, 1, 8, 1, 2, 2, 0, 1.0, 1, 0, None) == ERR_ALIAS  # in place needs equal dtypes
     assert sm(FAKE, 0, 1, 8, 1, 2, 2, 0, 1.0, 1, 1, None) == ERR_NULL
+    bw = lib.diagmm_banded_softmax_backward
+    P_, D_, O_ = FAKE, FAKE + (1 << 30), FAKE + (1 << 34)
+    assert bw(P_, D_, 0, 1, 8, 1, 2, 2, 0, 1.0, 1, None) == ERR_NULL
+    assert bw(0, D_, O_, 1, 8, 1, 2, 2, 0, 1.0, 1, None) == ERR_NULL
+    assert bw(P_, D_, O_, 1, 8, 1, -2, 2, 0, 1.0, 1, None) == ERR_SHAPE
+    assert bw(P_, D_, O_, 1, 8, 1, 2, 2, 0, 1.0, 5, None) == ERR_DTYPE
+    assert bw(P_, D_, P_ + 2, 1, 8, 1, 2, 2, 0, 1.0, 1, None) == ERR_ALIAS   # partial overlap
+    assert bw(P_, D_, D_ + 78, 1, 8, 1, 2, 2, 0, 1.0, 1, None) == ERR_ALIAS  # last element
+    assert "diagmm_banded_softmax_backward" in lib.diagmm_last_error().decode()
 
 
 def test_empty_problems_are_noops(lib):
@@ -93,6 +102,7 @@ def test_empty_problems_are_noops(lib):
     assert call_qk(lib, q=0, k=0, band=0, b=0) == OK
     assert lib.diagmm_pv(0, 0, 0, 1, 8, 0, 4, 2, 2, 0, 0.0, 2, 0, None) == OK
     assert lib.diagmm_banded_softmax(0, 0, 0, 8, 3, 2, 2, 0, 1.0, 1, 1, None) == OK
+    assert lib.diagmm_banded_softmax_backward(0, 0, 0, 0, 8, 3, 2, 2, 0, 1.0, 1, None) == OK
     assert lib.diagmm_last_error().decode() == ""
 
 
@@ -106,14 +116,14 @@ def test_python_binding_rejects_bad_tensors():
         dm.diagmm_pv(cpu, cpu, -1)
 
 
-@pytest.mark.parametrize("mode", ["qk", "pv", "pvT", "softmax"])
+@pytest.mark.parametrize("mode", ["qk", "pv", "pvT", "softmax", "softmax_bwd"])
 @pytest.mark.parametrize("shape", [(1, 4096, 12, 64, 256, 256, 0), (1, 4096, 12, 64, 256, 256, 3),
                                    (12, 4096, 12, 64, 256, 0, 0), (1, 32768, 12, 64, 4096, 4096, 0),
                                    (1, 512, 1, 64, 32, 32, 0), (2, 37, 3, 24, 5, 0, 2)])
 def test_plans_are_consistent(lib, mode, shape):
     b, n, h, d, w, wu, dil = shape
     dt = torch.bfloat16 if wu == 0 else torch.float16
-    odt = torch.float32 if wu == 0 else dt
+    odt = torch.float32 if wu == 0 and mode != "softmax_bwd" else dt
     p = dm.diagmm_plan(mode, b, n, h, d, w, wu, dil, dt, odt)
     assert p["kernel"]
     assert p["threads"] in (64, 128, 256, 512, 1024)
@@ -129,3 +139,17 @@ def test_plan_rejects_what_the_calls_reject(lib):
     with pytest.raises(dm.DiagmmError) as e:
         dm.diagmm_plan("qk", 1, -4, 1, 64, 2)
     assert e.value.status == ERR_SHAPE
+
+
+def test_softmax_bwd_plan_picks_lanes_by_row_length(lib):
+    fast = dm.diagmm_plan("softmax_bwd", 1, 4096, 12, 1, 256, 256, 0, torch.float16)
+    assert fast["kernel"] == "softmax_bwd_group"
+    # 12 * 4096 rows, 8 lanes per row (513 slots: up to 66 pieces of 8), 4 waves per block
+    assert fast["workgroups"] == 12 * 4096 // (4 * 8)
+    long = dm.diagmm_plan("softmax_bwd", 1, 32768, 12, 1, 4096, 4096, 0, torch.float16)
+    assert long["kernel"] == "softmax_bwd_wave"
+    huge = dm.diagmm_plan("softmax_bwd", 1, 64, 1, 1, 9000, 9000, 0, torch.float16)
+    assert huge["kernel"] == "softmax_bwd_rows"
+    with pytest.raises(dm.DiagmmError) as e:
+        dm.diagmm_plan("softmax_bwd", 1, 64, 1, 1, 8, 8, 0, torch.float16, torch.float32)
+    assert e.value.status == ERR_DTYPE

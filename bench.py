@@ -61,6 +61,8 @@ def op_costs(dil):
         "softmax": {"bytes": cnt * E + band, "flops": 0},
         "pv": {"bytes": cnt * E + 2 * dense, "flops": 2 * D * cnt},
         "pvT": {"bytes": cnt * E + 2 * dense, "flops": 2 * D * cnt},
+        # gradient path: P and dP read on their in-range slots, the whole band written
+        "softmax_bwd": {"bytes": 2 * cnt * E + band, "flops": 0},
     }
 
 
@@ -182,8 +184,9 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-probe", action="store_true",
-                    help="short run for hardware counters: 3 passes of each kernel at the bench "
-                         "workload plus a reference copy of 64 MiB (calibrates FETCH_SIZE / "
+                    help="short run for hardware counters: 3 passes of each kernel (and the softmax "
+                         "backward) at the bench workload plus a reference copy of 64 MiB "
+                         "(calibrates FETCH_SIZE / "
                          "WRITE_SIZE); prints the reference size and exits")
     args = ap.parse_args()
 
@@ -218,6 +221,8 @@ def main():
         ref_bytes = 64 << 20
         # The reference copy reads a buffer no kernel has touched (so none of it sits in
         # L2 or the Infinity Cache) after a 512 MiB fill has flushed both caches.
+        dprobs = dm.diagmm_qk(sets[0]["do"], sets[0]["v"], W, WU, 0, 0.0)
+        dscores = torch.empty_like(dprobs)
         flush = torch.empty(256 << 20, dtype=torch.float16, device=dev)
         src = torch.empty(ref_bytes // 2, dtype=torch.float16, device=dev)
         dst = torch.empty_like(src)
@@ -233,6 +238,8 @@ def main():
                 dm.diagmm_banded_softmax(t[f"S{dil}"], W, WU, dil, SCALE, inplace=True)
                 dm.diagmm_pv(t[f"S{dil}"], t["v"], W, WU, dil, out=t[f"O{dil}"])
                 dm.diagmm_pvT(t[f"S{dil}"], t["do"], W, WU, dil, out=t[f"X{dil}"])
+                dm.diagmm_banded_softmax_backward(t[f"S{dil}"], dprobs, W, WU, dil, SCALE,
+                                                  out=dscores)
         torch.cuda.synchronize()
         print(json.dumps({"pmc_probe": True, "reference_copy_bytes": ref_bytes,
                           "qk_algorithmic_bytes": op_costs(0)["qk"]["bytes"],
@@ -294,6 +301,39 @@ def main():
             "kernel": dm.diagmm_plan(op, B, N, H, D, W, WU, dil, torch.float16)["kernel"],
         }
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # The banded softmax backward, the one kernel the gradient path adds (it sits between
+    # dP = qk(dO, V) and the two transposed products), timed on its own over the same
+    # rotating sets: P from the step above, dP = qk(dO, V) computed once per set.
+    extra = {}
+    for t in sets:
+        t["dP"] = dm.diagmm_qk(t["do"], t["v"], W, WU, 0, 0.0)
+        t["dS"] = torch.empty_like(t["dP"])
+    for dil in DILATIONS:
+        def bwd(t):
+            dm.diagmm_banded_softmax_backward(t[f"S{dil}"], t["dP"], W, WU, dil, SCALE,
+                                              out=t["dS"])
+        for i in range(args.warmup):
+            bwd(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        dm.diagmm_timing_begin(args.steps)
+        for i in range(args.steps):
+            bwd(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        dm.diagmm_timing_end()
+        recs = [ms for name, ms in dm.diagmm_timing_read() if name == "softmax_bwd"]
+        assert len(recs) == args.steps, (len(recs), args.steps)
+        ms = sum(recs) / len(recs)
+        c = op_costs(dil)["softmax_bwd"]
+        extra[f"softmax_bwd_dil{dil}"] = {
+            "us": round(ms * 1e3, 2),
+            "GB/s": round(c["bytes"] / (ms * 1e-3) / 1e9, 1),
+            "bytes": c["bytes"],
+            "kernel": dm.diagmm_plan("softmax_bwd", B, N, H, 1, W, WU, dil,
+                                     torch.float16)["kernel"],
+        }
+    for t in sets:
+        del t["dP"], t["dS"]
     ceiling = practical_ceiling(torch, dev, stream)
     qk_us = per_op["qk_dil0"]["us"]
     qk_bytes = op_costs(0)["qk"]["bytes"]
@@ -321,6 +361,7 @@ def main():
         "tflops": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "per_op": per_op,
+        "extra_ops": extra,
         "roofline": {"kernel": per_op["qk_dil0"]["kernel"], "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

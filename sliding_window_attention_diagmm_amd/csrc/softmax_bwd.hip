@@ -230,11 +230,12 @@ hipError_t launch_g(const void* probs, const void* dprobs, void* dscores, const 
 }
 
 // Lanes per row for a row touching `pieces` 16-byte pieces: the fewest lanes holding at
-// most 9 pieces each, or a whole wavefront with up to 17 each; 0 = the row kernel.
+// most 3 pieces each (a 513-slot f16 row on 32 lanes: one load instruction then covers two
+// rows of 512 contiguous bytes), or a whole wavefront with up to 17 each; 0 = the row kernel.
 int group_lanes(int64_t pieces, int* per_lane) {
     for (int l = 1; l <= 32; l *= 2)
-        if (pieces <= 9 * l) {
-            *per_lane = 9;
+        if (pieces <= 3 * l) {
+            *per_lane = 3;
             return l;
         }
     for (int pl : {2, 4, 8, 17})
@@ -255,12 +256,12 @@ hipError_t launch_t(const void* probs, const void* dprobs, void* dscores, const 
     int per = 0;
     const int l = fast ? group_lanes(pieces, &per) : 0;
     switch (l) {
-    case 1: return launch_g<T, 1, 9>(probs, dprobs, dscores, p, scale, rd, stream);
-    case 2: return launch_g<T, 2, 9>(probs, dprobs, dscores, p, scale, rd, stream);
-    case 4: return launch_g<T, 4, 9>(probs, dprobs, dscores, p, scale, rd, stream);
-    case 8: return launch_g<T, 8, 9>(probs, dprobs, dscores, p, scale, rd, stream);
-    case 16: return launch_g<T, 16, 9>(probs, dprobs, dscores, p, scale, rd, stream);
-    case 32: return launch_g<T, 32, 9>(probs, dprobs, dscores, p, scale, rd, stream);
+    case 1: return launch_g<T, 1, 3>(probs, dprobs, dscores, p, scale, rd, stream);
+    case 2: return launch_g<T, 2, 3>(probs, dprobs, dscores, p, scale, rd, stream);
+    case 4: return launch_g<T, 4, 3>(probs, dprobs, dscores, p, scale, rd, stream);
+    case 8: return launch_g<T, 8, 3>(probs, dprobs, dscores, p, scale, rd, stream);
+    case 16: return launch_g<T, 16, 3>(probs, dprobs, dscores, p, scale, rd, stream);
+    case 32: return launch_g<T, 32, 3>(probs, dprobs, dscores, p, scale, rd, stream);
     case 64:
         if (per == 2) return launch_g<T, 64, 2>(probs, dprobs, dscores, p, scale, rd, stream);
         if (per == 4) return launch_g<T, 64, 4>(probs, dprobs, dscores, p, scale, rd, stream);

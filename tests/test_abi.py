@@ -144,8 +144,8 @@ def test_plan_rejects_what_the_calls_reject(lib):
 def test_softmax_bwd_plan_picks_lanes_by_row_length(lib):
     fast = dm.diagmm_plan("softmax_bwd", 1, 4096, 12, 1, 256, 256, 0, torch.float16)
     assert fast["kernel"] == "softmax_bwd_group"
-    # 12 * 4096 rows, 8 lanes per row (513 slots: up to 66 pieces of 8), 4 waves per block
-    assert fast["workgroups"] == 12 * 4096 // (4 * 8)
+    # 12 * 4096 rows, 32 lanes per row (513 slots: up to 66 pieces of 8), 4 waves per block
+    assert fast["workgroups"] == 12 * 4096 // (4 * 2)
     long = dm.diagmm_plan("softmax_bwd", 1, 32768, 12, 1, 4096, 4096, 0, torch.float16)
     assert long["kernel"] == "softmax_bwd_wave"
     huge = dm.diagmm_plan("softmax_bwd", 1, 64, 1, 1, 9000, 9000, 0, torch.float16)

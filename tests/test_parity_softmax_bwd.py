@@ -3,7 +3,7 @@
 dS = scale * P * (dP - sum(P * dP)) per band row over the in-range slots, exactly +0 in
 the others (the chain rule through the banded softmax; the oracle's pins are in
 test_oracle.py).  Cases cover every lane layout of the kernel (1 .. 32 lanes per row,
-whole wavefronts with 8 and 17 pieces per lane), the row kernel (forced, and for
+whole wavefronts with 2 .. 17 pieces per lane), the row kernel (forced, and for
 misaligned tensors), the three dtypes, dilation, ragged and tiny sequences, in-place
 use and poisoned out-of-range slots; at the benchmark shape and the long-document shape
 the probabilities come from the GPU chain itself (qk -> softmax) and the gradient from
@@ -25,24 +25,27 @@ pytestmark = pytest.mark.gpu
 DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 # (b, n, h, w, w_upper, dilation, dtype): the comment names the kernel layout it reaches
+# (L lanes per row for rows of up to 3 L pieces of 16 bytes, then whole wavefronts)
 CASES = [
-    (1, 512, 1, 32, 32, 0, "f32"),      # 65 slots: 2 lanes per row (f32, 4 per piece)
+    (1, 512, 1, 32, 32, 0, "f32"),      # 65 slots, f32 (4 per piece): 8 lanes
     (1, 1, 1, 3, 3, 0, "f16"),          # one position
     (2, 7, 3, 3, 0, 0, "bf16"),         # 4 slots, causal: 1 lane per row
-    (1, 100, 2, 31, 31, 0, "f16"),      # 63 slots
-    (1, 1000, 2, 256, 256, 0, "f16"),   # 513 slots: 8 lanes per row
+    (1, 100, 2, 31, 31, 0, "f16"),      # 63 slots: 4 lanes
+    (1, 1000, 2, 256, 256, 0, "f16"),   # 513 slots: 32 lanes per row
     (1, 1000, 2, 256, 256, 3, "bf16"),
-    (1, 300, 2, 350, 350, 0, "f16"),    # window wider than the sequence: 16 lanes
+    (1, 300, 2, 350, 350, 0, "f16"),    # window wider than the sequence: 32 lanes
     (1, 333, 1, 20, 20, 9, "f16"),
     (1, 64, 1, 0, 0, 0, "f16"),         # K = 1
     (1, 70, 2, 4, 4, 2, "f32"),
     (2, 96, 2, 40, 40, 3, "f32"),
-    (1, 40, 1, 300, 0, 0, "bf16"),      # 301 slots, causal
-    (1, 30, 1, 700, 700, 0, "f16"),     # 1401 slots: 32 lanes per row
+    (1, 40, 1, 300, 0, 0, "bf16"),      # 301 slots, causal: 16 lanes
+    (1, 30, 1, 700, 700, 0, "f16"),     # 1401 slots: wave, 4 pieces per lane
     (1, 30, 1, 1200, 1200, 0, "f16"),   # 2401 slots: a wavefront, 8 pieces per lane
     (1, 12, 1, 4096, 4096, 0, "f16"),   # 8193 slots: a wavefront, 17 pieces per lane
-    (1, 20, 1, 150, 150, 0, "f32"),     # 301 f32 slots: 16 lanes
-    (1, 20, 1, 1000, 1000, 0, "f32"),   # 2001 f32 slots: a wavefront
+    (1, 20, 1, 150, 150, 0, "f32"),     # 301 f32 slots: 32 lanes
+    (1, 20, 1, 1000, 1000, 0, "f32"),   # 2001 f32 slots: a wavefront, 8 pieces per lane
+    (1, 50, 2, 16, 15, 0, "f16"),       # 32 slots: 2 lanes per row
+    (1, 30, 1, 450, 450, 0, "f16"),     # 901 slots: a wavefront, 2 pieces per lane
 ]
 
 

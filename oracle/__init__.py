@@ -18,6 +18,8 @@ posts 1, 3, 5 and 6): with stride ``s = max(dilation, 1)`` and ``K = w + w_upper
   (backward function with transpose_t1 = 1);
 * ``softmax``: per band row, scale, mask out-of-range slots to -inf, max, exp, sum,
   divide (attention softmax of the first fusion repro on csarofeen/pytorch issue 2096);
+* ``softmax_masked``: the same softmax with the page's additive attention mask, a per-key
+  mask m adding (1 - m) * mask_value (-10000 there) before the max;
 * ``softmax_bwd``: the derivative of that softmax with respect to the stored scores,
   scale * P * (dP - sum(P * dP)) per row over in-range slots, 0 elsewhere (not printed
   on the pages; the chain rule through the recipe above).
@@ -66,6 +68,8 @@ def _load():
             lib.oracle_pvT.argtypes = [vp, vp, vp] + [i64] * 7 + [ci, ci, vp, i64, ci]
             lib.oracle_softmax.argtypes = [vp, vp] + [i64] * 6 + [cd, ci, ci, vp, i64, ci]
             lib.oracle_softmax_bwd.argtypes = [vp, vp, vp] + [i64] * 6 + [cd, ci, ci, vp, i64, ci]
+            lib.oracle_softmax_masked.argtypes = [vp, vp, vp] + [i64] * 6 + [cd, cd, ci, ci, vp,
+                                                                                 i64, ci]
             for f in (lib.oracle_qk, lib.oracle_pv, lib.oracle_pvT, lib.oracle_softmax):
                 f.restype = ci
             lib.oracle_convert.argtypes = [vp, vp, i64, ci]
@@ -177,6 +181,35 @@ def softmax(scores, w, w_upper, dilation=0, scale=1.0, out_dtype=None, n=None, r
                             threads or default_threads())
     if st:
         raise ValueError(f"oracle.softmax: bad arguments ({st})")
+    return out
+
+
+def softmax_masked(scores, key_mask, w, w_upper, dilation=0, scale=1.0, mask_value=-10000.0,
+                   out_dtype=None, n=None, rows=None, threads=None):
+    """Banded softmax with a per-key attention mask ``key_mask`` (float32 [b, n]): the
+    scaled score of a slot whose key is j gains (1 - key_mask[b, j]) * mask_value."""
+    lib = _load()
+    s = _check(scores, "scores")
+    km = key_mask.to(torch.float32).contiguous()
+    out_dtype = out_dtype or s.dtype
+    rt, rp, nr = _rows(rows)
+    if rt is None:
+        b, n, h, K = s.shape
+    else:
+        if n is None:
+            raise ValueError("oracle.softmax_masked: n is required with a row list")
+        _, h, K = s.shape
+        b = km.shape[0]
+    if K != w + w_upper + 1:
+        raise ValueError("oracle.softmax_masked: band width mismatch")
+    if tuple(km.shape) != (b, n):
+        raise ValueError("oracle.softmax_masked: key_mask must be [b, n]")
+    out = torch.empty(s.shape, dtype=out_dtype)
+    st = lib.oracle_softmax_masked(_ptr(s), _ptr(out), _ptr(km), b, n, h, w, w_upper, dilation,
+                                   float(scale), float(mask_value), _CODE[s.dtype],
+                                   _CODE[out_dtype], rp, nr, threads or default_threads())
+    if st:
+        raise ValueError(f"oracle.softmax_masked: bad arguments ({st})")
     return out
 
 

@@ -350,3 +350,55 @@ int oracle_softmax_bwd(const void* probs, const void* dprobs, void* dscores, int
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------ masked softmax
+ * The attention softmax of the first fusion repro on the csarofeen/pytorch issue 2096
+ * page with its attention mask: a per-key mask m[bb, j] (1 keeps key j, 0 masks it;
+ * any value is used linearly) adds (1 - m) * mask_value (-10000 there) to the scaled
+ * score before the row max:
+ *     x_k = scale * S[k] + (1 - m[bb, j]) * mask_value,   j = i + (k - w) * s,
+ * for in-range slots; out-of-range slots are -inf as in oracle_softmax, so their
+ * probability is exactly 0.  key_mask is float32 [b][n] (the full batch, also when a
+ * row list is given: it is reached through the key index). */
+int oracle_softmax_masked(const void* scores, void* probs, const float* key_mask, int64_t b,
+                          int64_t n, int64_t h, int64_t w, int64_t wu, int64_t dil,
+                          double scale, double mask_value, int in_dt, int out_dt,
+                          const int64_t* rows, int64_t nrows, int nthreads)
+{
+    int bad = or_check(b, n, h, 1, w, wu, dil, in_dt, out_dt);
+    if (bad) return bad;
+    if (!key_mask) return 1;
+    const int64_t K = w + wu + 1, s = or_stride(dil);
+    if (!rows) nrows = b * n;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t bn = or_row(rows, r), i = bn % n, bb = bn / n;
+        for (int64_t hh = 0; hh < h; ++hh) {
+            const int64_t row = (r * h + hh) * K;
+            double m = -INFINITY;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t j = i + (k - w) * s;
+                if (j < 0 || j >= n) continue;
+                const double x = scale * or_load(scores, row + k, in_dt) +
+                                 (1.0 - (double)key_mask[bb * n + j]) * mask_value;
+                if (x > m) m = x;
+            }
+            double sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t j = i + (k - w) * s;
+                if (j < 0 || j >= n) continue;
+                sum += exp(scale * or_load(scores, row + k, in_dt) +
+                           (1.0 - (double)key_mask[bb * n + j]) * mask_value - m);
+            }
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t j = i + (k - w) * s;
+                double p = 0.0;
+                if (j >= 0 && j < n)
+                    p = exp(scale * or_load(scores, row + k, in_dt) +
+                            (1.0 - (double)key_mask[bb * n + j]) * mask_value - m) / sum;
+                or_store(probs, row + k, out_dt, p);
+            }
+        }
+    }
+    return 0;
+}

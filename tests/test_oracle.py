@@ -423,6 +423,72 @@ def test_softmax_invariants_fp16():
     assert torch.allclose(U, torch.where(inr[:, :, :1], 1.0 / cnt, 0.0), rtol=1e-15, atol=0)
 
 
+# ------------------------------------------------------ masked softmax pins
+# The page's attention mask: a per-key mask m adds (1 - m) * (-10000) to the scaled score
+# (csarofeen/pytorch issue 2096, first fusion repro).
+
+def test_masked_softmax_with_all_ones_is_the_plain_softmax():
+    n, w, wu = 50, 7, 3
+    g = datagen.rng(61)
+    S = datagen.normal(g, (2, n, 2, w + wu + 1), "f16", 3.0)
+    ones = torch.ones(2, n)
+    for dil in (0, 2):
+        a = oracle.softmax_masked(S, ones, w, wu, dil, scale=0.125, out_dtype=torch.float64)
+        b = oracle.softmax(S, w, wu, dil, scale=0.125, out_dtype=torch.float64)
+        assert torch.equal(a, b)
+
+
+def test_masked_softmax_matches_torch_on_dense_rows():
+    n, w, wu, d = 31, 5, 4, 8
+    for dil in (0, 3):
+        s = max(dil, 1)
+        g = datagen.rng(67 + dil)
+        Q = datagen.normal(g, (2, n, 1, d), "f32").double()
+        Kt = datagen.normal(g, (2, n, 1, d), "f32").double()
+        m = torch.from_numpy((g.random((2, n)) > 0.3).astype(np.float32))
+        m[:, ::7] = 0.25                                   # the term is linear in m
+        band = oracle.qk(Q, Kt, w, wu, dil, padding=0.0)
+        P = oracle.softmax_masked(band, m, w, wu, dil, scale=0.3, mask_value=-7.0,
+                                  out_dtype=torch.float64)
+        sel = torch.from_numpy(_selected(n, w, wu, s))
+        for bb in range(2):
+            D = (Q[bb, :, 0] @ Kt[bb, :, 0].T) * 0.3 + (1 - m[bb].double())[None, :] * -7.0
+            ref = torch.softmax(D.masked_fill(~sel, float("-inf")), -1)
+            for i in range(n):
+                cols = torch.nonzero(sel[i]).flatten()
+                ks = (cols - i) // s + w
+                np.testing.assert_allclose(P[bb, i, 0, ks].numpy(), ref[i, cols].numpy(),
+                                           rtol=1e-12, atol=1e-15)
+                out = torch.ones(w + wu + 1, dtype=torch.bool)
+                out[ks] = False
+                assert torch.all(P[bb, i, 0, out] == 0)
+
+
+def test_masked_softmax_closed_forms():
+    n, w, wu = 40, 6, 6
+    g = datagen.rng(71)
+    S = datagen.normal(g, (1, n, 2, w + wu + 1), "f32").double()
+    plain = oracle.softmax(S, w, wu, 0, scale=0.5, out_dtype=torch.float64)
+    # every key masked: the same shift for every slot, so the plain softmax again
+    zeros = torch.zeros(1, n)
+    allm = oracle.softmax_masked(S, zeros, w, wu, 0, scale=0.5, out_dtype=torch.float64)
+    assert torch.allclose(allm, plain, rtol=1e-9, atol=0)
+    # one masked key among kept ones: its probability underflows to exactly 0, and the
+    # row is the plain softmax of the other slots
+    m = torch.ones(1, n)
+    m[0, 20] = 0
+    P = oracle.softmax_masked(S, m, w, wu, 0, scale=0.5, out_dtype=torch.float64)
+    for i in range(14, 27):
+        k = 20 - i + w                                     # slot of key 20 in row i
+        assert P[0, i, :, k].eq(0).all()
+        keep = plain[0, i].clone()
+        keep[:, k] = 0
+        assert torch.allclose(P[0, i], keep / keep.sum(-1, keepdim=True), rtol=1e-12, atol=0)
+    # one rounding of a 16-bit output
+    P16 = oracle.softmax_masked(S, m, w, wu, 0, scale=0.5, out_dtype=torch.float16)
+    assert torch.equal(P16, oracle.convert(P, torch.float16))
+
+
 # ---------------------------------------------------- softmax backward pins
 # The gradient of the banded softmax with respect to its stored scores is not printed
 # on the pages; it is the chain rule through their softmax recipe.  Three independent

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DIAGMM_ABI_VERSION 3
+#define DIAGMM_ABI_VERSION 4
 
 typedef enum {
     DIAGMM_F32 = 0,
@@ -123,6 +123,24 @@ diagmm_status_t diagmm_banded_softmax(const void* scores, void* probs, int64_t b
                                       diagmm_dtype_t out_dtype, void* stream);
 
 /*
+ * diagmm_banded_softmax_masked - diagmm_banded_softmax with the attention mask of the
+ * issue 2096 repro: key_mask is float32 [b][n] on the device (1 keeps key j, 0 masks it;
+ * any value is used linearly), and
+ *   x_k = scale * scores[bb,i,hh,k] + (1 - key_mask[bb, i + (k - w) * s]) * mask_value
+ * for in-range slots (mask_value -10000 on the page), -inf for the others; then max,
+ * exp, sum and divide as diagmm_banded_softmax.  Its gradient with respect to scores is
+ * diagmm_banded_softmax_backward's (the mask term does not depend on the scores).
+ * probs may be scores itself with equal dtypes; probs overlapping key_mask, or scores
+ * other than exactly, is DIAGMM_ERR_ALIAS; key_mask NULL is DIAGMM_ERR_NULL.
+ */
+diagmm_status_t diagmm_banded_softmax_masked(const void* scores, void* probs,
+                                             const float* key_mask, int64_t b, int64_t n,
+                                             int64_t h, int64_t w, int64_t w_upper,
+                                             int64_t dilation, float scale, float mask_value,
+                                             diagmm_dtype_t in_dtype, diagmm_dtype_t out_dtype,
+                                             void* stream);
+
+/*
  * diagmm_banded_softmax_backward - gradient of diagmm_banded_softmax with respect to its
  * stored scores, given its output probs and the gradient dprobs of a loss with respect
  * to probs (the chain rule through the issue 2096 recipe; the pages print only the
@@ -184,7 +202,8 @@ diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d
  * diagmm_timing_begin(capacity) and diagmm_timing_end(), each of the next `capacity`
  * kernel launches by this library records a pair of HIP events at the kernel's own start
  * and end on the stream it is launched on (hipExtLaunchKernel), tagged with the entry
- * point (the diagmm_plan modes: 0 qk, 1 pv, 2 pvT, 3 banded softmax, 4 its backward); further launches
+ * point (the diagmm_plan modes: 0 qk, 1 pv, 2 pvT, 3 banded softmax, 4 its backward;
+ * 5 the masked softmax); further launches
  * run untimed.  One session at a time, process-wide, on one device (the events are made
  * on the device current at diagmm_timing_begin; launches on another device are not to be
  * timed).  diagmm_timing_read waits for the recorded kernels and writes, for the first

@@ -32,7 +32,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdiagmm.so")
 
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-MODES = {"qk": 0, "pv": 1, "pvT": 2, "softmax": 3, "softmax_bwd": 4}
+MODES = {"qk": 0, "pv": 1, "pvT": 2, "softmax": 3, "softmax_bwd": 4, "softmax_masked": 5}
 
 
 class DiagmmError(RuntimeError):
@@ -76,6 +76,8 @@ def load() -> ctypes.CDLL:
     lib.diagmm_banded_softmax.restype = ci
     lib.diagmm_banded_softmax_backward.argtypes = [vp, vp, vp] + [i64] * 6 + [f32, ci, vp]
     lib.diagmm_banded_softmax_backward.restype = ci
+    lib.diagmm_banded_softmax_masked.argtypes = [vp, vp, vp] + [i64] * 6 + [f32, f32, ci, ci, vp]
+    lib.diagmm_banded_softmax_masked.restype = ci
     lib.diagmm_status_string.argtypes = [ci]
     lib.diagmm_status_string.restype = ctypes.c_char_p
     lib.diagmm_last_error.argtypes = []
@@ -190,9 +192,11 @@ def diagmm_pvT(band, x, w, w_upper=None, dilation=0, out_dtype=None, out=None):
 
 
 def diagmm_banded_softmax(scores, w, w_upper=None, dilation=0, scale=1.0, out_dtype=None,
-                          out=None, inplace=False):
+                          out=None, inplace=False, key_mask=None, mask_value=-10000.0):
     """Softmax of scale * scores over each band row's in-range slots; out-of-range slots
-    get exactly 0.  ``inplace=True`` overwrites ``scores`` (same dtype only)."""
+    get exactly 0.  ``inplace=True`` overwrites ``scores`` (same dtype only).  With
+    ``key_mask`` (float32 [b, n] on the GPU: 1 keeps a key, 0 masks it) each slot's scaled
+    score gains (1 - key_mask[b, key]) * mask_value first."""
     lib = load()
     w, w_upper, dilation = _window(w, w_upper, dilation)
     s = _dense(scores, "scores")
@@ -206,8 +210,20 @@ def diagmm_banded_softmax(scores, w, w_upper=None, dilation=0, scale=1.0, out_dt
         res = s
     else:
         res = _out(out, s.shape, out_dtype, s.device)
-    st = lib.diagmm_banded_softmax(s.data_ptr(), res.data_ptr(), b, n, h, w, w_upper, dilation,
-                                   float(scale), _DT[s.dtype], _DT[out_dtype], _stream(s.device))
+    if key_mask is not None:
+        if (not isinstance(key_mask, torch.Tensor) or key_mask.dtype != torch.float32 or
+                tuple(key_mask.shape) != (b, n) or key_mask.device != s.device or
+                not key_mask.is_contiguous()):
+            raise ValueError(f"key_mask must be a contiguous float32 [{b}, {n}] tensor on "
+                             f"{s.device}")
+        st = lib.diagmm_banded_softmax_masked(s.data_ptr(), res.data_ptr(), key_mask.data_ptr(),
+                                              b, n, h, w, w_upper, dilation, float(scale),
+                                              float(mask_value), _DT[s.dtype], _DT[out_dtype],
+                                              _stream(s.device))
+    else:
+        st = lib.diagmm_banded_softmax(s.data_ptr(), res.data_ptr(), b, n, h, w, w_upper,
+                                       dilation, float(scale), _DT[s.dtype], _DT[out_dtype],
+                                       _stream(s.device))
     if st:
         _raise(lib, st)
     return res

@@ -5,7 +5,7 @@ serves one forward function and two backward functions told apart by ``transpose
 with the banded softmax between them (csarofeen/pytorch issue 2096, first fusion repro)
 they give attention over a (dilated) sliding window and its gradients:
 
-    forward:   S = qk(Q, K)        P = softmax(scale * S)       O = pv(P, V)
+    forward:   S = qk(Q, K)        P = softmax(scale * S [+ key mask term])   O = pv(P, V)
     backward:  dP = qk(dO, V)      dV = pvT(P, dO)
                dS = softmax_backward(P, dP)                    (scale included)
                dQ = pv(dS, K)      dK = pvT(dS, Q)
@@ -26,9 +26,10 @@ class BandedAttention(torch.autograd.Function):
     """O = softmax_band(scale * Q K^T) V over the window (w, w_upper, dilation)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, w, w_upper, dilation, scale):
+    def forward(ctx, q, k, v, w, w_upper, dilation, scale, key_mask=None, mask_value=-10000.0):
         band = diagmm_qk(q, k, w, w_upper, dilation, 0.0)
-        probs = diagmm_banded_softmax(band, w, w_upper, dilation, scale, inplace=True)
+        probs = diagmm_banded_softmax(band, w, w_upper, dilation, scale, inplace=True,
+                                      key_mask=key_mask, mask_value=mask_value)
         out = diagmm_pv(probs, v, w, w_upper, dilation)
         ctx.save_for_backward(q, k, v, probs)
         ctx.window = (w, w_upper, dilation, scale)
@@ -45,15 +46,19 @@ class BandedAttention(torch.autograd.Function):
                                                  out=dprobs)
         dq = diagmm_pv(dscores, k, w, w_upper, dilation)
         dk = diagmm_pvT(dscores, q, w, w_upper, dilation)
-        return dq, dk, dv, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None
 
 
-def banded_attention(q, k, v, w, w_upper=None, dilation=0, scale=None):
+def banded_attention(q, k, v, w, w_upper=None, dilation=0, scale=None, key_mask=None,
+                     mask_value=-10000.0):
     """Sliding-window attention of ``q`` over ``k``/``v`` ([b, n, h, d] each): slot kk of
     row i attends key i + (kk - w) * max(dilation, 1) for kk in 0 .. w + w_upper; keys
-    outside the sequence are masked.  ``scale`` defaults to 1 / sqrt(d)."""
+    outside the sequence are masked.  ``scale`` defaults to 1 / sqrt(d).  ``key_mask``
+    (float32 [b, n], 1 = keep) adds (1 - key_mask) * mask_value to each key's scores (the
+    attention mask of the issue 2096 repro); the backward pass is unchanged by it."""
     if w_upper is None:
         w_upper = w
     if scale is None:
         scale = q.shape[-1] ** -0.5
-    return BandedAttention.apply(q, k, v, int(w), int(w_upper), int(dilation), float(scale))
+    return BandedAttention.apply(q, k, v, int(w), int(w_upper), int(dilation), float(scale),
+                                 key_mask, float(mask_value))

@@ -249,6 +249,35 @@ diagmm_status_t diagmm_banded_softmax(const void* scores, void* probs, int64_t b
                                 static_cast<hipStream_t>(stream)));
 }
 
+diagmm_status_t diagmm_banded_softmax_masked(const void* scores, void* probs,
+                                             const float* key_mask, int64_t b, int64_t n,
+                                             int64_t h, int64_t w, int64_t w_upper,
+                                             int64_t dilation, float scale, float mask_value,
+                                             diagmm_dtype_t in_dtype, diagmm_dtype_t out_dtype,
+                                             void* stream) {
+    const char* fn = "diagmm_banded_softmax_masked";
+    Problem p;
+    int64_t de, be;
+    diagmm_status_t st = check_common(fn, b, n, h, 1, w, w_upper, dilation, in_dtype, out_dtype,
+                                      &p, &de, &be);
+    if (st != DIAGMM_OK) return st;
+    if (p.rows() * p.h == 0) return ok();
+    if (!scores || !probs || !key_mask) return fail(DIAGMM_ERR_NULL, "%s: null pointer", fn);
+    const bool in_place = scores == probs && in_dtype == out_dtype;
+    const int64_t pb = be * static_cast<int64_t>(elem_size(out_dtype));
+    if (!in_place && overlaps(probs, pb, scores, be * elem_size(in_dtype)))
+        return fail(DIAGMM_ERR_ALIAS, "%s: probs overlaps scores (only exact in-place with "
+                    "equal dtypes is allowed)", fn);
+    if (overlaps(probs, pb, key_mask, p.rows() * 4))
+        return fail(DIAGMM_ERR_ALIAS, "%s: probs overlaps key_mask", fn);
+    if (!softmax_masked_supported(p))
+        return fail(DIAGMM_ERR_UNSUPPORTED, "%s: more than 2^31 rows or 2^30 slots", fn);
+    timing_set_op(kOpSoftmaxMasked);
+    return launched(fn, launch_softmax_masked(scores, probs, key_mask, p, scale, mask_value,
+                                              in_dtype, out_dtype,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 diagmm_status_t diagmm_banded_softmax_backward(const void* probs, const void* dprobs,
                                                void* dscores, int64_t b, int64_t n,
                                                int64_t h, int64_t w, int64_t w_upper,

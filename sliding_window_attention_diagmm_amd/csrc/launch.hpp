@@ -39,6 +39,12 @@ hipError_t launch_softmax_bwd(const void* probs, const void* dprobs, void* dscor
                               const Problem& p, float scale, int dt, bool fast,
                               hipStream_t stream);
 
+// Banded softmax with a per-key additive mask (float32 [b][n]).
+bool softmax_masked_supported(const Problem& p);
+hipError_t launch_softmax_masked(const void* scores, void* probs, const float* key_mask,
+                                 const Problem& p, float scale, float mask_value, int in_dt,
+                                 int out_dt, hipStream_t stream);
+
 // qk on MFMA (f16 / bf16 inputs, d in {32, 64, 128}, 16-byte aligned pointers).
 constexpr int kQkRows = 128;                 // rows per tile
 constexpr int64_t kQkLdsBytes = 160 * 1024;  // one workgroup per compute unit

@@ -36,7 +36,8 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for want in ("diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax",
-                 "diagmm_banded_softmax_backward", "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
+                 "diagmm_banded_softmax_backward", "diagmm_banded_softmax_masked",
+                 "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
                  "diagmm_plan"):
         assert want in names
 
@@ -47,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dm.diagmm_abi_version() == 3
+    assert dm.diagmm_abi_version() == 4
     seen = set()
     for st in range(7):
         s = lib.diagmm_status_string(st).decode()
@@ -95,6 +96,14 @@ def test_validation_errors_are_reported_without_launching(lib):
     assert bw(P_, D_, P_ + 2, 1, 8, 1, 2, 2, 0, 1.0, 1, None) == ERR_ALIAS   # partial overlap
     assert bw(P_, D_, D_ + 78, 1, 8, 1, 2, 2, 0, 1.0, 1, None) == ERR_ALIAS  # last element
     assert "diagmm_banded_softmax_backward" in lib.diagmm_last_error().decode()
+    ms = lib.diagmm_banded_softmax_masked
+    M_ = FAKE + (1 << 38)
+    assert ms(P_, O_, 0, 1, 8, 1, 2, 2, 0, 1.0, -1e4, 1, 1, None) == ERR_NULL
+    assert ms(P_, O_, M_, 1, 8, 1, 2, 2, -1, 1.0, -1e4, 1, 1, None) == ERR_SHAPE
+    assert ms(P_, O_, M_, 1, 8, 1, 2, 2, 0, 1.0, -1e4, 1, 2, None) == ERR_DTYPE
+    assert ms(P_, P_ + 2, M_, 1, 8, 1, 2, 2, 0, 1.0, -1e4, 1, 1, None) == ERR_ALIAS
+    assert ms(P_, O_, O_ + 16, 1, 8, 1, 2, 2, 0, 1.0, -1e4, 1, 1, None) == ERR_ALIAS
+    assert "diagmm_banded_softmax_masked" in lib.diagmm_last_error().decode()
 
 
 def test_empty_problems_are_noops(lib):
@@ -103,6 +112,8 @@ def test_empty_problems_are_noops(lib):
     assert lib.diagmm_pv(0, 0, 0, 1, 8, 0, 4, 2, 2, 0, 0.0, 2, 0, None) == OK
     assert lib.diagmm_banded_softmax(0, 0, 0, 8, 3, 2, 2, 0, 1.0, 1, 1, None) == OK
     assert lib.diagmm_banded_softmax_backward(0, 0, 0, 0, 8, 3, 2, 2, 0, 1.0, 1, None) == OK
+    assert lib.diagmm_banded_softmax_masked(0, 0, 0, 0, 8, 3, 2, 2, 0, 1.0, -1e4, 1, 1,
+                                            None) == OK
     assert lib.diagmm_last_error().decode() == ""
 
 

@@ -63,6 +63,8 @@ def op_costs(dil):
         "pvT": {"bytes": cnt * E + 2 * dense, "flops": 2 * D * cnt},
         # gradient path: P and dP read on their in-range slots, the whole band written
         "softmax_bwd": {"bytes": 2 * cnt * E + band, "flops": 0},
+        # the softmax with the per-key mask: the softmax's bytes and the [b, n] f32 mask
+        "softmax_masked": {"bytes": cnt * E + band + B * N * 4, "flops": 0},
     }
 
 
@@ -185,7 +187,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="short run for hardware counters: 3 passes of each kernel (and the softmax "
-                         "backward) at the bench workload plus a reference copy of 64 MiB "
+                         "backward and masked softmax) at the bench workload plus a reference copy of 64 MiB "
                          "(calibrates FETCH_SIZE / "
                          "WRITE_SIZE); prints the reference size and exits")
     args = ap.parse_args()
@@ -223,6 +225,8 @@ def main():
         # L2 or the Infinity Cache) after a 512 MiB fill has flushed both caches.
         dprobs = dm.diagmm_qk(sets[0]["do"], sets[0]["v"], W, WU, 0, 0.0)
         dscores = torch.empty_like(dprobs)
+        key_mask = torch.ones((B, N), dtype=torch.float32, device=dev)
+        key_mask[:, -N // 10:] = 0.0
         flush = torch.empty(256 << 20, dtype=torch.float16, device=dev)
         src = torch.empty(ref_bytes // 2, dtype=torch.float16, device=dev)
         dst = torch.empty_like(src)
@@ -240,6 +244,8 @@ def main():
                 dm.diagmm_pvT(t[f"S{dil}"], t["do"], W, WU, dil, out=t[f"X{dil}"])
                 dm.diagmm_banded_softmax_backward(t[f"S{dil}"], dprobs, W, WU, dil, SCALE,
                                                   out=dscores)
+                dm.diagmm_banded_softmax(t[f"S{dil}"], W, WU, dil, SCALE, out=dscores,
+                                         key_mask=key_mask)
         torch.cuda.synchronize()
         print(json.dumps({"pmc_probe": True, "reference_copy_bytes": ref_bytes,
                           "qk_algorithmic_bytes": op_costs(0)["qk"]["bytes"],
@@ -305,33 +311,40 @@ def main():
     # The banded softmax backward, the one kernel the gradient path adds (it sits between
     # dP = qk(dO, V) and the two transposed products), timed on its own over the same
     # rotating sets: P from the step above, dP = qk(dO, V) computed once per set.
+    # The softmax with the per-key attention mask (the last tenth of the positions masked)
+    # is timed the same way, out of place from the step's band.
     extra = {}
+    key_mask = torch.ones((B, N), dtype=torch.float32, device=dev)
+    key_mask[:, -N // 10:] = 0.0
     for t in sets:
         t["dP"] = dm.diagmm_qk(t["do"], t["v"], W, WU, 0, 0.0)
         t["dS"] = torch.empty_like(t["dP"])
-    for dil in DILATIONS:
-        def bwd(t):
-            dm.diagmm_banded_softmax_backward(t[f"S{dil}"], t["dP"], W, WU, dil, SCALE,
-                                              out=t["dS"])
-        for i in range(args.warmup):
-            bwd(sets[i % len(sets)])
-        torch.cuda.synchronize()
-        dm.diagmm_timing_begin(args.steps)
-        for i in range(args.steps):
-            bwd(sets[i % len(sets)])
-        torch.cuda.synchronize()
-        dm.diagmm_timing_end()
-        recs = [ms for name, ms in dm.diagmm_timing_read() if name == "softmax_bwd"]
-        assert len(recs) == args.steps, (len(recs), args.steps)
-        ms = sum(recs) / len(recs)
-        c = op_costs(dil)["softmax_bwd"]
-        extra[f"softmax_bwd_dil{dil}"] = {
-            "us": round(ms * 1e3, 2),
-            "GB/s": round(c["bytes"] / (ms * 1e-3) / 1e9, 1),
-            "bytes": c["bytes"],
-            "kernel": dm.diagmm_plan("softmax_bwd", B, N, H, 1, W, WU, dil,
-                                     torch.float16)["kernel"],
-        }
+    for op in ("softmax_bwd", "softmax_masked"):
+        for dil in DILATIONS:
+            def run(t):
+                if op == "softmax_bwd":
+                    dm.diagmm_banded_softmax_backward(t[f"S{dil}"], t["dP"], W, WU, dil, SCALE,
+                                                      out=t["dS"])
+                else:
+                    dm.diagmm_banded_softmax(t[f"S{dil}"], W, WU, dil, SCALE, out=t["dS"],
+                                             key_mask=key_mask)
+            for i in range(args.warmup):
+                run(sets[i % len(sets)])
+            torch.cuda.synchronize()
+            dm.diagmm_timing_begin(args.steps)
+            for i in range(args.steps):
+                run(sets[i % len(sets)])
+            torch.cuda.synchronize()
+            dm.diagmm_timing_end()
+            recs = [ms for name, ms in dm.diagmm_timing_read() if name == op]
+            assert len(recs) == args.steps, (len(recs), args.steps)
+            ms = sum(recs) / len(recs)
+            c = op_costs(dil)[op]
+            extra[f"{op}_dil{dil}"] = {
+                "us": round(ms * 1e3, 2),
+                "GB/s": round(c["bytes"] / (ms * 1e-3) / 1e9, 1),
+                "bytes": c["bytes"],
+            }
     for t in sets:
         del t["dP"], t["dS"]
     ceiling = practical_ceiling(torch, dev, stream)

@@ -8,9 +8,10 @@
 //
 // The work is laid out as in the unmasked softmax: L lanes per band row, here with at
 // most 3 pieces of 16 bytes per lane (a 513-slot f16 row on 32 lanes), every piece loaded
-// whole, then the mask values of the lane's slots gathered (the index of an out-of-range
-// slot is clamped to the row's own key, so every gather is in bounds and none depends on
-// a branch), then the reductions and the stores (row ends element by element, so the
+// whole, then the mask values of the lane's slots gathered (16-byte loads for a piece
+// wholly in range without dilation; otherwise element by element, the index of an
+// out-of-range slot clamped to the row's own key, so every gather is in bounds), then the
+// reductions and the stores (row ends element by element, so the
 // softmax may run in place).  Other shapes, dtype pairs and alignments go to a
 // workgroup-per-row kernel.  The gradient needs no variant: the added term does not
 // depend on the scores, so the banded softmax backward applies as it is.
@@ -118,16 +119,25 @@ softmax_masked_group_kernel(const typename T::T* scores, typename T::T* probs,
     }
     // Mask values of this lane's slots (key i + (k - w) s; the row's own key when the slot
     // is out of range, whose value is then not used).
+    // Without dilation a piece's slots have consecutive keys: a piece wholly in range reads
+    // its mask values as one run (the loads merge into wide ones), the others element by
+    // element.
     float mk[kPer][kVec];
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
         const int base = (t + L * q) * kVec - sh;
+        if (p.s == 1 && base >= rg.k_lo && base + kVec <= rg.k_hi) {
+            const float* mp = key_mask + rg.mrow + (base - p.w);   // consecutive, merged
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-            const int k = base + e;
-            const bool in = k >= rg.k_lo && k < rg.k_hi;
-            const int64_t off = in ? static_cast<int64_t>(k - p.w) * p.s : 0;
-            mk[q][e] = key_mask[rg.mrow + off];
+            for (int e = 0; e < kVec; ++e) mk[q][e] = mp[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                const int k = base + e;
+                const bool in = k >= rg.k_lo && k < rg.k_hi;
+                const int64_t off = in ? static_cast<int64_t>(k - p.w) * p.s : 0;
+                mk[q][e] = key_mask[rg.mrow + off];
+            }
         }
     }
     float x[kPer][kVec];

@@ -811,12 +811,18 @@ QkTilePlan plan_qk_mfma(const Problem& p, int out_dt) {
     // The widest chunk (at most 513 slots) whose ring + query tiles fit in LDS ...
     int64_t max_slots = kMaxSlots;
     while (max_slots > 16 && layout_for(max_slots, p.d).bytes > kQkLdsBytes) --max_slots;
-    // ... then the chunk count that balances the tiles over the compute units best: the
-    // busiest unit's work ~ ceil(tiles / units) x (rows + chunk + a fixed cost per tile).
+    // ... as few chunks as possible: every chunk reads the query and key rows again, and
+    // the whole launch is bound by HBM traffic.  With 1.5 tiles per unit (n=4096, h=12,
+    // 513 slots) one chunk took 22.9 us against 24.0 us for two, although its busiest
+    // units sweep twice the slots: units with one tile finish early and leave the rest
+    // the bandwidth.  Only when that leaves fewer than 1.4 tiles per unit is the chunk
+    // count that balances the tiles best chosen instead: the busiest unit's work ~
+    // ceil(tiles / units) x (rows + chunk + a fixed cost per tile).
     const int64_t cus = device_cus();
     TileGrid best = make_grid(p.b, p.n, p.h, p.K, p.s, kRows, max_slots);
+    const bool balance = best.tiles * 10 < cus * 14;
     int64_t best_cost = -1;
-    for (int64_t extra = 0; extra < 4; ++extra) {
+    for (int64_t extra = 0; balance && extra < 4; ++extra) {
         const int64_t nkb = ceil_div(p.K, max_slots) + extra;
         if (nkb > p.K) break;
         const TileGrid g = make_grid(p.b, p.n, p.h, p.K, p.s, kRows, ceil_div(p.K, nkb));

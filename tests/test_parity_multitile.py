@@ -18,6 +18,7 @@ DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 # (b, n, h, d, w, w_upper, dilation, in, out, workgroups)
 CASES = [
     (1, 2048, 3, 64, 256, 256, 0, "f16", "f16", 8),
+    (1, 2048, 2, 64, 300, 300, 0, "f16", "f16", 8),   # 601 slots: two qk slot chunks
     (1, 2048, 3, 64, 256, 256, 3, "f16", "f16", 8),
     (2, 1100, 2, 64, 128, 40, 2, "bf16", "f32", 5),
     (1, 1500, 2, 32, 200, 200, 0, "f16", "f16", 3),
@@ -96,3 +97,17 @@ def test_small_grid_matches_oracle(case, monkeypatch):
         p_gpu = dm.diagmm_banded_softmax(pc, w, wu, dil, 0.5).cpu()
         check_close(p_gpu, oracle.softmax(probs, w, wu, dil, 0.5, out_dtype=torch.float64),
                     DT[ind], "softmax", mask)
+
+
+def test_qk_takes_the_fewest_slot_chunks_when_tiles_suffice(monkeypatch):
+    """One chunk at the benchmark shape (384 tiles for 256 units); more only when the
+    fewest leave under 1.4 tiles per unit (a 65-slot band of 512 positions: 4 tiles)."""
+    monkeypatch.delenv("DIAGMM_MAX_WORKGROUPS", raising=False)
+    for dil in (0, 3):
+        pl = dm.diagmm_plan("qk", 1, 4096, 12, 64, 256, 256, dil, torch.float16)
+        if pl["workgroups"] == 256:
+            assert pl["slots_per_tile"] == 513, pl
+    assert dm.diagmm_plan("qk", 1, 2048, 2, 64, 300, 300, 0, torch.float16)["slots_per_tile"] < 601
+    monkeypatch.setenv("DIAGMM_MAX_WORKGROUPS", "8")
+    pl = dm.diagmm_plan("qk", 1, 512, 1, 64, 32, 32, 0, torch.float16)
+    assert pl["tiles"] >= 8 and pl["slots_per_tile"] < 65, pl

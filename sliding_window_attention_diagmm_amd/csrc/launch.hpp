@@ -54,6 +54,7 @@ struct QkTilePlan {
     int64_t rs = 0;         // staging row stride (elements)
     int64_t lds_bytes = 0;
     int64_t workgroups = 0; // persistent workgroups (at most one per compute unit)
+    int64_t strip_wgs = 0;  // workgroups per strip with the strip split, 0 = flat split
     bool ok = false;        // the shape fits the kernel's 32-bit tile arithmetic
 };
 

@@ -777,6 +777,8 @@ hipError_t launch_typed(const void* q, const void* k, void* band, const Problem&
              static_cast<int32_t>(l.q_off),
              static_cast<uint32_t>(tp.workgroups), pad,
              make_decode(tp.grid, p.h, p.n, p.s, tp.grid.tiles, tp.workgroups)};
+    if (tp.strip_wgs > 0)
+        set_strip_split(&a.dc, tp.grid.tiles / tp.grid.rb, tp.grid.rb, tp.strip_wgs);
     auto kern = qk_mfma_kernel<In, Out, D>;
     // Once per instantiation (thread-safe static initialisation): allow all of the
     // compute unit's LDS as dynamic LDS.
@@ -837,6 +839,21 @@ QkTilePlan plan_qk_mfma(const Problem& p, int out_dt) {
     tp.rs = 0;
     tp.lds_bytes = l.bytes;
     tp.workgroups = tp.grid.tiles < cus ? tp.grid.tiles : cus;
+    // Strip split: a fixed group of workgroups per strip (the row blocks of one slot chunk
+    // of one residue class of one (batch, head)) whenever it does not lengthen the longest
+    // tile list.  A range that crosses into a second strip has to load that strip's whole
+    // window; with one 513-slot chunk two windows do not fit in the ring, so that load is
+    // not prefetched and such workgroups would end last.  (n=4096, h=12: 21 workgroups
+    // per strip of 32 row blocks, 11 of them with two tiles; 252 of 256 busy.)
+    {
+        const int64_t per_strip = tp.grid.rb;
+        const int64_t strips = per_strip > 0 ? tp.grid.tiles / per_strip : 0;
+        const int64_t g = strips > 0 ? tp.workgroups / strips : 0;
+        if (g >= 1 && g <= per_strip && strips * per_strip == tp.grid.tiles &&
+            ceil_div(per_strip, g) <= ceil_div(tp.grid.tiles, tp.workgroups) &&
+            ceil_div(tp.grid.tiles, tp.workgroups) > 1)
+            tp.strip_wgs = g;
+    }
     // (q and k rows of one strip are addressed by 32-bit byte offsets)
     tp.ok = tp.grid.tiles <= kMaxTiles && ceil_div(p.n, p.s) < (int64_t(1) << 30) &&
             (p.n + p.s) * p.h * p.d * 2 < (int64_t(1) << 32) &&

@@ -49,6 +49,7 @@ Plan plan_qk(const Problem& p, int in_dt, int out_dt) {
     pl.slots_per_tile = tp.grid.kb;
     pl.tiles = tp.grid.tiles;
     pl.workgroups = tp.workgroups;
+    pl.strip_wgs = tp.strip_wgs;
     pl.threads = 512;
     pl.lds_bytes = tp.lds_bytes;
     pl.residues = tp.grid.res;

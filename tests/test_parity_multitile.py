@@ -63,8 +63,14 @@ def test_strip_split_choice(monkeypatch):
     for mode in ("pv", "pvT"):
         assert dm.diagmm_plan(mode, 2, 1100, 1, 64, 96, 30, 4,
                               torch.bfloat16)["strip_workgroups"] == 2
+    # qk takes the strip split whenever it does not lengthen the longest tile list
     assert dm.diagmm_plan("qk", 2, 1100, 1, 64, 96, 30, 4,
-                          torch.bfloat16)["strip_workgroups"] == 0
+                          torch.bfloat16)["strip_workgroups"] == 2
+    monkeypatch.delenv("DIAGMM_MAX_WORKGROUPS")
+    for dil, g in ((0, 21), (3, 7)):
+        pl = dm.diagmm_plan("qk", 1, 4096, 12, 64, 256, 256, dil, torch.float16)
+        if pl["workgroups"] == 256:
+            assert pl["strip_workgroups"] == g, pl
 
 
 @pytest.mark.gpu

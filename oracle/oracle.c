@@ -402,3 +402,37 @@ int oracle_softmax_masked(const void* scores, void* probs, const float* key_mask
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------ dropout
+ * The dropout of the first fusion repro on the csarofeen/pytorch issue 2096 page, on
+ * the band: a slot is kept when its uniform random number exceeds p, and a kept
+ * probability is scaled by 1 / (1 - p) (1.11111 there, for p = 0.1):
+ *     out[k] = rand[k] > p ? probs[k] / (1 - p) : 0     for in-range slots,
+ *     out[k] = 0                                        for out-of-range slots.
+ * The random numbers are an input (float32, one per band element), so the keep decision
+ * is the same comparison on both sides; it is taken in float32 (rand and p as floats). */
+int oracle_dropout(const void* probs, const float* rand, void* out, int64_t b, int64_t n,
+                   int64_t h, int64_t w, int64_t wu, int64_t dil, float p, int in_dt,
+                   int out_dt, int nthreads)
+{
+    int bad = or_check(b, n, h, 1, w, wu, dil, in_dt, out_dt);
+    if (bad) return bad;
+    if (!rand || !(p >= 0.0f) || !(p < 1.0f)) return 1;
+    const int64_t K = w + wu + 1, s = or_stride(dil);
+    const double scale = 1.0 / (1.0 - (double)p);
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t r = 0; r < b * n; ++r) {
+        const int64_t i = r % n;
+        for (int64_t hh = 0; hh < h; ++hh) {
+            const int64_t row = (r * h + hh) * K;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t j = i + (k - w) * s;
+                double v = 0.0;
+                if (j >= 0 && j < n && rand[row + k] > p)
+                    v = or_load(probs, row + k, in_dt) * scale;
+                or_store(out, row + k, out_dt, v);
+            }
+        }
+    }
+    return 0;
+}

@@ -489,6 +489,42 @@ def test_masked_softmax_closed_forms():
     assert torch.equal(P16, oracle.convert(P, torch.float16))
 
 
+# ------------------------------------------------------------- dropout pins
+
+def test_dropout_keeps_by_comparison_and_scales():
+    n, w, wu = 60, 8, 8
+    K = w + wu + 1
+    g = datagen.rng(81)
+    S = datagen.normal(g, (2, n, 3, K), "f32")
+    P = oracle.softmax(S, w, wu, 0, out_dtype=torch.float64)
+    rand = torch.from_numpy(g.random((2, n, 3, K), dtype=np.float32))
+    ones = torch.ones(1, n, 1, 1)
+    inr = (oracle.qk(ones, ones, w, wu, padding=0.0) == 1).expand_as(P)
+    for p in (0.1, 0.5):
+        out = oracle.dropout(P, rand, w, wu, 0, p=p, out_dtype=torch.float64)
+        keep = inr & (rand > torch.tensor(p, dtype=torch.float32))
+        assert torch.equal(out != 0, keep & (P != 0))
+        pf = float(np.float32(p))                          # p as the float the call takes
+        np.testing.assert_allclose(out[keep].numpy(), (P[keep] / (1.0 - pf)).numpy(),
+                                   rtol=1e-15)
+        assert torch.all(out[~inr] == 0)
+        # the kept share of in-range slots is 1 - p within five binomial deviations
+        m = int(inr.sum())
+        share = keep.sum().item() / m
+        assert abs(share - (1 - p)) <= 5 * math.sqrt(p * (1 - p) / m)
+    # out-of-range slots are 0 whatever the band holds there
+    poisoned = torch.where(inr, P, torch.full_like(P, 7.0))
+    assert torch.all(oracle.dropout(poisoned, rand, w, wu, 0, p=0.1,
+                                    out_dtype=torch.float64)[~inr] == 0)
+    # p = 0 keeps every in-range probability exactly; a 16-bit output is rounded once
+    assert torch.equal(oracle.dropout(P, rand, w, wu, 0, p=0.0, out_dtype=torch.float64),
+                       torch.where(inr, P, torch.zeros_like(P)))
+    Ph = oracle.convert(P, torch.float16)
+    d64 = oracle.dropout(Ph, rand, w, wu, 0, p=0.1, out_dtype=torch.float64)
+    assert torch.equal(oracle.dropout(Ph, rand, w, wu, 0, p=0.1),
+                       oracle.convert(d64, torch.float16))
+
+
 # ---------------------------------------------------- softmax backward pins
 # The gradient of the banded softmax with respect to its stored scores is not printed
 # on the pages; it is the chain rule through their softmax recipe.  Three independent

@@ -65,6 +65,8 @@ def op_costs(dil):
         "softmax_bwd": {"bytes": 2 * cnt * E + band, "flops": 0},
         # the softmax with the per-key mask: the softmax's bytes and the [b, n] f32 mask
         "softmax_masked": {"bytes": cnt * E + band + B * N * 4, "flops": 0},
+        # dropout: P and its float32 random numbers on the in-range slots, the band written
+        "dropout": {"bytes": cnt * (E + 4) + band, "flops": 0},
     }
 
 
@@ -227,6 +229,7 @@ def main():
         dscores = torch.empty_like(dprobs)
         key_mask = torch.ones((B, N), dtype=torch.float32, device=dev)
         key_mask[:, -N // 10:] = 0.0
+        rand = torch.rand(dprobs.shape, device=dev, dtype=torch.float32)
         flush = torch.empty(256 << 20, dtype=torch.float16, device=dev)
         src = torch.empty(ref_bytes // 2, dtype=torch.float16, device=dev)
         dst = torch.empty_like(src)
@@ -246,6 +249,7 @@ def main():
                                                   out=dscores)
                 dm.diagmm_banded_softmax(t[f"S{dil}"], W, WU, dil, SCALE, out=dscores,
                                          key_mask=key_mask)
+                dm.diagmm_banded_dropout(t[f"S{dil}"], rand, W, WU, dil, 0.1, out=dscores)
         torch.cuda.synchronize()
         print(json.dumps({"pmc_probe": True, "reference_copy_bytes": ref_bytes,
                           "qk_algorithmic_bytes": op_costs(0)["qk"]["bytes"],
@@ -312,22 +316,28 @@ def main():
     # dP = qk(dO, V) and the two transposed products), timed on its own over the same
     # rotating sets: P from the step above, dP = qk(dO, V) computed once per set.
     # The softmax with the per-key attention mask (the last tenth of the positions masked)
-    # is timed the same way, out of place from the step's band.
+    # is timed the same way, out of place from the step's band, and so is the dropout
+    # (p = 0.1, float32 random numbers drawn once per set by torch's generator).
     extra = {}
     key_mask = torch.ones((B, N), dtype=torch.float32, device=dev)
     key_mask[:, -N // 10:] = 0.0
+    gen = torch.Generator(device=dev).manual_seed(5)
     for t in sets:
         t["dP"] = dm.diagmm_qk(t["do"], t["v"], W, WU, 0, 0.0)
         t["dS"] = torch.empty_like(t["dP"])
-    for op in ("softmax_bwd", "softmax_masked"):
+        t["rand"] = torch.rand(t["dP"].shape, generator=gen, device=dev, dtype=torch.float32)
+    for op in ("softmax_bwd", "softmax_masked", "dropout"):
         for dil in DILATIONS:
             def run(t):
                 if op == "softmax_bwd":
                     dm.diagmm_banded_softmax_backward(t[f"S{dil}"], t["dP"], W, WU, dil, SCALE,
                                                       out=t["dS"])
-                else:
+                elif op == "softmax_masked":
                     dm.diagmm_banded_softmax(t[f"S{dil}"], W, WU, dil, SCALE, out=t["dS"],
                                              key_mask=key_mask)
+                else:
+                    dm.diagmm_banded_dropout(t[f"S{dil}"], t["rand"], W, WU, dil, 0.1,
+                                             out=t["dS"])
             for i in range(args.warmup):
                 run(sets[i % len(sets)])
             torch.cuda.synchronize()
@@ -346,7 +356,7 @@ def main():
                 "bytes": c["bytes"],
             }
     for t in sets:
-        del t["dP"], t["dS"]
+        del t["dP"], t["dS"], t["rand"]
     ceiling = practical_ceiling(torch, dev, stream)
     qk_us = per_op["qk_dil0"]["us"]
     qk_bytes = op_costs(0)["qk"]["bytes"]

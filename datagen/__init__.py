@@ -92,6 +92,11 @@ def uniform_rows(g: np.random.Generator, shape, dtype) -> torch.Tensor:
     return to_dtype(u, dtype)
 
 
+def uniform(g: np.random.Generator, shape) -> torch.Tensor:
+    """float32 U[0, 1) values (the random numbers a dropout compares with its p)."""
+    return torch.from_numpy(g.random(size=shape, dtype=np.float32))
+
+
 def softmax_rows(g: np.random.Generator, shape, dtype) -> torch.Tensor:
     """Probabilities: a float32 softmax over the whole last axis of N(0,1) logits."""
     z = torch.from_numpy(g.standard_normal(size=shape, dtype=np.float32))

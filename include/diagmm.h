@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DIAGMM_ABI_VERSION 4
+#define DIAGMM_ABI_VERSION 5
 
 typedef enum {
     DIAGMM_F32 = 0,
@@ -160,6 +160,27 @@ diagmm_status_t diagmm_banded_softmax_backward(const void* probs, const void* dp
                                                int64_t dilation, float scale,
                                                diagmm_dtype_t dtype, void* stream);
 
+/*
+ * diagmm_banded_dropout - dropout on a probability band, as in the issue 2096 repro
+ * (a uniform random tensor of the band's shape compared with the drop probability, the
+ * kept values scaled by 1 / (1 - p)):
+ *   out[bb,i,hh,k] = probs[bb,i,hh,k] / (1 - p)   if rand[bb,i,hh,k] > p and slot k is in
+ *                                                 range (0 <= i + (k - w) * s < n),
+ *                    +0                           otherwise.
+ * The random numbers are an input: rand is float32 [b][n][h][K] on the device (any
+ * values; a slot is kept when its float32 rand compares greater than p, so rand == p
+ * drops), drawn by the caller.  With the same rand, the call applied to the gradient of
+ * a loss with respect to out gives its gradient with respect to probs.  probs and out
+ * are band tensors [b][n][h][K] of one dtype (f32, f16 or bf16; the product in f32 with
+ * 1 / (1 - p) rounded to f32 once, then rounded to nearest even).  p in [0, 1), else
+ * DIAGMM_ERR_SHAPE.  out may be probs itself (in place); any other overlap with probs,
+ * or any overlap with rand, is DIAGMM_ERR_ALIAS.  Errors otherwise as for the other calls.
+ */
+diagmm_status_t diagmm_banded_dropout(const void* probs, const float* rand, void* out,
+                                      int64_t b, int64_t n, int64_t h, int64_t w,
+                                      int64_t w_upper, int64_t dilation, float p,
+                                      diagmm_dtype_t dtype, void* stream);
+
 /* Static text for a status code. */
 const char* diagmm_status_string(diagmm_status_t status);
 
@@ -174,8 +195,11 @@ int diagmm_abi_version(void);
  * call with these arguments is cut into workgroups: which kernel runs, the tile shape
  * (rows per tile, slots per tile), how many tiles and workgroups, the LDS bytes per
  * workgroup, and how many residue classes the dilation splits the rows into.
- * mode: 0 = qk, 1 = pv, 2 = pvT, 3 = banded softmax, 4 = banded softmax backward
- * (planned for 16-byte aligned tensors; out_dtype must equal in_dtype).  Returns DIAGMM_ERR_SHAPE /
+ * mode: 0 = qk, 1 = pv, 2 = pvT, 3 = banded softmax, 4 = banded softmax backward,
+ * 6 = banded dropout (the timing tags; 5, the masked softmax, has no plan).  Modes 4 and
+ * 6 are planned for 16-byte aligned tensors, and out_dtype must equal in_dtype; for 6
+ * rows_per_tile is 0, slots_per_tile the band elements a workgroup takes and tiles the
+ * workgroups.  Returns DIAGMM_ERR_SHAPE /
  * DIAGMM_ERR_DTYPE for invalid arguments, as the compute calls would.
  */
 typedef struct {
@@ -203,7 +227,7 @@ diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d
  * kernel launches by this library records a pair of HIP events at the kernel's own start
  * and end on the stream it is launched on (hipExtLaunchKernel), tagged with the entry
  * point (the diagmm_plan modes: 0 qk, 1 pv, 2 pvT, 3 banded softmax, 4 its backward;
- * 5 the masked softmax); further launches
+ * 5 the masked softmax, 6 dropout); further launches
  * run untimed.  One session at a time, process-wide, on one device (the events are made
  * on the device current at diagmm_timing_begin; launches on another device are not to be
  * timed).  diagmm_timing_read waits for the recorded kernels and writes, for the first

@@ -70,7 +70,8 @@ def _load():
             lib.oracle_pvT.argtypes = [vp, vp, vp] + [i64] * 7 + [ci, ci, vp, i64, ci]
             lib.oracle_softmax.argtypes = [vp, vp] + [i64] * 6 + [cd, ci, ci, vp, i64, ci]
             lib.oracle_softmax_bwd.argtypes = [vp, vp, vp] + [i64] * 6 + [cd, ci, ci, vp, i64, ci]
-            lib.oracle_dropout.argtypes = [vp, vp, vp] + [i64] * 6 + [ctypes.c_float, ci, ci, ci]
+            lib.oracle_dropout.argtypes = [vp, vp, vp] + [i64] * 6 + [ctypes.c_float, ci, ci, vp, i64,
+                                           ci]
             lib.oracle_softmax_masked.argtypes = [vp, vp, vp] + [i64] * 6 + [cd, cd, ci, ci, vp,
                                                                                  i64, ci]
             for f in (lib.oracle_qk, lib.oracle_pv, lib.oracle_pvT, lib.oracle_softmax):
@@ -216,21 +217,30 @@ def softmax_masked(scores, key_mask, w, w_upper, dilation=0, scale=1.0, mask_val
     return out
 
 
-def dropout(probs, rand, w, w_upper, dilation=0, p=0.1, out_dtype=None, threads=None):
-    """Dropout on a band [b, n, h, K]: in-range slots with rand > p keep probs / (1 - p),
-    the others 0 (rand: float32 uniforms of the band's shape)."""
+def dropout(probs, rand, w, w_upper, dilation=0, p=0.1, out_dtype=None, n=None, rows=None,
+            threads=None):
+    """Dropout on a band [b, n, h, K] (or packed [len(rows), h, K] with ``n`` given):
+    in-range slots with rand > p keep probs / (1 - p), the others 0 (rand: float32
+    uniforms of the band's shape)."""
     lib = _load()
     pr = _check(probs, "probs")
     rd = rand.to(torch.float32).contiguous()
     if rd.shape != pr.shape:
         raise ValueError("oracle.dropout: rand must have the band's shape")
     out_dtype = out_dtype or pr.dtype
-    b, n, h, K = pr.shape
+    rt, rp, nr = _rows(rows)
+    if rt is None:
+        b, n, h, K = pr.shape
+    else:
+        if n is None:
+            raise ValueError("oracle.dropout: n is required with a row list")
+        b = 1
+        _, h, K = pr.shape
     if K != w + w_upper + 1:
         raise ValueError("oracle.dropout: band width mismatch")
     out = torch.empty(pr.shape, dtype=out_dtype)
     st = lib.oracle_dropout(_ptr(pr), _ptr(rd), _ptr(out), b, n, h, w, w_upper, dilation,
-                            float(p), _CODE[pr.dtype], _CODE[out_dtype],
+                            float(p), _CODE[pr.dtype], _CODE[out_dtype], rp, nr,
                             threads or default_threads())
     if st:
         raise ValueError(f"oracle.dropout: bad arguments ({st})")

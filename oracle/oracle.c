@@ -413,16 +413,17 @@ int oracle_softmax_masked(const void* scores, void* probs, const float* key_mask
  * is the same comparison on both sides; it is taken in float32 (rand and p as floats). */
 int oracle_dropout(const void* probs, const float* rand, void* out, int64_t b, int64_t n,
                    int64_t h, int64_t w, int64_t wu, int64_t dil, float p, int in_dt,
-                   int out_dt, int nthreads)
+                   int out_dt, const int64_t* rows, int64_t nrows, int nthreads)
 {
     int bad = or_check(b, n, h, 1, w, wu, dil, in_dt, out_dt);
     if (bad) return bad;
     if (!rand || !(p >= 0.0f) || !(p < 1.0f)) return 1;
     const int64_t K = w + wu + 1, s = or_stride(dil);
     const double scale = 1.0 / (1.0 - (double)p);
+    if (!rows) nrows = b * n;
 #pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads > 0 ? nthreads : 1)
-    for (int64_t r = 0; r < b * n; ++r) {
-        const int64_t i = r % n;
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = or_row(rows, r) % n;
         for (int64_t hh = 0; hh < h; ++hh) {
             const int64_t row = (r * h + hh) * K;
             for (int64_t k = 0; k < K; ++k) {

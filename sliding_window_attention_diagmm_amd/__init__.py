@@ -24,7 +24,7 @@ import os
 import torch
 
 __all__ = ["diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax",
-           "diagmm_banded_softmax_backward", "diagmm_plan",
+           "diagmm_banded_softmax_backward", "diagmm_banded_dropout", "diagmm_plan",
            "diagmm_timing_begin", "diagmm_timing_end", "diagmm_timing_read",
            "diagmm_abi_version", "library_path", "load", "DiagmmError"]
 
@@ -32,7 +32,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdiagmm.so")
 
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-MODES = {"qk": 0, "pv": 1, "pvT": 2, "softmax": 3, "softmax_bwd": 4, "softmax_masked": 5}
+MODES = {"qk": 0, "pv": 1, "pvT": 2, "softmax": 3, "softmax_bwd": 4, "softmax_masked": 5,
+         "dropout": 6}
 
 
 class DiagmmError(RuntimeError):
@@ -78,6 +79,8 @@ def load() -> ctypes.CDLL:
     lib.diagmm_banded_softmax_backward.restype = ci
     lib.diagmm_banded_softmax_masked.argtypes = [vp, vp, vp] + [i64] * 6 + [f32, f32, ci, ci, vp]
     lib.diagmm_banded_softmax_masked.restype = ci
+    lib.diagmm_banded_dropout.argtypes = [vp, vp, vp] + [i64] * 6 + [f32, ci, vp]
+    lib.diagmm_banded_dropout.restype = ci
     lib.diagmm_status_string.argtypes = [ci]
     lib.diagmm_status_string.restype = ctypes.c_char_p
     lib.diagmm_last_error.argtypes = []
@@ -247,6 +250,29 @@ def diagmm_banded_softmax_backward(probs, dprobs, w, w_upper=None, dilation=0, s
     st = lib.diagmm_banded_softmax_backward(p.data_ptr(), dp.data_ptr(), res.data_ptr(), b, n,
                                             h, w, w_upper, dilation, float(scale),
                                             _DT[p.dtype], _stream(p.device))
+    if st:
+        _raise(lib, st)
+    return res
+
+
+def diagmm_banded_dropout(probs, rand, w, w_upper=None, dilation=0, p=0.1, out=None):
+    """Dropout on a probability band with caller-drawn uniforms ``rand`` (float32, the
+    band's shape): in-range slots with ``rand > p`` keep ``probs / (1 - p)``, the others
+    are 0.  With the same ``rand`` it also maps the gradient with respect to the output to
+    the gradient with respect to ``probs``.  ``out`` may be ``probs`` itself (in place)."""
+    lib = load()
+    w, w_upper, dilation = _window(w, w_upper, dilation)
+    pr = _dense(probs, "probs")
+    rd = _dense(rand, "rand")
+    if rd.dtype != torch.float32 or rd.shape != pr.shape or rd.device != pr.device:
+        raise ValueError("rand must be float32 with the band's shape, on the band's device")
+    b, n, h, K = pr.shape
+    if K != w + w_upper + 1:
+        raise ValueError(f"probs last dim {K} != w + w_upper + 1 = {w + w_upper + 1}")
+    res = out if out is pr else _out(out, pr.shape, pr.dtype, pr.device)
+    st = lib.diagmm_banded_dropout(pr.data_ptr(), rd.data_ptr(), res.data_ptr(), b, n, h, w,
+                                   w_upper, dilation, float(p), _DT[pr.dtype],
+                                   _stream(pr.device))
     if st:
         _raise(lib, st)
     return res

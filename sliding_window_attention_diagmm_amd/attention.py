@@ -5,60 +5,80 @@ serves one forward function and two backward functions told apart by ``transpose
 with the banded softmax between them (csarofeen/pytorch issue 2096, first fusion repro)
 they give attention over a (dilated) sliding window and its gradients:
 
-    forward:   S = qk(Q, K)        P = softmax(scale * S [+ key mask term])   O = pv(P, V)
-    backward:  dP = qk(dO, V)      dV = pvT(P, dO)
-               dS = softmax_backward(P, dP)                    (scale included)
+    forward:   S = qk(Q, K)        P = softmax(scale * S [+ key mask term])
+               Pd = dropout(P, rand)                            (when p > 0; else Pd = P)
+               O = pv(Pd, V)
+    backward:  dPd = qk(dO, V)     dV = pvT(Pd, dO)
+               dP = dropout(dPd, rand)                          (the same keep pattern)
+               dS = softmax_backward(P, dP)                     (scale included)
                dQ = pv(dS, K)      dK = pvT(dS, Q)
 
 Every step runs in the library's kernels; this module only orders the calls, keeps P
-for the backward pass and hands torch's autograd the results.  Tensors are contiguous
-``[b, n, h, d]`` on the GPU in one dtype (f32, f16 or bf16); gradients come back in it.
+(and the caller's random numbers) for the backward pass, where Pd is drawn again from
+them, and hands torch's autograd the results.  Tensors are contiguous ``[b, n, h, d]``
+on the GPU in one dtype (f32, f16 or bf16); gradients come back in it.
 """
 from __future__ import annotations
 
 import torch
 
-from . import (diagmm_banded_softmax, diagmm_banded_softmax_backward, diagmm_pv, diagmm_pvT,
-               diagmm_qk)
+from . import (diagmm_banded_dropout, diagmm_banded_softmax, diagmm_banded_softmax_backward,
+               diagmm_pv, diagmm_pvT, diagmm_qk)
 
 
 class BandedAttention(torch.autograd.Function):
     """O = softmax_band(scale * Q K^T) V over the window (w, w_upper, dilation)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, w, w_upper, dilation, scale, key_mask=None, mask_value=-10000.0):
+    def forward(ctx, q, k, v, w, w_upper, dilation, scale, key_mask=None, mask_value=-10000.0,
+                dropout_p=0.0, dropout_rand=None):
         band = diagmm_qk(q, k, w, w_upper, dilation, 0.0)
         probs = diagmm_banded_softmax(band, w, w_upper, dilation, scale, inplace=True,
                                       key_mask=key_mask, mask_value=mask_value)
-        out = diagmm_pv(probs, v, w, w_upper, dilation)
-        ctx.save_for_backward(q, k, v, probs)
-        ctx.window = (w, w_upper, dilation, scale)
+        kept = probs
+        if dropout_p > 0.0:
+            kept = diagmm_banded_dropout(probs, dropout_rand, w, w_upper, dilation, dropout_p)
+        out = diagmm_pv(kept, v, w, w_upper, dilation)
+        ctx.save_for_backward(q, k, v, probs, dropout_rand if dropout_p > 0.0 else None)
+        ctx.window = (w, w_upper, dilation, scale, dropout_p)
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v, probs = ctx.saved_tensors
-        w, w_upper, dilation, scale = ctx.window
+        q, k, v, probs, rand = ctx.saved_tensors
+        w, w_upper, dilation, scale, p = ctx.window
         dout = dout.contiguous()
         dprobs = diagmm_qk(dout, v, w, w_upper, dilation, 0.0)
-        dv = diagmm_pvT(probs, dout, w, w_upper, dilation)
+        if p > 0.0:
+            kept = diagmm_banded_dropout(probs, rand, w, w_upper, dilation, p)
+            dv = diagmm_pvT(kept, dout, w, w_upper, dilation)
+            del kept
+            diagmm_banded_dropout(dprobs, rand, w, w_upper, dilation, p, out=dprobs)
+        else:
+            dv = diagmm_pvT(probs, dout, w, w_upper, dilation)
         dscores = diagmm_banded_softmax_backward(probs, dprobs, w, w_upper, dilation, scale,
                                                  out=dprobs)
         dq = diagmm_pv(dscores, k, w, w_upper, dilation)
         dk = diagmm_pvT(dscores, q, w, w_upper, dilation)
-        return dq, dk, dv, None, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None, None, None
 
 
 def banded_attention(q, k, v, w, w_upper=None, dilation=0, scale=None, key_mask=None,
-                     mask_value=-10000.0):
+                     mask_value=-10000.0, dropout_p=0.0, dropout_rand=None):
     """Sliding-window attention of ``q`` over ``k``/``v`` ([b, n, h, d] each): slot kk of
     row i attends key i + (kk - w) * max(dilation, 1) for kk in 0 .. w + w_upper; keys
     outside the sequence are masked.  ``scale`` defaults to 1 / sqrt(d).  ``key_mask``
     (float32 [b, n], 1 = keep) adds (1 - key_mask) * mask_value to each key's scores (the
-    attention mask of the issue 2096 repro); the backward pass is unchanged by it."""
+    attention mask of the issue 2096 repro); the backward pass is unchanged by it.
+    ``dropout_p`` > 0 drops attention probabilities as that repro does: ``dropout_rand``
+    (float32 [b, n, h, w + w_upper + 1] on the GPU, drawn by the caller) keeps slot kk
+    of row i when it is greater than ``dropout_p``, and kept probabilities are scaled by
+    1 / (1 - dropout_p)."""
     if w_upper is None:
         w_upper = w
     if scale is None:
         scale = q.shape[-1] ** -0.5
+    if dropout_p > 0.0 and dropout_rand is None:
+        raise ValueError("dropout_p > 0 needs dropout_rand (the caller draws the uniforms)")
     return BandedAttention.apply(q, k, v, int(w), int(w_upper), int(dilation), float(scale),
-                                 key_mask, float(mask_value))
+                                 key_mask, float(mask_value), float(dropout_p), dropout_rand)

@@ -304,16 +304,59 @@ diagmm_status_t diagmm_banded_softmax_backward(const void* probs, const void* dp
                                            static_cast<hipStream_t>(stream)));
 }
 
+diagmm_status_t diagmm_banded_dropout(const void* probs, const float* rand, void* out,
+                                      int64_t b, int64_t n, int64_t h, int64_t w,
+                                      int64_t w_upper, int64_t dilation, float drop_p,
+                                      diagmm_dtype_t dtype, void* stream) {
+    const char* fn = "diagmm_banded_dropout";
+    Problem p;
+    int64_t de, be;
+    diagmm_status_t st = check_common(fn, b, n, h, 1, w, w_upper, dilation, dtype, dtype, &p,
+                                      &de, &be);
+    if (st != DIAGMM_OK) return st;
+    if (!(drop_p >= 0.0f && drop_p < 1.0f))
+        return fail(DIAGMM_ERR_SHAPE, "%s: p = %g is outside [0, 1)", fn, double(drop_p));
+    if (p.rows() * p.h == 0) return ok();
+    if (!probs || !rand || !out) return fail(DIAGMM_ERR_NULL, "%s: null pointer", fn);
+    const int64_t bytes = be * static_cast<int64_t>(elem_size(dtype));
+    if (out != probs && overlaps(out, bytes, probs, bytes))
+        return fail(DIAGMM_ERR_ALIAS, "%s: out overlaps probs (only the exact same pointer, "
+                    "in place, is allowed)", fn);
+    if (overlaps(out, bytes, rand, be * 4))
+        return fail(DIAGMM_ERR_ALIAS, "%s: out overlaps rand", fn);
+    if (!dropout_supported(p))
+        return fail(DIAGMM_ERR_UNSUPPORTED, "%s: more than 2^31 - 1 rows or 2^30 slots", fn);
+    const bool wide = !force_simple() && dropout_wide(p, dtype, probs, rand, out);
+    timing_set_op(kOpDropout);
+    return launched(fn, launch_dropout(probs, rand, out, p, drop_p, dtype, wide,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,
                             int64_t w_upper, int64_t dilation, diagmm_dtype_t in_dtype,
                             diagmm_dtype_t out_dtype, diagmm_plan_t* out) {
     if (!out) return fail(DIAGMM_ERR_NULL, "diagmm_plan: null plan pointer");
-    if (mode < 0 || mode > 4) return fail(DIAGMM_ERR_UNSUPPORTED, "diagmm_plan: mode %d", mode);
+    if (mode < 0 || mode > 6 || mode == 5)
+        return fail(DIAGMM_ERR_UNSUPPORTED, "diagmm_plan: mode %d", mode);
     Problem p;
     int64_t de, be;
     diagmm_status_t st = check_common("diagmm_plan", b, n, h, mode >= 3 ? 1 : d, w, w_upper,
                                       dilation, in_dtype, out_dtype, &p, &de, &be);
     if (st != DIAGMM_OK) return st;
+    if (mode == 6) {
+        if (out_dtype != in_dtype)
+            return fail(DIAGMM_ERR_DTYPE, "diagmm_plan: dropout has one dtype");
+        const void* al = reinterpret_cast<const void*>(uintptr_t(256));   // aligned tensors
+        const bool wide = !force_simple() && dropout_wide(p, in_dtype, al, al, al);
+        std::memset(out, 0, sizeof *out);
+        std::snprintf(out->kernel, sizeof out->kernel, "%s",
+                      wide ? "dropout_wide" : "dropout_elems");
+        out->workgroups = out->tiles = dropout_workgroups(p, in_dtype, wide);
+        out->slots_per_tile = dropout_chunk(in_dtype, wide);
+        out->threads = 256;
+        out->residues = 1;
+        return ok();
+    }
     if (mode == 4) {
         if (out_dtype != in_dtype)
             return fail(DIAGMM_ERR_DTYPE, "diagmm_plan: the softmax backward has one dtype");

@@ -45,6 +45,16 @@ hipError_t launch_softmax_masked(const void* scores, void* probs, const float* k
                                  const Problem& p, float scale, float mask_value, int in_dt,
                                  int out_dt, hipStream_t stream);
 
+// Dropout on a band with caller-drawn uniforms (one dtype for probs and out): 16-byte
+// pieces when `wide` (dropout_wide), else element by element.
+bool dropout_supported(const Problem& p);
+bool dropout_wide(const Problem& p, int dt, const void* probs, const void* rand,
+                  const void* out);
+int64_t dropout_chunk(int dt, bool wide);   // band elements per workgroup
+int64_t dropout_workgroups(const Problem& p, int dt, bool wide);
+hipError_t launch_dropout(const void* probs, const float* rand, void* out, const Problem& p,
+                          float drop_p, int dt, bool wide, hipStream_t stream);
+
 // qk on MFMA (f16 / bf16 inputs, d in {32, 64, 128}, 16-byte aligned pointers).
 constexpr int kQkRows = 128;                 // rows per tile
 constexpr int64_t kQkLdsBytes = 160 * 1024;  // one workgroup per compute unit

@@ -37,7 +37,7 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for want in ("diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax",
                  "diagmm_banded_softmax_backward", "diagmm_banded_softmax_masked",
-                 "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
+                 "diagmm_banded_dropout", "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
                  "diagmm_plan"):
         assert want in names
 
@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dm.diagmm_abi_version() == 4
+    assert dm.diagmm_abi_version() == 5
     seen = set()
     for st in range(7):
         s = lib.diagmm_status_string(st).decode()
@@ -104,6 +104,18 @@ def test_validation_errors_are_reported_without_launching(lib):
     assert ms(P_, P_ + 2, M_, 1, 8, 1, 2, 2, 0, 1.0, -1e4, 1, 1, None) == ERR_ALIAS
     assert ms(P_, O_, O_ + 16, 1, 8, 1, 2, 2, 0, 1.0, -1e4, 1, 1, None) == ERR_ALIAS
     assert "diagmm_banded_softmax_masked" in lib.diagmm_last_error().decode()
+    dr = lib.diagmm_banded_dropout
+    R_ = FAKE + (1 << 38)
+    assert dr(P_, 0, O_, 1, 8, 1, 2, 2, 0, 0.1, 1, None) == ERR_NULL
+    assert dr(P_, R_, 0, 1, 8, 1, 2, 2, 0, 0.1, 1, None) == ERR_NULL
+    for bad_p in (1.0, -0.1, float("nan")):
+        assert dr(P_, R_, O_, 1, 8, 1, 2, 2, 0, bad_p, 1, None) == ERR_SHAPE
+    assert dr(P_, R_, O_, 1, 8, 1, 2, 2, -1, 0.1, 1, None) == ERR_SHAPE
+    assert dr(P_, R_, O_, 1, 8, 1, 2, 2, 0, 0.1, 3, None) == ERR_DTYPE
+    assert dr(P_, R_, P_ + 2, 1, 8, 1, 2, 2, 0, 0.1, 1, None) == ERR_ALIAS   # partial overlap
+    assert dr(P_, R_, R_ + 156, 1, 8, 1, 2, 2, 0, 0.1, 1, None) == ERR_ALIAS  # rand's last one
+    assert dr(P_, O_ - 150, O_, 1, 8, 1, 2, 2, 0, 0.1, 1, None) == ERR_ALIAS  # rand's tail
+    assert "diagmm_banded_dropout" in lib.diagmm_last_error().decode()
 
 
 def test_empty_problems_are_noops(lib):
@@ -114,6 +126,7 @@ def test_empty_problems_are_noops(lib):
     assert lib.diagmm_banded_softmax_backward(0, 0, 0, 0, 8, 3, 2, 2, 0, 1.0, 1, None) == OK
     assert lib.diagmm_banded_softmax_masked(0, 0, 0, 0, 8, 3, 2, 2, 0, 1.0, -1e4, 1, 1,
                                             None) == OK
+    assert lib.diagmm_banded_dropout(0, 0, 0, 1, 0, 3, 2, 2, 0, 0.5, 2, None) == OK
     assert lib.diagmm_last_error().decode() == ""
 
 
@@ -127,14 +140,14 @@ def test_python_binding_rejects_bad_tensors():
         dm.diagmm_pv(cpu, cpu, -1)
 
 
-@pytest.mark.parametrize("mode", ["qk", "pv", "pvT", "softmax", "softmax_bwd"])
+@pytest.mark.parametrize("mode", ["qk", "pv", "pvT", "softmax", "softmax_bwd", "dropout"])
 @pytest.mark.parametrize("shape", [(1, 4096, 12, 64, 256, 256, 0), (1, 4096, 12, 64, 256, 256, 3),
                                    (12, 4096, 12, 64, 256, 0, 0), (1, 32768, 12, 64, 4096, 4096, 0),
                                    (1, 512, 1, 64, 32, 32, 0), (2, 37, 3, 24, 5, 0, 2)])
 def test_plans_are_consistent(lib, mode, shape):
     b, n, h, d, w, wu, dil = shape
     dt = torch.bfloat16 if wu == 0 else torch.float16
-    odt = torch.float32 if wu == 0 and mode != "softmax_bwd" else dt
+    odt = torch.float32 if wu == 0 and mode not in ("softmax_bwd", "dropout") else dt
     p = dm.diagmm_plan(mode, b, n, h, d, w, wu, dil, dt, odt)
     assert p["kernel"]
     assert p["threads"] in (64, 128, 256, 512, 1024)
@@ -164,3 +177,18 @@ def test_softmax_bwd_plan_picks_lanes_by_row_length(lib):
     with pytest.raises(dm.DiagmmError) as e:
         dm.diagmm_plan("softmax_bwd", 1, 64, 1, 1, 8, 8, 0, torch.float16, torch.float32)
     assert e.value.status == ERR_DTYPE
+
+
+def test_dropout_plan_covers_the_band(lib):
+    """One workgroup per 256 x 4 pieces of 16 bytes: 8192 elements of a 16-bit type,
+    4096 of float32; rows shorter than a piece go element by element."""
+    p = dm.diagmm_plan("dropout", 1, 4096, 12, 1, 256, 256, 0, torch.float16)
+    assert p["kernel"] == "dropout_wide" and p["slots_per_tile"] == 8192
+    assert p["workgroups"] == -(-4096 * 12 * 513 // 8192)
+    p = dm.diagmm_plan("dropout", 1, 4096, 12, 1, 256, 256, 3, torch.float32)
+    assert p["slots_per_tile"] == 4096 and p["workgroups"] == -(-4096 * 12 * 513 // 4096)
+    p = dm.diagmm_plan("dropout", 2, 50, 3, 1, 3, 3, 0, torch.float16)   # K = 7 < 8
+    assert p["kernel"] == "dropout_elems" and p["workgroups"] == -(-2 * 50 * 3 * 7 // 1024)
+    with pytest.raises(dm.DiagmmError) as e:
+        dm.diagmm_plan("softmax_masked", 1, 64, 1, 1, 8, 8, 0, torch.float16)
+    assert e.value.status == ERR_UNSUPPORTED

@@ -73,3 +73,50 @@ def test_banded_attention_low_precision_tracks_f32(dt):
     for name, lo, hi in zip(("out", "dq", "dk", "dv"), grads[dt], grads[torch.float32]):
         err = ((lo - hi).abs().max() / hi.abs().max()).item()
         assert err <= tol, f"{dt} {name}: normwise deviation from f32 {err:.3e}"
+
+
+def _dense_keep(rand, n, w, wu, s, p):
+    """Dense [b, h, n, n] dropout factors from a band of uniforms: (rand > p) / (1 - p)
+    at key i + (kk - w) s of row i, 0 off the window."""
+    b, _, h, K = rand.shape
+    p = float(torch.tensor(p, dtype=torch.float32))   # the float32 p the kernels compare
+    D = torch.zeros(b, h, n, n, dtype=torch.float64)
+    i = torch.arange(n)
+    for kk in range(K):
+        j = i + (kk - w) * s
+        ok = (j >= 0) & (j < n)
+        keep = (rand[:, :, :, kk] > p).double() / (1 - p)
+        D[:, :, i[ok], j[ok]] = keep.permute(0, 2, 1)[:, :, ok]
+    return D
+
+
+@pytest.mark.parametrize("shape", [(1, 200, 2, 32, 16, 16, 0), (1, 170, 3, 32, 12, 9, 2)])
+def test_banded_attention_with_dropout_matches_dense_autograd(shape):
+    """Dropout between the softmax and pv: the dense reference multiplies the masked
+    softmax by the same keep factors (rand > p) / (1 - p) before the product with V."""
+    from sliding_window_attention_diagmm_amd.attention import banded_attention
+    b, n, h, d, w, wu, dil = shape
+    p = 0.2
+    g_ = datagen.rng(740 + n)
+    q, k, v, gout = (datagen.normal(g_, (b, n, h, d), "f32") for _ in range(4))
+    rand = datagen.uniform(g_, (b, n, h, w + wu + 1))
+    scale = 1.0 / math.sqrt(d)
+    qc, kc, vc = (t_.cuda().requires_grad_(True) for t_ in (q, k, v))
+    o = banded_attention(qc, kc, vc, w, wu, dil, dropout_p=p, dropout_rand=rand.cuda())
+    o.backward(gout.cuda())
+    D = _dense_keep(rand, n, w, wu, max(dil, 1), p)
+    qd, kd, vd = (t_.double().requires_grad_(True) for t_ in (q, k, v))
+    mask = _selected(n, w, wu, max(dil, 1))
+    sc = torch.einsum("bihd,bjhd->bhij", qd, kd) * scale
+    pr = torch.softmax(sc.masked_fill(~mask, float("-inf")), -1) * D
+    ro = torch.einsum("bhij,bjhd->bihd", pr, vd)
+    (ro * gout.double()).sum().backward()
+    for name, got, ref in (("out", o, ro.detach()), ("dq", qc.grad, qd.grad),
+                           ("dk", kc.grad, kd.grad), ("dv", vc.grad, vd.grad)):
+        err = _normwise(got.detach(), ref)
+        assert err <= 1e-5, f"{name}: normwise error {err:.3e}"
+    # p = 0 with any uniforms in (0, 1) is the attention without dropout
+    o0 = banded_attention(qc.detach(), kc.detach(), vc.detach(), w, wu, dil)
+    o1 = banded_attention(qc.detach(), kc.detach(), vc.detach(), w, wu, dil, dropout_p=0.0,
+                          dropout_rand=rand.cuda())
+    assert torch.equal(o0, o1)

@@ -640,6 +640,10 @@ def test_row_list_equals_full_computation():
     full_sm = oracle.softmax(P, w, wu, dil, 0.5).reshape(2 * n, 2, -1)
     assert torch.equal(oracle.softmax(P.reshape(2 * n, 2, -1)[bi], w, wu, dil, 0.5, n=n,
                                       rows=rows), full_sm[bi])
+    R = datagen.uniform(g, P.shape)
+    full_dr = oracle.dropout(P, R, w, wu, dil, p=0.3).reshape(2 * n, 2, -1)
+    assert torch.equal(oracle.dropout(P.reshape(2 * n, 2, -1)[bi], R.reshape(2 * n, 2, -1)[bi],
+                                      w, wu, dil, p=0.3, n=n, rows=rows), full_dr[bi])
 
 
 def test_sample_rows_cover_edges():

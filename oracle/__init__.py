@@ -72,6 +72,8 @@ def _load():
             lib.oracle_softmax_bwd.argtypes = [vp, vp, vp] + [i64] * 6 + [cd, ci, ci, vp, i64, ci]
             lib.oracle_dropout.argtypes = [vp, vp, vp] + [i64] * 6 + [ctypes.c_float, ci, ci, vp, i64,
                                            ci]
+            lib.oracle_attention.argtypes = [vp, vp, vp, vp] + [i64] * 7 + [cd, ci, ci, vp, i64,
+                                                                              ci]
             lib.oracle_softmax_masked.argtypes = [vp, vp, vp] + [i64] * 6 + [cd, cd, ci, ci, vp,
                                                                                  i64, ci]
             for f in (lib.oracle_qk, lib.oracle_pv, lib.oracle_pvT, lib.oracle_softmax):
@@ -160,6 +162,29 @@ def pvT(band, x, w, w_upper, dilation=0, out_dtype=None, rows=None, threads=None
     """Transposed band times X: [b, n, h, d].  The band and X are always full; a row
     list selects output rows j."""
     return _pv_like(_load().oracle_pvT, band, x, w, w_upper, dilation, out_dtype, rows, threads)
+
+
+def attention(q, k, v, w, w_upper, dilation=0, scale=1.0, out_dtype=None, rows=None,
+              threads=None):
+    """Sliding-window attention, one row at a time in double: scores on the window's
+    in-range diagonals, their softmax, and the probability-weighted sum of V rows.
+    q, k, v are full [b, n, h, d] tensors of one dtype; the result is [b, n, h, d], or
+    [len(rows), h, d] for a list of flattened positions b * n + i."""
+    lib = _load()
+    q, k, v = _check(q, "q"), _check(k, "k"), _check(v, "v")
+    if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype):
+        raise ValueError("oracle.attention: q, k, v differ in shape or dtype")
+    b, n, h, d = q.shape
+    out_dtype = out_dtype or q.dtype
+    rt, rp, nr = _rows(rows)
+    shape = (b, n, h, d) if rt is None else (nr, h, d)
+    out = torch.empty(shape, dtype=out_dtype)
+    st = lib.oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), b, n, h, d, w, w_upper,
+                              dilation, float(scale), _CODE[q.dtype], _CODE[out_dtype], rp, nr,
+                              threads or default_threads())
+    if st:
+        raise ValueError(f"oracle.attention: bad arguments ({st})")
+    return out
 
 
 def softmax(scores, w, w_upper, dilation=0, scale=1.0, out_dtype=None, n=None, rows=None,

@@ -40,6 +40,7 @@
  * type (OR_F64 keeps the unrounded double, for tolerance checks).
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -436,4 +437,62 @@ int oracle_dropout(const void* probs, const float* rand, void* out, int64_t b, i
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------ attention
+ * Sliding-window attention with the band never stored: the forward function of [TVM]
+ * post 6 (scores on the window's diagonals), the softmax of the issue 2096 repro over
+ * them (scale, max, subtract, exp, sum, divide), and the backward function with
+ * transpose_t1 = 0 applied to the probabilities - one row at a time, in double:
+ *     x_k = scale * sum_c Q[bb,i,hh,c] K[bb,j,hh,c],   j = i + (k - w) * s in [0, n),
+ *     P_k = exp(x_k - max x) / sum exp(x - max x),
+ *     out[bb,i,hh,c] = sum_k P_k V[bb,j,hh,c].
+ * Q, K and V are full tensors; a row list selects the output positions (packed). */
+int oracle_attention(const void* q, const void* kt, const void* v, void* out, int64_t b,
+                     int64_t n, int64_t h, int64_t d, int64_t w, int64_t wu, int64_t dil,
+                     double scale, int in_dt, int out_dt, const int64_t* rows, int64_t nrows,
+                     int nthreads)
+{
+    int bad = or_check(b, n, h, d, w, wu, dil, in_dt, out_dt);
+    if (bad) return bad;
+    const int64_t K = w + wu + 1, s = or_stride(dil);
+    if (!rows) nrows = b * n;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t bi = or_row(rows, r), bb = bi / n, i = bi % n;
+        double* x = (double*)malloc((size_t)K * sizeof(double));
+        if (!x) { failed = 1; continue; }
+        for (int64_t hh = 0; hh < h; ++hh) {
+            const int64_t qrow = ((bb * n + i) * h + hh) * d;
+            double mx = -INFINITY;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t j = i + (k - w) * s;
+                x[k] = -INFINITY;
+                if (j < 0 || j >= n) continue;
+                double acc = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    acc += or_load(q, qrow + c, in_dt) *
+                           or_load(kt, ((bb * n + j) * h + hh) * d + c, in_dt);
+                x[k] = scale * acc;
+                if (x[k] > mx) mx = x[k];
+            }
+            double sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                x[k] = (x[k] == -INFINITY) ? 0.0 : exp(x[k] - mx);
+                sum += x[k];
+            }
+            for (int64_t c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const int64_t j = i + (k - w) * s;
+                    if (j < 0 || j >= n) continue;
+                    acc += (x[k] / sum) * or_load(v, ((bb * n + j) * h + hh) * d + c, in_dt);
+                }
+                or_store(out, (r * h + hh) * d + c, out_dt, acc);
+            }
+        }
+        free(x);
+    }
+    return failed ? 3 : 0;
 }

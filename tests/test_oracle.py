@@ -650,3 +650,67 @@ def test_sample_rows_cover_edges():
     rows = datagen.sample_rows(32768, 4096)
     assert len(rows) == 64 == len(set(rows.tolist()))
     assert {0, 4095, 32768 - 4096, 32767} <= set(rows.tolist())
+
+
+# ------------------------------------------------------------ fused attention pins
+# attention = the window's scores, their softmax and the weighted sum of V rows in one
+# pass.  Pins: torch's float64 softmax attention over dense rows with the unselected
+# diagonals at -inf (a library routine), closed forms (constant V rows, a one-slot
+# window, zero queries give window means), and agreement with the three-step oracle.
+
+def _dense_attention(q, k, v, w, wu, dil, scale):
+    n = q.shape[1]
+    i = torch.arange(n)[:, None]
+    j = torch.arange(n)[None, :]
+    off = j - i
+    s = max(dil, 1)
+    sel = (off % s == 0) & (off >= -w * s) & (off <= wu * s)
+    sc = torch.einsum("bihd,bjhd->bhij", q.double(), k.double()) * scale
+    p = torch.softmax(sc.masked_fill(~sel, float("-inf")), -1)
+    return torch.einsum("bhij,bjhd->bihd", p, v.double())
+
+
+@pytest.mark.parametrize("shape", [(1, 40, 2, 8, 5, 5, 0), (2, 33, 1, 16, 4, 0, 0),
+                                   (1, 50, 2, 8, 6, 3, 3), (1, 9, 1, 4, 20, 20, 0),
+                                   (1, 61, 1, 8, 7, 2, 9), (1, 1, 1, 4, 3, 3, 0)])
+def test_attention_matches_dense_softmax_attention(shape):
+    b, n, h, d, w, wu, dil = shape
+    g = datagen.rng(900 + n)
+    q, k, v = (datagen.normal(g, (b, n, h, d), "f32") for _ in range(3))
+    got = oracle.attention(q, k, v, w, wu, dil, scale=0.7, out_dtype=torch.float64)
+    ref = _dense_attention(q, k, v, w, wu, dil, 0.7)
+    assert torch.allclose(got, ref, rtol=0, atol=1e-12)
+    three = oracle.pv(oracle.softmax(oracle.qk(q.double(), k.double(), w, wu, dil, 0.0),
+                                     w, wu, dil, 0.7), v.double(), w, wu, dil)
+    assert torch.allclose(got, three, rtol=0, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    b, n, h, d, w, wu, dil = 1, 30, 2, 8, 4, 6, 2
+    g = datagen.rng(950)
+    q, k = (datagen.normal(g, (b, n, h, d), "f32") for _ in range(2))
+    v = datagen.normal(g, (b, n, h, d), "f32")
+    # constant value rows: every output row is that row
+    c = datagen.normal(g, (1, 1, h, d), "f32").expand(b, n, h, d).contiguous()
+    got = oracle.attention(q, k, c, w, wu, dil, 0.5, out_dtype=torch.float64)
+    assert torch.allclose(got, c.double().expand_as(got), rtol=0, atol=1e-14)
+    # a one-slot window attends the diagonal only: the output is V exactly
+    assert torch.equal(oracle.attention(q, k, v, 0, 0, dil, 0.5, out_dtype=torch.float64),
+                       v.double())
+    # zero queries: uniform weights, the mean of the in-range V rows
+    z = torch.zeros_like(q)
+    got = oracle.attention(z, k, v, w, wu, dil, 0.5, out_dtype=torch.float64)
+    s = max(dil, 1)
+    for i in range(n):
+        js = [i + o * s for o in range(-w, wu + 1) if 0 <= i + o * s < n]
+        assert torch.allclose(got[0, i], v[0, js].double().mean(0), rtol=0, atol=1e-14)
+
+
+def test_attention_row_list_equals_full():
+    b, n, h, d, w, wu, dil = 2, 40, 2, 8, 5, 3, 3
+    g = datagen.rng(960)
+    q, k, v = (datagen.normal(g, (b, n, h, d), "f16") for _ in range(3))
+    rows = np.array([0, 1, 39, 40, 41, 79])
+    full = oracle.attention(q, k, v, w, wu, dil, 0.3).reshape(b * n, h, d)
+    assert torch.equal(oracle.attention(q, k, v, w, wu, dil, 0.3, rows=rows),
+                       full[torch.from_numpy(rows)])

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DIAGMM_ABI_VERSION 5
+#define DIAGMM_ABI_VERSION 6
 
 typedef enum {
     DIAGMM_F32 = 0,
@@ -181,6 +181,23 @@ diagmm_status_t diagmm_banded_dropout(const void* probs, const float* rand, void
                                       int64_t w_upper, int64_t dilation, float p,
                                       diagmm_dtype_t dtype, void* stream);
 
+/*
+ * diagmm_banded_attention - sliding-window attention in one pass, the band never written:
+ *   out[bb,i,hh,:] = sum_k P_k V[bb,j_k,hh,:],   j_k = i + (k - w) * s,
+ *   P = softmax over the in-range slots k of x_k = scale * sum_c Q[bb,i,hh,c] K[bb,j_k,hh,c]
+ * - diagmm_qk, diagmm_banded_softmax and diagmm_pv composed ([TVM] post 6 forward and
+ * transpose_t1 = 0 functions, the issue 2096 softmax recipe), with the scores and
+ * probabilities kept in float32 registers (the probabilities enter the second product
+ * rounded to the input dtype, as the three-call path stores them).  q, k, v and out are
+ * [b][n][h][d] of one dtype: f16 or bf16 with d in {32, 64, 128} and 16-byte aligned
+ * pointers, else DIAGMM_ERR_UNSUPPORTED (use the three calls).  out overlapping q, k or
+ * v is DIAGMM_ERR_ALIAS.  Errors otherwise as for the other calls.
+ */
+diagmm_status_t diagmm_banded_attention(const void* q, const void* k, const void* v, void* out,
+                                        int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,
+                                        int64_t w_upper, int64_t dilation, float scale,
+                                        diagmm_dtype_t dtype, void* stream);
+
 /* Static text for a status code. */
 const char* diagmm_status_string(diagmm_status_t status);
 
@@ -196,10 +213,11 @@ int diagmm_abi_version(void);
  * (rows per tile, slots per tile), how many tiles and workgroups, the LDS bytes per
  * workgroup, and how many residue classes the dilation splits the rows into.
  * mode: 0 = qk, 1 = pv, 2 = pvT, 3 = banded softmax, 4 = banded softmax backward,
- * 6 = banded dropout (the timing tags; 5, the masked softmax, has no plan).  Modes 4 and
- * 6 are planned for 16-byte aligned tensors, and out_dtype must equal in_dtype; for 6
- * rows_per_tile is 0, slots_per_tile the band elements a workgroup takes and tiles the
- * workgroups.  Returns DIAGMM_ERR_SHAPE /
+ * 6 = banded dropout, 7 = attention in one pass (the timing tags; 5, the masked softmax,
+ * has no plan).  Modes 4, 6 and 7 are planned for 16-byte aligned tensors, and out_dtype
+ * must equal in_dtype; for 6 rows_per_tile is 0, slots_per_tile the band elements a
+ * workgroup takes and tiles the workgroups; for 7 a tile is 64 rows of one residue class
+ * with keys staged 64 at a time (slots_per_tile), one workgroup per tile.  Returns DIAGMM_ERR_SHAPE /
  * DIAGMM_ERR_DTYPE for invalid arguments, as the compute calls would.
  */
 typedef struct {
@@ -227,7 +245,7 @@ diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d
  * kernel launches by this library records a pair of HIP events at the kernel's own start
  * and end on the stream it is launched on (hipExtLaunchKernel), tagged with the entry
  * point (the diagmm_plan modes: 0 qk, 1 pv, 2 pvT, 3 banded softmax, 4 its backward;
- * 5 the masked softmax, 6 dropout); further launches
+ * 5 the masked softmax, 6 dropout, 7 attention in one pass); further launches
  * run untimed.  One session at a time, process-wide, on one device (the events are made
  * on the device current at diagmm_timing_begin; launches on another device are not to be
  * timed).  diagmm_timing_read waits for the recorded kernels and writes, for the first

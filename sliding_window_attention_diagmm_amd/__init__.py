@@ -24,7 +24,7 @@ import os
 import torch
 
 __all__ = ["diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax",
-           "diagmm_banded_softmax_backward", "diagmm_banded_dropout", "diagmm_plan",
+           "diagmm_banded_softmax_backward", "diagmm_banded_dropout", "diagmm_banded_attention", "diagmm_plan",
            "diagmm_timing_begin", "diagmm_timing_end", "diagmm_timing_read",
            "diagmm_abi_version", "library_path", "load", "DiagmmError"]
 
@@ -33,7 +33,7 @@ _LIB_PATH = os.path.join(_HERE, "libdiagmm.so")
 
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 MODES = {"qk": 0, "pv": 1, "pvT": 2, "softmax": 3, "softmax_bwd": 4, "softmax_masked": 5,
-         "dropout": 6}
+         "dropout": 6, "attention": 7}
 
 
 class DiagmmError(RuntimeError):
@@ -81,6 +81,8 @@ def load() -> ctypes.CDLL:
     lib.diagmm_banded_softmax_masked.restype = ci
     lib.diagmm_banded_dropout.argtypes = [vp, vp, vp] + [i64] * 6 + [f32, ci, vp]
     lib.diagmm_banded_dropout.restype = ci
+    lib.diagmm_banded_attention.argtypes = [vp, vp, vp, vp] + [i64] * 7 + [f32, ci, vp]
+    lib.diagmm_banded_attention.restype = ci
     lib.diagmm_status_string.argtypes = [ci]
     lib.diagmm_status_string.restype = ctypes.c_char_p
     lib.diagmm_last_error.argtypes = []
@@ -273,6 +275,28 @@ def diagmm_banded_dropout(probs, rand, w, w_upper=None, dilation=0, p=0.1, out=N
     st = lib.diagmm_banded_dropout(pr.data_ptr(), rd.data_ptr(), res.data_ptr(), b, n, h, w,
                                    w_upper, dilation, float(p), _DT[pr.dtype],
                                    _stream(pr.device))
+    if st:
+        _raise(lib, st)
+    return res
+
+
+def diagmm_banded_attention(q, k, v, w, w_upper=None, dilation=0, scale=None, out=None):
+    """Sliding-window attention in one pass: ``softmax(scale * Q K^T)`` over the window's
+    in-range diagonals times V, without writing the band ([b, n, h, d] in and out, f16 or
+    bf16, d in {32, 64, 128}).  ``scale`` defaults to 1 / sqrt(d)."""
+    lib = load()
+    w, w_upper, dilation = _window(w, w_upper, dilation)
+    q, k, v = _dense(q, "q"), _dense(k, "k"), _dense(v, "v")
+    if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype
+            and q.device == k.device == v.device):
+        raise ValueError("q, k and v must have the same shape, dtype and device")
+    b, n, h, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    res = _out(out, q.shape, q.dtype, q.device)
+    st = lib.diagmm_banded_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), res.data_ptr(),
+                                     b, n, h, d, w, w_upper, dilation, float(scale),
+                                     _DT[q.dtype], _stream(q.device))
     if st:
         _raise(lib, st)
     return res

@@ -332,17 +332,59 @@ diagmm_status_t diagmm_banded_dropout(const void* probs, const float* rand, void
                                        static_cast<hipStream_t>(stream)));
 }
 
+diagmm_status_t diagmm_banded_attention(const void* q, const void* k, const void* v, void* out,
+                                        int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,
+                                        int64_t w_upper, int64_t dilation, float scale,
+                                        diagmm_dtype_t dtype, void* stream) {
+    const char* fn = "diagmm_banded_attention";
+    Problem p;
+    int64_t de, be;
+    diagmm_status_t st = check_common(fn, b, n, h, d, w, w_upper, dilation, dtype, dtype, &p,
+                                      &de, &be);
+    if (st != DIAGMM_OK) return st;
+    if (p.rows() * p.h == 0) return ok();
+    if (!q || !k || !v || !out) return fail(DIAGMM_ERR_NULL, "%s: null pointer", fn);
+    const int64_t bytes = de * static_cast<int64_t>(elem_size(dtype));
+    for (const void* in : {q, k, v})
+        if (overlaps(out, bytes, in, bytes))
+            return fail(DIAGMM_ERR_ALIAS, "%s: out overlaps q, k or v", fn);
+    if (!attention_supported(p, dtype, q, k, v, out))
+        return fail(DIAGMM_ERR_UNSUPPORTED, "%s: needs f16 or bf16, d in {32, 64, 128} and "
+                    "16-byte aligned tensors", fn);
+    timing_set_op(kOpAttention);
+    return launched(fn, launch_attention(q, k, v, out, p, scale, dtype,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,
                             int64_t w_upper, int64_t dilation, diagmm_dtype_t in_dtype,
                             diagmm_dtype_t out_dtype, diagmm_plan_t* out) {
     if (!out) return fail(DIAGMM_ERR_NULL, "diagmm_plan: null plan pointer");
-    if (mode < 0 || mode > 6 || mode == 5)
+    if (mode < 0 || mode > 7 || mode == 5)
         return fail(DIAGMM_ERR_UNSUPPORTED, "diagmm_plan: mode %d", mode);
     Problem p;
     int64_t de, be;
-    diagmm_status_t st = check_common("diagmm_plan", b, n, h, mode >= 3 ? 1 : d, w, w_upper,
+    diagmm_status_t st = check_common("diagmm_plan", b, n, h, (mode >= 3 && mode != 7) ? 1 : d, w, w_upper,
                                       dilation, in_dtype, out_dtype, &p, &de, &be);
     if (st != DIAGMM_OK) return st;
+    if (mode == 7) {
+        if (out_dtype != in_dtype)
+            return fail(DIAGMM_ERR_DTYPE, "diagmm_plan: attention has one dtype");
+        const void* al = reinterpret_cast<const void*>(uintptr_t(256));   // aligned tensors
+        if (!attention_supported(p, in_dtype, al, al, al, al))
+            return fail(DIAGMM_ERR_UNSUPPORTED, "diagmm_plan: attention needs f16 or bf16 and "
+                        "d in {32, 64, 128}");
+        std::memset(out, 0, sizeof *out);
+        std::snprintf(out->kernel, sizeof out->kernel, "attn_fwd_%s_d%lld",
+                      in_dtype == DIAGMM_F16 ? "f16" : "bf16", static_cast<long long>(d));
+        out->rows_per_tile = 64;
+        out->slots_per_tile = 64;
+        out->workgroups = out->tiles = attention_workgroups(p);
+        out->threads = 256;
+        out->lds_bytes = 2 * 64 * 2 * d;
+        out->residues = p.s;
+        return ok();
+    }
     if (mode == 6) {
         if (out_dtype != in_dtype)
             return fail(DIAGMM_ERR_DTYPE, "diagmm_plan: dropout has one dtype");

@@ -1,0 +1,335 @@
+// Sliding-window attention in one pass, the band never written to HBM:
+//
+//   out[i] = sum_k P_k V[j_k],   P = softmax(scale * S) over the in-range slots,
+//   S_k = Q[i] . K[j_k],         j_k = i + (k - w) * s
+//
+// (TVM Discuss, "Developing a faster schedule for Longformer's kernel", post 6: the
+// forward function and the backward function with transpose_t1 = 0; csarofeen/pytorch
+// issue 2096, first fusion repro: the softmax recipe between them).  The three-call path
+// stores the scores and the probabilities, two band tensors of 2 (w + w_upper + 1) bytes
+// per query row and head; this kernel keeps them in registers and reads only Q, K and V.
+//
+// Work.  Within one residue class of the dilation the window is an undilated band (rows
+// t = 0 .. len - 1 of the class attend class keys t - w .. t + w_upper).  A workgroup of
+// four waves takes 64 consecutive class rows of one (batch, head); wave v owns rows
+// 16 v .. 16 v + 15.  It walks the keys its rows reach, t0 - w .. t0 + 63 + w_upper, in
+// blocks of 64 staged in LDS, with an online softmax: per block the running row maximum
+// is raised, the accumulators and the running sums are rescaled by exp(old - new), and
+// the block's probabilities are added in.
+//
+// MFMA layouts (v_mfma_f32_16x16x32_{f16,bf16}; A lanes hold a row and 8 K-values, B
+// lanes a column and 8 K-values, C lanes a column and 4 rows).  Scores are computed
+// transposed, S^T = K Q^T: A is 16 key rows read from LDS, B this wave's 16 query rows
+// held in registers, and C gives lane (column = query, group g) four keys.  Two such key
+// tiles per 32 keys take the key rows 8 g + e and 8 g + 4 + e (e = 0..3) for A row 4 g + e,
+// so lane group g ends up with the 8 consecutive keys 8 g .. 8 g + 7 of its query - in
+// the order the product with V needs as its B operand.  out^T = V^T P^T then takes
+// A = V^T (16 channels x 8 consecutive keys) through gfx950's transposing LDS reads of the
+// row-major V block, as the pv kernel does, and C gives lane (query, g) channels
+// 4 g .. 4 g + 3 of each 16-channel block - all of one query row, so the online
+// softmax's rescaling is per lane.  Row maxima and sums combine the four lane groups of a
+// query with two cross-lane steps.
+#include "launch.hpp"
+#include "ring.hpp"
+
+namespace diagmm {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <class In> struct Mfma;
+template <> struct Mfma<F16> {
+    using V = f16x8;
+    __device__ __forceinline__ static f32x4 run(V a, V b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<BF16> {
+    using V = bf16x8;
+    __device__ __forceinline__ static f32x4 run(V a, V b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+constexpr int kThreads = 256;
+constexpr int kRows = 64;     // class rows per workgroup
+constexpr int kKeys = 64;     // keys per LDS block
+
+struct AttnArgs {
+    int64_t n, h, w, wu, s;
+    int64_t cls_q, cls_m;     // n = cls_q s + cls_m: class r has cls_q + (r < cls_m) rows
+    int64_t nqb_hi, nqb_lo;   // 64-row blocks of a long / short class
+    int64_t per_head;         // workgroups per (batch, head)
+    int64_t groups;           // workgroups in the grid
+    float scale_log2;         // scale * log2(e)
+};
+
+// K block: row r (key), 16-byte piece ch at r * 2D + 16 (ch ^ sw(r)); the swizzle puts the
+// eight rows 8 (m / 4) + (m % 4) (+ 4) read by lanes m = 0..7 of a score tile on distinct
+// 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int kpiece(int r, int ch) {
+    const int hi = (r >> 3) & 1;
+    const int sw = D == 32 ? hi : D == 64 ? (((r >> 1) & 1) | (hi << 1)) : ((r & 3) | (hi << 2));
+    return r * (2 * D) + 16 * (ch ^ sw);
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b, F16) {
+    return static_cast<uint32_t>(F16::from_f32(a)) | (static_cast<uint32_t>(F16::from_f32(b)) << 16);
+}
+__device__ __forceinline__ uint32_t pack2(float a, float b, BF16) {
+    return static_cast<uint32_t>(BF16::from_f32(a)) | (static_cast<uint32_t>(BF16::from_f32(b)) << 16);
+}
+
+template <class In, int D>
+__global__ void __launch_bounds__(kThreads)
+attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __restrict__ k,
+                const typename In::T* __restrict__ v, typename In::T* __restrict__ out,
+                AttnArgs a) {
+    using ST = typename In::T;
+    using V = typename Mfma<In>::V;
+    constexpr int kPieces = D / 8;                       // 16-byte pieces per row
+    constexpr int kStage = kKeys * kPieces / kThreads;   // pieces per thread per tensor
+    constexpr int kQk = D / 32;                          // MFMA K-steps over the channels
+    constexpr int kCb = D / 16;                          // 16-channel output blocks
+    __shared__ __attribute__((aligned(16))) unsigned char klds[kKeys * 2 * D];
+    __shared__ __attribute__((aligned(16))) unsigned char vlds[kKeys * 2 * D];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+
+    // ---- workgroup -> (batch, head, residue class, row block), XCD-aware: the dispatcher
+    // deals workgroups to the 8 XCDs in turn, so XCD x gets a contiguous range of ids.
+    int64_t id;
+    {
+        const int64_t g = a.groups, per = g / 8, rem = g % 8;
+        const int64_t x = blockIdx.x % 8, loc = blockIdx.x / 8;
+        id = x * per + (x < rem ? x : rem) + loc;
+    }
+    const int64_t bh = id / a.per_head;
+    int64_t rest = id - bh * a.per_head;
+    int64_t r, qb;
+    if (rest < a.cls_m * a.nqb_hi) {
+        r = rest / a.nqb_hi;
+        qb = rest - r * a.nqb_hi;
+    } else {
+        rest -= a.cls_m * a.nqb_hi;
+        r = a.cls_m + rest / a.nqb_lo;
+        qb = rest - (r - a.cls_m) * a.nqb_lo;
+    }
+    const int64_t bb = bh / a.h, hh = bh - bb * a.h;
+    const int len = static_cast<int>(a.cls_q + (r < a.cls_m ? 1 : 0));
+    const int t0 = static_cast<int>(qb) * kRows;
+    // element offset of class row t: base + t * step
+    const int64_t base = ((bb * a.n + r) * a.h + hh) * D;
+    const int64_t step = a.s * a.h * D;
+
+    // ---- this lane's query row as the B operand of S^T (channels 32 kk + 8 grp .. +7)
+    const int tq = t0 + 16 * wv + col;
+    const int tq_ld = tq < len ? tq : len - 1;
+    V qop[kQk];
+#pragma unroll
+    for (int kk = 0; kk < kQk; ++kk)
+        qop[kk] = *reinterpret_cast<const V*>(q + base + int64_t(tq_ld) * step + 32 * kk + 8 * grp);
+
+    const int w = static_cast<int>(a.w), wu = static_cast<int>(a.wu);
+    const int u_lo = t0 - w > 0 ? t0 - w : 0;
+    const int last_q = (t0 + kRows - 1 < len - 1) ? t0 + kRows - 1 : len - 1;
+    const int u_hi = (last_q + wu < len - 1) ? last_q + wu : len - 1;   // inclusive
+    const int nblk = (u_hi - u_lo + kKeys) / kKeys;
+
+    // ---- staging of one key block: K and V rows u0 .. u0 + 63 (rows past the class are
+    // loaded from its last row and written as zeros)
+    u32x4 kreg[kStage], vreg[kStage];
+    auto load_block = [&](int u0) {
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
+            int u = u0 + row;
+            u = u < len ? u : len - 1;
+            const int64_t off = base + int64_t(u) * step + 8 * ch;
+            kreg[i] = *reinterpret_cast<const u32x4*>(k + off);
+            vreg[i] = *reinterpret_cast<const u32x4*>(v + off);
+        }
+    };
+    auto store_block = [&](int u0) {
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
+            const bool ok = u0 + row < len;
+            const u32x4 z{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(klds + kpiece<D>(row, ch)) = ok ? kreg[i] : z;
+            *reinterpret_cast<u32x4*>(vlds + ring_piece<D>(row, ch)) = ok ? vreg[i] : z;
+        }
+    };
+
+    f32x4 acc[kCb];
+#pragma unroll
+    for (int cb = 0; cb < kCb; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -__builtin_inff();   // running maximum of this lane's query (log2 units)
+    float l_run = 0.0f;                // this lane's share of the running sum
+
+    int aoff[kCb];
+#pragma unroll
+    for (int cb = 0; cb < kCb; ++cb) aoff[cb] = tr_lane_off<D>(col, cb);
+    // K rows of this lane's A operand within a 32-key chunk: tile 0 and tile 1
+    const int krow0 = 8 * (col >> 2) + (col & 3), krow1 = krow0 + 4;
+
+    load_block(u_lo);
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int u0 = u_lo + kKeys * blk;
+        store_block(u0);
+        __syncthreads();
+        // the next block's loads overlap this block's compute (a clamped repeat of the
+        // last block when there is none, so the loads are unconditional)
+        load_block(blk + 1 < nblk ? u0 + kKeys : u0);
+
+        // ---- scores: lane (col, grp) gets S[query tq][keys u0 + 32 c + 8 grp + 0..7]
+        f32x4 s0[2], s1[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            s0[c] = s1[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < kQk; ++kk) {
+                const V a0 = *reinterpret_cast<const V*>(klds + kpiece<D>(32 * c + krow0, 4 * kk + grp));
+                const V a1 = *reinterpret_cast<const V*>(klds + kpiece<D>(32 * c + krow1, 4 * kk + grp));
+                s0[c] = Mfma<In>::run(a0, qop[kk], s0[c]);
+                s1[c] = Mfma<In>::run(a1, qop[kk], s1[c]);
+            }
+        }
+        // ---- mask, block maximum, rescale
+        float x[2][8];
+        float mx = -__builtin_inff();
+        const int lo = tq - w, hi = tq + wu;   // in-range keys of this query (and < len)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int u = u0 + 32 * c + 8 * grp + e;
+                const float sv = e < 4 ? s0[c][e] : s1[c][e - 4];
+                const bool ok = u >= lo && u <= hi && u < len;
+                x[c][e] = ok ? sv * a.scale_log2 : -__builtin_inff();
+                mx = fmaxf(mx, x[c][e]);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
+        const float alpha = exp2f(m_run - m_use);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < kCb; ++cb) acc[cb] *= alpha;
+
+        // ---- probabilities as the B operand of out^T = V^T P^T, and the products
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = exp2f(x[c][e] - m_use);
+                l_run += p[e];
+            }
+            const u32x4 pb{pack2(p[0], p[1], In{}), pack2(p[2], p[3], In{}),
+                           pack2(p[4], p[5], In{}), pack2(p[6], p[7], In{})};
+            const V bop = __builtin_bit_cast(V, pb);
+            const unsigned char* rp = vlds + (32 * c + 8 * grp) * (2 * D);
+#pragma unroll
+            for (int cb = 0; cb < kCb; ++cb) {
+                const V av = tr_read8<V, D>(rp + aoff[cb]);
+                acc[cb] = Mfma<In>::run(av, bop, acc[cb]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- normalise and store: lane (col, grp) holds channels 16 cb + 4 grp .. +3
+    float l = l_run;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (tq < len) {
+        const float inv = 1.0f / l;
+        ST* orow = out + base + int64_t(tq) * step + 4 * grp;
+#pragma unroll
+        for (int cb = 0; cb < kCb; ++cb) {
+            const u32x2 o{pack2(acc[cb][0] * inv, acc[cb][1] * inv, In{}),
+                          pack2(acc[cb][2] * inv, acc[cb][3] * inv, In{})};
+            *reinterpret_cast<u32x2*>(orow + 16 * cb) = o;
+        }
+    }
+}
+
+AttnArgs make_args(const Problem& p, float scale) {
+    AttnArgs a;
+    a.n = p.n;
+    a.h = p.h;
+    a.w = p.w;
+    a.wu = p.wu;
+    a.s = p.s;
+    a.cls_q = p.n / p.s;
+    a.cls_m = p.n % p.s;
+    a.nqb_hi = (a.cls_q + 1 + kRows - 1) / kRows;
+    a.nqb_lo = (a.cls_q + kRows - 1) / kRows;
+    a.per_head = a.cls_m * a.nqb_hi + (p.s - a.cls_m) * a.nqb_lo;
+    a.groups = p.b * p.h * a.per_head;
+    a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    return a;
+}
+
+template <class In, int D>
+hipError_t launch_t(const void* q, const void* k, const void* v, void* out, const AttnArgs& a,
+                    hipStream_t stream) {
+    using ST = typename In::T;
+    launch_kernel(attn_fwd_kernel<In, D>, dim3(static_cast<uint32_t>(a.groups)), dim3(kThreads), 0,
+                  stream, static_cast<const ST*>(q), static_cast<const ST*>(k),
+                  static_cast<const ST*>(v), static_cast<ST*>(out), a);
+    return hipGetLastError();
+}
+
+template <class In>
+hipError_t launch_d(const void* q, const void* k, const void* v, void* out, const AttnArgs& a,
+                    int64_t d, hipStream_t stream) {
+    switch (d) {
+    case 32: return launch_t<In, 32>(q, k, v, out, a, stream);
+    case 64: return launch_t<In, 64>(q, k, v, out, a, stream);
+    case 128: return launch_t<In, 128>(q, k, v, out, a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+bool is16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+// f16 / bf16, d in {32, 64, 128}, 16-byte aligned tensors, class rows and window offsets
+// in 32-bit range, a grid below 2^31 workgroups.
+bool attention_supported(const Problem& p, int dt, const void* q, const void* k, const void* v,
+                         const void* out) {
+    if (dt != kF16 && dt != kBF16) return false;
+    if (p.d != 32 && p.d != 64 && p.d != 128) return false;
+    if (!is16(q) || !is16(k) || !is16(v) || !is16(out)) return false;
+    if (p.n >= (int64_t(1) << 30) || p.w >= (int64_t(1) << 30) || p.wu >= (int64_t(1) << 30))
+        return false;
+    const AttnArgs a = make_args(p, 1.0f);
+    return a.groups < (int64_t(1) << 31);
+}
+
+int64_t attention_workgroups(const Problem& p) { return make_args(p, 1.0f).groups; }
+
+hipError_t launch_attention(const void* q, const void* k, const void* v, void* out,
+                            const Problem& p, float scale, int dt, hipStream_t stream) {
+    const AttnArgs a = make_args(p, scale);
+    if (a.groups == 0) return hipSuccess;
+    switch (dt) {
+    case kF16: return launch_d<F16>(q, k, v, out, a, p.d, stream);
+    case kBF16: return launch_d<BF16>(q, k, v, out, a, p.d, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace diagmm

@@ -55,6 +55,14 @@ int64_t dropout_workgroups(const Problem& p, int dt, bool wide);
 hipError_t launch_dropout(const void* probs, const float* rand, void* out, const Problem& p,
                           float drop_p, int dt, bool wide, hipStream_t stream);
 
+// Sliding-window attention in one pass (f16 / bf16, d in {32, 64, 128}, 16-byte aligned
+// tensors): 256-thread workgroups of 64 class rows, keys staged 64 at a time.
+bool attention_supported(const Problem& p, int dt, const void* q, const void* k, const void* v,
+                         const void* out);
+int64_t attention_workgroups(const Problem& p);
+hipError_t launch_attention(const void* q, const void* k, const void* v, void* out,
+                            const Problem& p, float scale, int dt, hipStream_t stream);
+
 // qk on MFMA (f16 / bf16 inputs, d in {32, 64, 128}, 16-byte aligned pointers).
 constexpr int kQkRows = 128;                 // rows per tile
 constexpr int64_t kQkLdsBytes = 160 * 1024;  // one workgroup per compute unit

@@ -15,7 +15,7 @@ namespace diagmm {
 
 // Entry point tags (the modes of diagmm_plan).
 constexpr int kOpQk = 0, kOpPv = 1, kOpPvT = 2, kOpSoftmax = 3, kOpSoftmaxBwd = 4,
-              kOpSoftmaxMasked = 5, kOpDropout = 6;
+              kOpSoftmaxMasked = 5, kOpDropout = 6, kOpAttention = 7;
 
 // The entry point whose kernels are launched next (set by the C ABI before it launches).
 void timing_set_op(int op);

@@ -37,7 +37,7 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for want in ("diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax",
                  "diagmm_banded_softmax_backward", "diagmm_banded_softmax_masked",
-                 "diagmm_banded_dropout", "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
+                 "diagmm_banded_dropout", "diagmm_banded_attention", "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
                  "diagmm_plan"):
         assert want in names
 
@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dm.diagmm_abi_version() == 5
+    assert dm.diagmm_abi_version() == 6
     seen = set()
     for st in range(7):
         s = lib.diagmm_status_string(st).decode()
@@ -116,6 +116,16 @@ def test_validation_errors_are_reported_without_launching(lib):
     assert dr(P_, R_, R_ + 156, 1, 8, 1, 2, 2, 0, 0.1, 1, None) == ERR_ALIAS  # rand's last one
     assert dr(P_, O_ - 150, O_, 1, 8, 1, 2, 2, 0, 0.1, 1, None) == ERR_ALIAS  # rand's tail
     assert "diagmm_banded_dropout" in lib.diagmm_last_error().decode()
+    at = lib.diagmm_banded_attention
+    Q_, K_, V_, O_ = FAKE, FAKE + (1 << 30), FAKE + (1 << 34), FAKE + (1 << 38)
+    assert at(Q_, K_, 0, O_, 1, 8, 1, 64, 2, 2, 0, 0.125, 1, None) == ERR_NULL
+    assert at(Q_, K_, V_, O_, 1, 8, 1, 0, 2, 2, 0, 0.125, 1, None) == ERR_SHAPE
+    assert at(Q_, K_, V_, O_, 1, 8, 1, 64, 2, 2, 0, 0.125, 4, None) == ERR_DTYPE
+    assert at(Q_, K_, V_, K_ + 64, 1, 8, 1, 64, 2, 2, 0, 0.125, 1, None) == ERR_ALIAS
+    assert at(Q_, K_, V_, O_, 1, 8, 1, 64, 2, 2, 0, 0.125, 0, None) == ERR_UNSUPPORTED  # f32
+    assert at(Q_, K_, V_, O_, 1, 8, 1, 48, 2, 2, 0, 0.125, 1, None) == ERR_UNSUPPORTED  # d
+    assert at(Q_ + 2, K_, V_, O_, 1, 8, 1, 64, 2, 2, 0, 0.125, 1, None) == ERR_UNSUPPORTED
+    assert "diagmm_banded_attention" in lib.diagmm_last_error().decode()
 
 
 def test_empty_problems_are_noops(lib):
@@ -127,6 +137,7 @@ def test_empty_problems_are_noops(lib):
     assert lib.diagmm_banded_softmax_masked(0, 0, 0, 0, 8, 3, 2, 2, 0, 1.0, -1e4, 1, 1,
                                             None) == OK
     assert lib.diagmm_banded_dropout(0, 0, 0, 1, 0, 3, 2, 2, 0, 0.5, 2, None) == OK
+    assert lib.diagmm_banded_attention(0, 0, 0, 0, 2, 0, 3, 64, 2, 2, 0, 0.1, 1, None) == OK
     assert lib.diagmm_last_error().decode() == ""
 
 
@@ -191,4 +202,19 @@ def test_dropout_plan_covers_the_band(lib):
     assert p["kernel"] == "dropout_elems" and p["workgroups"] == -(-2 * 50 * 3 * 7 // 1024)
     with pytest.raises(dm.DiagmmError) as e:
         dm.diagmm_plan("softmax_masked", 1, 64, 1, 1, 8, 8, 0, torch.float16)
+    assert e.value.status == ERR_UNSUPPORTED
+
+
+def test_attention_plan_one_workgroup_per_class_row_block(lib):
+    """64 class rows per workgroup: 64 blocks per head at n = 4096 undilated; with
+    dilation 3 the classes have 1366, 1365, 1365 rows, 22 blocks each."""
+    p = dm.diagmm_plan("attention", 1, 4096, 12, 64, 256, 256, 0, torch.float16)
+    assert p["kernel"] == "attn_fwd_f16_d64" and p["workgroups"] == 12 * 64
+    assert p["lds_bytes"] == 2 * 64 * 128 and p["residues"] == 1
+    p = dm.diagmm_plan("attention", 1, 4096, 12, 64, 256, 256, 3, torch.bfloat16)
+    assert p["workgroups"] == 12 * 3 * 22 and p["residues"] == 3
+    p = dm.diagmm_plan("attention", 2, 5, 1, 32, 2, 2, 9, torch.float16)   # 5 classes of 1
+    assert p["workgroups"] == 2 * 5
+    with pytest.raises(dm.DiagmmError) as e:
+        dm.diagmm_plan("attention", 1, 64, 1, 64, 8, 8, 0, torch.float32)
     assert e.value.status == ERR_UNSUPPORTED

@@ -67,6 +67,8 @@ def op_costs(dil):
         "softmax_masked": {"bytes": cnt * E + band + B * N * 4, "flops": 0},
         # dropout: P and its float32 random numbers on the in-range slots, the band written
         "dropout": {"bytes": cnt * (E + 4) + band, "flops": 0},
+        # attention in one pass: Q, K, V read and the output written; both products' flops
+        "attention": {"bytes": 4 * dense, "flops": 4 * D * cnt},
     }
 
 
@@ -250,6 +252,8 @@ def main():
                 dm.diagmm_banded_softmax(t[f"S{dil}"], W, WU, dil, SCALE, out=dscores,
                                          key_mask=key_mask)
                 dm.diagmm_banded_dropout(t[f"S{dil}"], rand, W, WU, dil, 0.1, out=dscores)
+                dm.diagmm_banded_attention(t["q"], t["k"], t["v"], W, WU, dil, SCALE,
+                                           out=t[f"O{dil}"])
         torch.cuda.synchronize()
         print(json.dumps({"pmc_probe": True, "reference_copy_bytes": ref_bytes,
                           "qk_algorithmic_bytes": op_costs(0)["qk"]["bytes"],
@@ -326,7 +330,7 @@ def main():
         t["dP"] = dm.diagmm_qk(t["do"], t["v"], W, WU, 0, 0.0)
         t["dS"] = torch.empty_like(t["dP"])
         t["rand"] = torch.rand(t["dP"].shape, generator=gen, device=dev, dtype=torch.float32)
-    for op in ("softmax_bwd", "softmax_masked", "dropout"):
+    for op in ("softmax_bwd", "softmax_masked", "dropout", "attention"):
         for dil in DILATIONS:
             def run(t):
                 if op == "softmax_bwd":
@@ -335,9 +339,12 @@ def main():
                 elif op == "softmax_masked":
                     dm.diagmm_banded_softmax(t[f"S{dil}"], W, WU, dil, SCALE, out=t["dS"],
                                              key_mask=key_mask)
-                else:
+                elif op == "dropout":
                     dm.diagmm_banded_dropout(t[f"S{dil}"], t["rand"], W, WU, dil, 0.1,
                                              out=t["dS"])
+                else:
+                    dm.diagmm_banded_attention(t["q"], t["k"], t["v"], W, WU, dil, SCALE,
+                                               out=t[f"O{dil}"])
             for i in range(args.warmup):
                 run(sets[i % len(sets)])
             torch.cuda.synchronize()
@@ -355,6 +362,13 @@ def main():
                 "GB/s": round(c["bytes"] / (ms * 1e-3) / 1e9, 1),
                 "bytes": c["bytes"],
             }
+            if op == "attention":
+                three = sum(per_op[f"{o}_dil{dil}"]["us"] for o in ("qk", "softmax", "pv"))
+                extra[f"{op}_dil{dil}"].update({
+                    "TFLOP/s": round(c["flops"] / (ms * 1e-3) / 1e12, 2),
+                    "flops": c["flops"],
+                    "three_calls_us": round(three, 2),
+                })
     for t in sets:
         del t["dP"], t["dS"], t["rand"]
     ceiling = practical_ceiling(torch, dev, stream)

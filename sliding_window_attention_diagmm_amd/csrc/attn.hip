@@ -13,9 +13,10 @@
 // t = 0 .. len - 1 of the class attend class keys t - w .. t + w_upper).  A workgroup of
 // four waves takes 64 consecutive class rows of one (batch, head); wave v owns rows
 // 16 v .. 16 v + 15.  It walks the keys its rows reach, t0 - w .. t0 + 63 + w_upper, in
-// blocks of 64 staged in LDS, with an online softmax: per block the running row maximum
-// is raised, the accumulators and the running sums are rescaled by exp(old - new), and
-// the block's probabilities are added in.
+// blocks of 64 staged in LDS, with an online softmax: when a block raises some row's
+// maximum by more than a factor 2^8 the running maxima are raised and the accumulators and
+// running sums rescaled by exp(old - new); then the block's probabilities, relative to the
+// running maximum, are added in.
 //
 // MFMA layouts (v_mfma_f32_16x16x32_{f16,bf16}; A lanes hold a row and 8 K-values, B
 // lanes a column and 8 K-values, C lanes a column and 4 rows).  Scores are computed
@@ -55,9 +56,10 @@ template <> struct Mfma<BF16> {
     }
 };
 
-constexpr int kThreads = 256;
-constexpr int kRows = 64;     // class rows per workgroup
-constexpr int kKeys = 64;     // keys per LDS block
+constexpr int kRows = 64;                   // class rows per workgroup, 16 per wave
+constexpr int kThreads = kRows / 16 * 64;
+constexpr int kKeys = 64;                   // keys per LDS block
+constexpr int kChunks = kKeys / 32;         // 32-key chunks per block
 
 struct AttnArgs {
     int64_t n, h, w, wu, s;
@@ -179,19 +181,12 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     // K rows of this lane's A operand within a 32-key chunk: tile 0 and tile 1
     const int krow0 = 8 * (col >> 2) + (col & 3), krow1 = krow0 + 4;
 
-    load_block(u_lo);
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int u0 = u_lo + kKeys * blk;
-        store_block(u0);
-        __syncthreads();
-        // the next block's loads overlap this block's compute (a clamped repeat of the
-        // last block when there is none, so the loads are unconditional)
-        load_block(blk + 1 < nblk ? u0 + kKeys : u0);
+    auto compute_block = [&](int u0) {
 
         // ---- scores: lane (col, grp) gets S[query tq][keys u0 + 32 c + 8 grp + 0..7]
-        f32x4 s0[2], s1[2];
+        f32x4 s0[kChunks], s1[kChunks];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < kChunks; ++c) {
             s0[c] = s1[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < kQk; ++kk) {
@@ -201,38 +196,57 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
                 s1[c] = Mfma<In>::run(a1, qop[kk], s1[c]);
             }
         }
-        // ---- mask, block maximum, rescale
-        float x[2][8];
+        // ---- scale, mask (only blocks that are not wholly inside every row's window of
+        // this wave need it), block maximum
+        float x[kChunks][8];
         float mx = -__builtin_inff();
         const int lo = tq - w, hi = tq + wu;   // in-range keys of this query (and < len)
+        const int tw = t0 + 16 * wv;           // this wave's first row
+        const bool inner = u0 >= tw + 15 - w && u0 + kKeys - 1 <= tw + wu &&
+                           u0 + kKeys - 1 < len;
+        if (inner) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+            for (int c = 0; c < kChunks; ++c)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int u = u0 + 32 * c + 8 * grp + e;
-                const float sv = e < 4 ? s0[c][e] : s1[c][e - 4];
-                const bool ok = u >= lo && u <= hi && u < len;
-                x[c][e] = ok ? sv * a.scale_log2 : -__builtin_inff();
-                mx = fmaxf(mx, x[c][e]);
-            }
+                for (int e = 0; e < 8; ++e) {
+                    x[c][e] = (e < 4 ? s0[c][e] : s1[c][e - 4]) * a.scale_log2;
+                    mx = fmaxf(mx, x[c][e]);
+                }
+        } else {
+#pragma unroll
+            for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int u = u0 + 32 * c + 8 * grp + e;
+                    const float sv = e < 4 ? s0[c][e] : s1[c][e - 4];
+                    const bool ok = u >= lo && u <= hi && u < len;
+                    x[c][e] = ok ? sv * a.scale_log2 : -__builtin_inff();
+                    mx = fmaxf(mx, x[c][e]);
+                }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
-        const float alpha = exp2f(m_run - m_use);
-        m_run = m_new;
-        l_run *= alpha;
+        // ---- rescale only when some row's maximum grew by more than 2^8: otherwise the
+        // old reference stays, and the block's terms exp2(x - m) stay below 256, exact
+        // in the sum and representable in the 16-bit probabilities alike
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(
+                m_run - (m_new == -__builtin_inff() ? 0.0f : m_new));
+            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
-        for (int cb = 0; cb < kCb; ++cb) acc[cb] *= alpha;
+            for (int cb = 0; cb < kCb; ++cb) acc[cb] *= alpha;
+        }
+        const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
 
         // ---- probabilities as the B operand of out^T = V^T P^T, and the products
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < kChunks; ++c) {
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                p[e] = exp2f(x[c][e] - m_use);
+                p[e] = __builtin_amdgcn_exp2f(x[c][e] - m_use);
                 l_run += p[e];
             }
             const u32x4 pb{pack2(p[0], p[1], In{}), pack2(p[2], p[3], In{}),
@@ -245,6 +259,17 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
                 acc[cb] = Mfma<In>::run(av, bop, acc[cb]);
             }
         }
+    };
+
+    // The next block's loads overlap this block's compute (a clamped repeat of the last
+    // block when there is none, so the loads are unconditional).
+    load_block(u_lo);
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int u0 = u_lo + kKeys * blk;
+        store_block(u0);
+        __syncthreads();
+        load_block(blk + 1 < nblk ? u0 + kKeys : u0);
+        compute_block(u0);
         __syncthreads();
     }
 

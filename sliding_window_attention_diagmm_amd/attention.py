@@ -13,6 +13,9 @@ they give attention over a (dilated) sliding window and its gradients:
                dS = softmax_backward(P, dP)                     (scale included)
                dQ = pv(dS, K)      dK = pvT(dS, Q)
 
+Without gradients (inference), f16/bf16 inputs with d in {32, 64, 128}, no key mask and no
+dropout go to the one-pass kernel, which never writes the band.
+
 Every step runs in the library's kernels; this module only orders the calls, keeps P
 (and the caller's random numbers) for the backward pass, where Pd is drawn again from
 them, and hands torch's autograd the results.  Tensors are contiguous ``[b, n, h, d]``
@@ -22,8 +25,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (diagmm_banded_dropout, diagmm_banded_softmax, diagmm_banded_softmax_backward,
-               diagmm_pv, diagmm_pvT, diagmm_qk)
+from . import (diagmm_banded_attention, diagmm_banded_dropout, diagmm_banded_softmax,
+               diagmm_banded_softmax_backward, diagmm_pv, diagmm_pvT, diagmm_qk)
 
 
 class BandedAttention(torch.autograd.Function):
@@ -80,5 +83,11 @@ def banded_attention(q, k, v, w, w_upper=None, dilation=0, scale=None, key_mask=
         scale = q.shape[-1] ** -0.5
     if dropout_p > 0.0 and dropout_rand is None:
         raise ValueError("dropout_p > 0 needs dropout_rand (the caller draws the uniforms)")
+    needs_grad = torch.is_grad_enabled() and any(t.requires_grad for t in (q, k, v))
+    if (not needs_grad and key_mask is None and dropout_p == 0.0
+            and q.dtype in (torch.float16, torch.bfloat16) and q.shape[-1] in (32, 64, 128)):
+        # inference: the one-pass kernel (the band is never written)
+        return diagmm_banded_attention(q, k, v, int(w), int(w_upper), int(dilation),
+                                       float(scale))
     return BandedAttention.apply(q, k, v, int(w), int(w_upper), int(dilation), float(scale),
                                  key_mask, float(mask_value), float(dropout_p), dropout_rand)

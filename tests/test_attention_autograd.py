@@ -120,3 +120,19 @@ def test_banded_attention_with_dropout_matches_dense_autograd(shape):
     o1 = banded_attention(qc.detach(), kc.detach(), vc.detach(), w, wu, dil, dropout_p=0.0,
                           dropout_rand=rand.cuda())
     assert torch.equal(o0, o1)
+
+
+def test_banded_attention_without_gradients_takes_the_one_pass_kernel():
+    """Under no_grad, f16 inputs go to diagmm_banded_attention (bit for bit its output),
+    which agrees with the three-call forward to the 16-bit bar."""
+    import sliding_window_attention_diagmm_amd as dm
+    from sliding_window_attention_diagmm_amd.attention import banded_attention
+    b, n, h, d, w, dil = 1, 600, 2, 64, 40, 2
+    g_ = datagen.rng(760)
+    q, k, v = (datagen.normal(g_, (b, n, h, d), "f16", 0.5).cuda() for _ in range(3))
+    with torch.no_grad():
+        o = banded_attention(q, k, v, w, w, dil)
+    assert torch.equal(o, dm.diagmm_banded_attention(q, k, v, w, w, dil))
+    qg = q.clone().requires_grad_(True)
+    o3 = banded_attention(qg, k, v, w, w, dil)
+    assert (o.float() - o3.detach().float()).abs().max().item() <= 4e-3

@@ -74,6 +74,8 @@ def _load():
                                            ci]
             lib.oracle_attention.argtypes = [vp, vp, vp, vp] + [i64] * 7 + [cd, ci, ci, vp, i64,
                                                                               ci]
+            lib.oracle_attention_global.argtypes = [vp, vp, vp, vp, i64, vp] + [i64] * 7 + [
+                cd, ci, ci, vp, i64, ci]
             lib.oracle_softmax_masked.argtypes = [vp, vp, vp] + [i64] * 6 + [cd, cd, ci, ci, vp,
                                                                                  i64, ci]
             for f in (lib.oracle_qk, lib.oracle_pv, lib.oracle_pvT, lib.oracle_softmax):
@@ -184,6 +186,30 @@ def attention(q, k, v, w, w_upper, dilation=0, scale=1.0, out_dtype=None, rows=N
                               threads or default_threads())
     if st:
         raise ValueError(f"oracle.attention: bad arguments ({st})")
+    return out
+
+
+def attention_global(q, k, v, glob, w, w_upper, dilation=0, scale=1.0, out_dtype=None,
+                     rows=None, threads=None):
+    """Sliding-window attention with global tokens: ``glob`` is an integer [b, ng] tensor
+    of distinct global positions per batch.  A row outside them attends its window and
+    the global keys (each key once); a global row attends every key."""
+    lib = _load()
+    q, k, v = _check(q, "q"), _check(k, "k"), _check(v, "v")
+    if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype):
+        raise ValueError("oracle.attention_global: q, k, v differ in shape or dtype")
+    b, n, h, d = q.shape
+    g = torch.as_tensor(glob, dtype=torch.int64).reshape(b, -1).contiguous()
+    out_dtype = out_dtype or q.dtype
+    rt, rp, nr = _rows(rows)
+    shape = (b, n, h, d) if rt is None else (nr, h, d)
+    out = torch.empty(shape, dtype=out_dtype)
+    st = lib.oracle_attention_global(_ptr(q), _ptr(k), _ptr(v), _ptr(g), g.shape[1], _ptr(out),
+                                     b, n, h, d, w, w_upper, dilation, float(scale),
+                                     _CODE[q.dtype], _CODE[out_dtype], rp, nr,
+                                     threads or default_threads())
+    if st:
+        raise ValueError(f"oracle.attention_global: bad arguments ({st})")
     return out
 
 

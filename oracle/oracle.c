@@ -496,3 +496,66 @@ int oracle_attention(const void* q, const void* kt, const void* v, void* out, in
     }
     return failed ? 3 : 0;
 }
+
+/* ------------------------------------------------------------------ global tokens
+ * Sliding-window attention with global tokens (onnxruntime issue 12448: the
+ * LongformerAttention op, a sliding window plus global tokens).  G_bb is a set of
+ * positions of batch bb (glob[bb * ng + g], g < ng, distinct).  A row i outside G_bb
+ * attends the keys of its window and every key in G_bb, each key once; a row in G_bb
+ * attends every key of the sequence.  Both use the same Q, K, V:
+ *     keys(i) = { j : i in G, or j in G, or j = i + (k - w) * s for a slot k },
+ *     out[i] = sum_{j in keys(i)} softmax_j(scale * Q[i] . K[j]) V[j].
+ * Written directly from that set, one row at a time in double. */
+int oracle_attention_global(const void* q, const void* kt, const void* v, const int64_t* glob,
+                            int64_t ng, void* out, int64_t b, int64_t n, int64_t h, int64_t d,
+                            int64_t w, int64_t wu, int64_t dil, double scale, int in_dt,
+                            int out_dt, const int64_t* rows, int64_t nrows, int nthreads)
+{
+    int bad = or_check(b, n, h, d, w, wu, dil, in_dt, out_dt);
+    if (bad) return bad;
+    if (ng < 0 || (ng > 0 && !glob)) return 1;
+    for (int64_t i = 0; i < b * ng; ++i)
+        if (glob[i] < 0 || glob[i] >= n) return 1;
+    const int64_t s = or_stride(dil);
+    if (!rows) nrows = b * n;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t bi = or_row(rows, r), bb = bi / n, i = bi % n;
+        double* x = (double*)malloc((size_t)n * sizeof(double));
+        char* isg = (char*)calloc((size_t)n, 1);
+        if (!x || !isg) { free(x); free(isg); failed = 1; continue; }
+        for (int64_t g = 0; g < ng; ++g) isg[glob[bb * ng + g]] = 1;
+        for (int64_t hh = 0; hh < h; ++hh) {
+            const int64_t qrow = ((bb * n + i) * h + hh) * d;
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < n; ++j) {
+                const int64_t off = j - i;
+                const int in_window = off % s == 0 && off >= -w * s && off <= wu * s;
+                x[j] = -INFINITY;
+                if (!(isg[i] || isg[j] || in_window)) continue;
+                double acc = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    acc += or_load(q, qrow + c, in_dt) *
+                           or_load(kt, ((bb * n + j) * h + hh) * d + c, in_dt);
+                x[j] = scale * acc;
+                if (x[j] > mx) mx = x[j];
+            }
+            double sum = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                x[j] = (x[j] == -INFINITY) ? 0.0 : exp(x[j] - mx);
+                sum += x[j];
+            }
+            for (int64_t c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < n; ++j)
+                    if (x[j] != 0.0)
+                        acc += (x[j] / sum) * or_load(v, ((bb * n + j) * h + hh) * d + c, in_dt);
+                or_store(out, (r * h + hh) * d + c, out_dt, acc);
+            }
+        }
+        free(x);
+        free(isg);
+    }
+    return failed ? 3 : 0;
+}

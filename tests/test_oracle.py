@@ -714,3 +714,58 @@ def test_attention_row_list_equals_full():
     full = oracle.attention(q, k, v, w, wu, dil, 0.3).reshape(b * n, h, d)
     assert torch.equal(oracle.attention(q, k, v, w, wu, dil, 0.3, rows=rows),
                        full[torch.from_numpy(rows)])
+
+
+# ------------------------------------------------------------ global-token pins
+# A row outside the global set attends its window and the global keys, each once; a
+# global row attends every key.  Pins: torch's float64 softmax attention with that key
+# set as a dense mask, no global tokens = the windowed attention, a global row = full
+# dense attention, and all rows global = full dense attention everywhere.
+
+def _dense_global(q, k, v, glob, w, wu, dil, scale):
+    b, n = q.shape[:2]
+    i = torch.arange(n)[:, None]
+    j = torch.arange(n)[None, :]
+    off = j - i
+    s = max(dil, 1)
+    win = (off % s == 0) & (off >= -w * s) & (off <= wu * s)
+    outs = []
+    for bb in range(b):
+        isg = torch.zeros(n, dtype=torch.bool)
+        isg[glob[bb]] = True
+        sel = win | isg[None, :] | isg[:, None]
+        sc = torch.einsum("ihd,jhd->hij", q[bb].double(), k[bb].double()) * scale
+        p = torch.softmax(sc.masked_fill(~sel, float("-inf")), -1)
+        outs.append(torch.einsum("hij,jhd->ihd", p, v[bb].double()))
+    return torch.stack(outs)
+
+
+@pytest.mark.parametrize("shape", [(2, 40, 2, 8, 3, 3, 0), (1, 50, 1, 8, 4, 0, 3),
+                                   (1, 33, 2, 4, 40, 40, 0), (2, 30, 1, 8, 2, 5, 2)])
+def test_attention_global_matches_dense_masked_attention(shape):
+    b, n, h, d, w, wu, dil = shape
+    g = datagen.rng(980 + n)
+    q, k, v = (datagen.normal(g, (b, n, h, d), "f32") for _ in range(3))
+    glob = torch.stack([torch.from_numpy(datagen.rng(990 + bb).choice(n, 4, replace=False))
+                        for bb in range(b)])
+    got = oracle.attention_global(q, k, v, glob, w, wu, dil, 0.6, out_dtype=torch.float64)
+    assert torch.allclose(got, _dense_global(q, k, v, glob, w, wu, dil, 0.6), rtol=0, atol=1e-12)
+
+
+def test_attention_global_special_cases():
+    b, n, h, d, w, wu, dil = 1, 36, 2, 8, 3, 2, 2
+    g = datagen.rng(995)
+    q, k, v = (datagen.normal(g, (b, n, h, d), "f32") for _ in range(3))
+    none = torch.zeros(b, 0, dtype=torch.int64)
+    assert torch.allclose(oracle.attention_global(q, k, v, none, w, wu, dil, 0.5,
+                                                  out_dtype=torch.float64),
+                          oracle.attention(q, k, v, w, wu, dil, 0.5, out_dtype=torch.float64),
+                          rtol=0, atol=1e-14)
+    dense = oracle.attention(q, k, v, n, n, 0, 0.5, out_dtype=torch.float64)   # every key
+    glob = torch.tensor([[5, 17]])
+    got = oracle.attention_global(q, k, v, glob, w, wu, dil, 0.5, out_dtype=torch.float64)
+    assert torch.allclose(got[0, [5, 17]], dense[0, [5, 17]], rtol=0, atol=1e-14)
+    every = torch.arange(n)[None, :]
+    assert torch.allclose(oracle.attention_global(q, k, v, every, w, wu, dil, 0.5,
+                                                  out_dtype=torch.float64), dense,
+                          rtol=0, atol=1e-14)

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DIAGMM_ABI_VERSION 6
+#define DIAGMM_ABI_VERSION 7
 
 typedef enum {
     DIAGMM_F32 = 0,
@@ -197,6 +197,26 @@ diagmm_status_t diagmm_banded_attention(const void* q, const void* k, const void
                                         int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,
                                         int64_t w_upper, int64_t dilation, float scale,
                                         diagmm_dtype_t dtype, void* stream);
+
+/*
+ * diagmm_banded_attention_global - diagmm_banded_attention with global tokens, as in the
+ * LongformerAttention op of onnxruntime issue 12448 (a sliding window plus global tokens).
+ * global_pos is int32 [b][ng] on the device: the positions of batch bb's global tokens
+ * (distinct; entries outside [0, n) are clamped into it, never read out of bounds).  A row
+ * outside the global set attends the keys of its window and every global key, each key
+ * once; a global row attends every key of the sequence.  One Q, K and V serve both.  ng =
+ * 0 is diagmm_banded_attention.  Two kernels run in order on `stream` (the rows outside
+ * the set, then the global rows).  ng outside [0, n] is DIAGMM_ERR_SHAPE; global_pos NULL
+ * with ng > 0 is DIAGMM_ERR_NULL; out overlapping q, k, v or global_pos is
+ * DIAGMM_ERR_ALIAS; besides the shapes diagmm_banded_attention refuses, windows with
+ * 64 + w + w_upper > 16384 are DIAGMM_ERR_UNSUPPORTED.
+ */
+diagmm_status_t diagmm_banded_attention_global(const void* q, const void* k, const void* v,
+                                               void* out, const int32_t* global_pos,
+                                               int64_t ng, int64_t b, int64_t n, int64_t h,
+                                               int64_t d, int64_t w, int64_t w_upper,
+                                               int64_t dilation, float scale,
+                                               diagmm_dtype_t dtype, void* stream);
 
 /* Static text for a status code. */
 const char* diagmm_status_string(diagmm_status_t status);

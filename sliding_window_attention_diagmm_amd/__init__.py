@@ -24,7 +24,8 @@ import os
 import torch
 
 __all__ = ["diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax",
-           "diagmm_banded_softmax_backward", "diagmm_banded_dropout", "diagmm_banded_attention", "diagmm_plan",
+           "diagmm_banded_softmax_backward", "diagmm_banded_dropout", "diagmm_banded_attention",
+           "diagmm_banded_attention_global", "diagmm_plan",
            "diagmm_timing_begin", "diagmm_timing_end", "diagmm_timing_read",
            "diagmm_abi_version", "library_path", "load", "DiagmmError"]
 
@@ -83,6 +84,8 @@ def load() -> ctypes.CDLL:
     lib.diagmm_banded_dropout.restype = ci
     lib.diagmm_banded_attention.argtypes = [vp, vp, vp, vp] + [i64] * 7 + [f32, ci, vp]
     lib.diagmm_banded_attention.restype = ci
+    lib.diagmm_banded_attention_global.argtypes = [vp, vp, vp, vp, vp] + [i64] * 8 + [f32, ci, vp]
+    lib.diagmm_banded_attention_global.restype = ci
     lib.diagmm_status_string.argtypes = [ci]
     lib.diagmm_status_string.restype = ctypes.c_char_p
     lib.diagmm_last_error.argtypes = []
@@ -297,6 +300,34 @@ def diagmm_banded_attention(q, k, v, w, w_upper=None, dilation=0, scale=None, ou
     st = lib.diagmm_banded_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), res.data_ptr(),
                                      b, n, h, d, w, w_upper, dilation, float(scale),
                                      _DT[q.dtype], _stream(q.device))
+    if st:
+        _raise(lib, st)
+    return res
+
+
+def diagmm_banded_attention_global(q, k, v, global_pos, w, w_upper=None, dilation=0,
+                                   scale=None, out=None):
+    """``diagmm_banded_attention`` with global tokens: ``global_pos`` is int32 [b, ng] on
+    the GPU (distinct positions).  Rows outside the set attend their window and the global
+    keys (each key once); global rows attend every key."""
+    lib = load()
+    w, w_upper, dilation = _window(w, w_upper, dilation)
+    q, k, v = _dense(q, "q"), _dense(k, "k"), _dense(v, "v")
+    if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype
+            and q.device == k.device == v.device):
+        raise ValueError("q, k and v must have the same shape, dtype and device")
+    b, n, h, d = q.shape
+    g = global_pos
+    if (not isinstance(g, torch.Tensor) or g.dtype != torch.int32 or g.dim() != 2
+            or g.shape[0] != b or g.device != q.device or not g.is_contiguous()):
+        raise ValueError("global_pos must be a contiguous int32 [b, ng] tensor on q's device")
+    if scale is None:
+        scale = d ** -0.5
+    res = _out(out, q.shape, q.dtype, q.device)
+    st = lib.diagmm_banded_attention_global(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                            res.data_ptr(), g.data_ptr(), g.shape[1], b, n, h,
+                                            d, w, w_upper, dilation, float(scale),
+                                            _DT[q.dtype], _stream(q.device))
     if st:
         _raise(lib, st)
     return res

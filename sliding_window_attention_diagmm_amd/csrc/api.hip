@@ -352,7 +352,38 @@ diagmm_status_t diagmm_banded_attention(const void* q, const void* k, const void
         return fail(DIAGMM_ERR_UNSUPPORTED, "%s: needs f16 or bf16, d in {32, 64, 128} and "
                     "16-byte aligned tensors", fn);
     timing_set_op(kOpAttention);
-    return launched(fn, launch_attention(q, k, v, out, p, scale, dtype,
+    return launched(fn, launch_attention(q, k, v, out, nullptr, 0, p, scale, dtype,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+diagmm_status_t diagmm_banded_attention_global(const void* q, const void* k, const void* v,
+                                               void* out, const int32_t* global_pos,
+                                               int64_t ng, int64_t b, int64_t n, int64_t h,
+                                               int64_t d, int64_t w, int64_t w_upper,
+                                               int64_t dilation, float scale,
+                                               diagmm_dtype_t dtype, void* stream) {
+    const char* fn = "diagmm_banded_attention_global";
+    Problem p;
+    int64_t de, be;
+    diagmm_status_t st = check_common(fn, b, n, h, d, w, w_upper, dilation, dtype, dtype, &p,
+                                      &de, &be);
+    if (st != DIAGMM_OK) return st;
+    if (ng < 0 || ng > n) return fail(DIAGMM_ERR_SHAPE, "%s: ng = %lld outside [0, n]", fn,
+                                      static_cast<long long>(ng));
+    if (p.rows() * p.h == 0) return ok();
+    if (!q || !k || !v || !out || (ng > 0 && !global_pos))
+        return fail(DIAGMM_ERR_NULL, "%s: null pointer", fn);
+    const int64_t bytes = de * static_cast<int64_t>(elem_size(dtype));
+    for (const void* in : {q, k, v})
+        if (overlaps(out, bytes, in, bytes))
+            return fail(DIAGMM_ERR_ALIAS, "%s: out overlaps q, k or v", fn);
+    if (ng > 0 && overlaps(out, bytes, global_pos, b * ng * 4))
+        return fail(DIAGMM_ERR_ALIAS, "%s: out overlaps global_pos", fn);
+    if (!attention_supported(p, dtype, q, k, v, out) || !attention_global_supported(p, ng))
+        return fail(DIAGMM_ERR_UNSUPPORTED, "%s: needs f16 or bf16, d in {32, 64, 128}, "
+                    "16-byte aligned tensors and 64 + w + w_upper <= 16384", fn);
+    timing_set_op(kOpAttention);
+    return launched(fn, launch_attention(q, k, v, out, global_pos, ng, p, scale, dtype,
                                          static_cast<hipStream_t>(stream)));
 }
 

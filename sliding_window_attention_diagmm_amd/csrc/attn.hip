@@ -68,7 +68,14 @@ struct AttnArgs {
     int64_t per_head;         // workgroups per (batch, head)
     int64_t groups;           // workgroups in the grid
     float scale_log2;         // scale * log2(e)
+    int32_t ng;               // global tokens per batch (0: none)
+    int64_t ngb;              // 64-row blocks of global rows per (batch, head)
 };
+
+// Kernel modes: the window only; the window plus the global keys for rows outside the
+// global set (global query rows are not stored); the global rows, each over every key.
+constexpr int kBand = 0, kBandGlobal = 1, kGlobalRows = 2;
+constexpr int kBitWords = 512;   // LDS bitmap of global keys in a workgroup's key range
 
 // K block: row r (key), 16-byte piece ch at r * 2D + 16 (ch ^ sw(r)); the swizzle puts the
 // eight rows 8 (m / 4) + (m % 4) (+ 4) read by lanes m = 0..7 of a score tile on distinct
@@ -87,11 +94,11 @@ __device__ __forceinline__ uint32_t pack2(float a, float b, BF16) {
     return static_cast<uint32_t>(BF16::from_f32(a)) | (static_cast<uint32_t>(BF16::from_f32(b)) << 16);
 }
 
-template <class In, int D>
+template <class In, int D, int kMode>
 __global__ void __launch_bounds__(kThreads)
 attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __restrict__ k,
                 const typename In::T* __restrict__ v, typename In::T* __restrict__ out,
-                AttnArgs a) {
+                const int32_t* __restrict__ glob, AttnArgs a) {
     using ST = typename In::T;
     using V = typename Mfma<In>::V;
     constexpr int kPieces = D / 8;                       // 16-byte pieces per row
@@ -100,6 +107,7 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     constexpr int kCb = D / 16;                          // 16-channel output blocks
     __shared__ __attribute__((aligned(16))) unsigned char klds[kKeys * 2 * D];
     __shared__ __attribute__((aligned(16))) unsigned char vlds[kKeys * 2 * D];
+    __shared__ uint32_t gbits[kMode == kBandGlobal ? kBitWords : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
@@ -112,10 +120,14 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
         const int64_t x = blockIdx.x % 8, loc = blockIdx.x / 8;
         id = x * per + (x < rem ? x : rem) + loc;
     }
-    const int64_t bh = id / a.per_head;
-    int64_t rest = id - bh * a.per_head;
+    const int64_t units = kMode == kGlobalRows ? a.ngb : a.per_head;
+    const int64_t bh = id / units;
+    int64_t rest = id - bh * units;
     int64_t r, qb;
-    if (rest < a.cls_m * a.nqb_hi) {
+    if (kMode == kGlobalRows) {
+        r = 0;              // the whole sequence as one undilated class, queries gathered
+        qb = rest;
+    } else if (rest < a.cls_m * a.nqb_hi) {
         r = rest / a.nqb_hi;
         qb = rest - r * a.nqb_hi;
     } else {
@@ -124,25 +136,53 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
         qb = rest - (r - a.cls_m) * a.nqb_lo;
     }
     const int64_t bb = bh / a.h, hh = bh - bb * a.h;
-    const int len = static_cast<int>(a.cls_q + (r < a.cls_m ? 1 : 0));
+    const int len = kMode == kGlobalRows ? static_cast<int>(a.n)
+                                         : static_cast<int>(a.cls_q + (r < a.cls_m ? 1 : 0));
     const int t0 = static_cast<int>(qb) * kRows;
     // element offset of class row t: base + t * step
     const int64_t base = ((bb * a.n + r) * a.h + hh) * D;
-    const int64_t step = a.s * a.h * D;
+    const int64_t step = (kMode == kGlobalRows ? 1 : a.s) * a.h * D;
+    const int ng = a.ng;
+    // position of global token g of this batch, clamped into the sequence
+    auto gpos = [&](int g) {
+        int x = glob[bb * ng + (g < ng ? g : ng - 1)];
+        return x < 0 ? 0 : (x >= a.n ? static_cast<int>(a.n) - 1 : x);
+    };
 
     // ---- this lane's query row as the B operand of S^T (channels 32 kk + 8 grp .. +7)
     const int tq = t0 + 16 * wv + col;
-    const int tq_ld = tq < len ? tq : len - 1;
+    const int tq_ld = kMode == kGlobalRows ? gpos(tq) : (tq < len ? tq : len - 1);
     V qop[kQk];
 #pragma unroll
     for (int kk = 0; kk < kQk; ++kk)
         qop[kk] = *reinterpret_cast<const V*>(q + base + int64_t(tq_ld) * step + 32 * kk + 8 * grp);
 
-    const int w = static_cast<int>(a.w), wu = static_cast<int>(a.wu);
-    const int u_lo = t0 - w > 0 ? t0 - w : 0;
+    const int w = kMode == kGlobalRows ? 0 : static_cast<int>(a.w);
+    const int wu = kMode == kGlobalRows ? 0 : static_cast<int>(a.wu);
+    int u_lo = t0 - w > 0 ? t0 - w : 0;
     const int last_q = (t0 + kRows - 1 < len - 1) ? t0 + kRows - 1 : len - 1;
-    const int u_hi = (last_q + wu < len - 1) ? last_q + wu : len - 1;   // inclusive
+    int u_hi = (last_q + wu < len - 1) ? last_q + wu : len - 1;   // inclusive
+    if (kMode == kGlobalRows) {
+        u_lo = 0;
+        u_hi = len - 1;
+    }
     const int nblk = (u_hi - u_lo + kKeys) / kKeys;
+
+    // global keys of this class inside the key range, as bits of u - u_lo
+    if constexpr (kMode == kBandGlobal) {
+        for (int i = tid; i < kBitWords; i += kThreads) gbits[i] = 0u;
+        __syncthreads();
+        for (int g = tid; g < ng; g += kThreads) {
+            const int x = gpos(g);
+            const int u = x / static_cast<int>(a.s);
+            if (x - u * static_cast<int>(a.s) == r && u >= u_lo && u <= u_hi)
+                atomicOr(&gbits[(u - u_lo) >> 5], 1u << ((u - u_lo) & 31));
+        }
+        __syncthreads();
+    }
+    auto is_global_key = [&](int u) {
+        return ((gbits[(u - u_lo) >> 5] >> ((u - u_lo) & 31)) & 1u) != 0u;
+    };
 
     // ---- staging of one key block: K and V rows u0 .. u0 + 63 (rows past the class are
     // loaded from its last row and written as zeros)
@@ -169,6 +209,27 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
         }
     };
 
+    // a block of global keys: tokens 64 gb .. 64 gb + 63 of this batch (zeros past ng)
+    auto load_gblock = [&](int gb) {
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
+            const int64_t off = ((bb * a.n + gpos(kKeys * gb + row)) * a.h + hh) * D + 8 * ch;
+            kreg[i] = *reinterpret_cast<const u32x4*>(k + off);
+            vreg[i] = *reinterpret_cast<const u32x4*>(v + off);
+        }
+    };
+    auto store_gblock = [&](int gb) {
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
+            const bool ok = kKeys * gb + row < ng;
+            const u32x4 z{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(klds + kpiece<D>(row, ch)) = ok ? kreg[i] : z;
+            *reinterpret_cast<u32x4*>(vlds + ring_piece<D>(row, ch)) = ok ? vreg[i] : z;
+        }
+    };
+
     f32x4 acc[kCb];
 #pragma unroll
     for (int cb = 0; cb < kCb; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -181,7 +242,8 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     // K rows of this lane's A operand within a 32-key chunk: tile 0 and tile 1
     const int krow0 = 8 * (col >> 2) + (col & 3), krow1 = krow0 + 4;
 
-    auto compute_block = [&](int u0) {
+    // gl: the staged block holds global keys u0 .. u0 + 63 (token indices), not window keys
+    auto compute_block = [&](int u0, bool gl) {
 
         // ---- scores: lane (col, grp) gets S[query tq][keys u0 + 32 c + 8 grp + 0..7]
         f32x4 s0[kChunks], s1[kChunks];
@@ -202,8 +264,10 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
         float mx = -__builtin_inff();
         const int lo = tq - w, hi = tq + wu;   // in-range keys of this query (and < len)
         const int tw = t0 + 16 * wv;           // this wave's first row
-        const bool inner = u0 >= tw + 15 - w && u0 + kKeys - 1 <= tw + wu &&
-                           u0 + kKeys - 1 < len;
+        const bool inner = kMode == kGlobalRows
+                               ? u0 + kKeys - 1 < len
+                               : (kMode == kBand && u0 >= tw + 15 - w &&
+                                  u0 + kKeys - 1 <= tw + wu && u0 + kKeys - 1 < len);
         if (inner) {
 #pragma unroll
             for (int c = 0; c < kChunks; ++c)
@@ -219,7 +283,11 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
                 for (int e = 0; e < 8; ++e) {
                     const int u = u0 + 32 * c + 8 * grp + e;
                     const float sv = e < 4 ? s0[c][e] : s1[c][e - 4];
-                    const bool ok = u >= lo && u <= hi && u < len;
+                    bool ok;
+                    if constexpr (kMode == kGlobalRows) ok = u < len;
+                    else if constexpr (kMode == kBandGlobal)
+                        ok = gl ? u < ng : (u >= lo && u <= hi && u < len && !is_global_key(u));
+                    else ok = u >= lo && u <= hi && u < len;
                     x[c][e] = ok ? sv * a.scale_log2 : -__builtin_inff();
                     mx = fmaxf(mx, x[c][e]);
                 }
@@ -263,13 +331,23 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
 
     // The next block's loads overlap this block's compute (a clamped repeat of the last
     // block when there is none, so the loads are unconditional).
+    if constexpr (kMode == kBandGlobal) {
+        const int ngb = (ng + kKeys - 1) / kKeys;
+        for (int gb = 0; gb < ngb; ++gb) {
+            load_gblock(gb);
+            store_gblock(gb);
+            __syncthreads();
+            compute_block(kKeys * gb, true);
+            __syncthreads();
+        }
+    }
     load_block(u_lo);
     for (int blk = 0; blk < nblk; ++blk) {
         const int u0 = u_lo + kKeys * blk;
         store_block(u0);
         __syncthreads();
         load_block(blk + 1 < nblk ? u0 + kKeys : u0);
-        compute_block(u0);
+        compute_block(u0, false);
         __syncthreads();
     }
 
@@ -277,9 +355,17 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     float l = l_run;
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    if (tq < len) {
+    bool store = tq < len;
+    int64_t orow_t = tq;
+    if constexpr (kMode == kGlobalRows) {
+        store = tq < ng;
+        orow_t = tq_ld;     // the token's position
+    } else if constexpr (kMode == kBandGlobal) {
+        store = store && !is_global_key(tq);   // global rows come from the global-row pass
+    }
+    if (store) {
         const float inv = 1.0f / l;
-        ST* orow = out + base + int64_t(tq) * step + 4 * grp;
+        ST* orow = out + base + orow_t * step + 4 * grp;
 #pragma unroll
         for (int cb = 0; cb < kCb; ++cb) {
             const u32x2 o{pack2(acc[cb][0] * inv, acc[cb][1] * inv, In{}),
@@ -289,7 +375,7 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     }
 }
 
-AttnArgs make_args(const Problem& p, float scale) {
+AttnArgs make_args(const Problem& p, float scale, int64_t ng = 0) {
     AttnArgs a;
     a.n = p.n;
     a.h = p.h;
@@ -303,26 +389,44 @@ AttnArgs make_args(const Problem& p, float scale) {
     a.per_head = a.cls_m * a.nqb_hi + (p.s - a.cls_m) * a.nqb_lo;
     a.groups = p.b * p.h * a.per_head;
     a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    a.ng = static_cast<int32_t>(ng);
+    a.ngb = (ng + kRows - 1) / kRows;
     return a;
 }
 
-template <class In, int D>
-hipError_t launch_t(const void* q, const void* k, const void* v, void* out, const AttnArgs& a,
-                    hipStream_t stream) {
+template <class In, int D, int kMode>
+void launch_mode(const void* q, const void* k, const void* v, void* out, const int32_t* glob,
+                 AttnArgs a, int64_t b, hipStream_t stream) {
     using ST = typename In::T;
-    launch_kernel(attn_fwd_kernel<In, D>, dim3(static_cast<uint32_t>(a.groups)), dim3(kThreads), 0,
-                  stream, static_cast<const ST*>(q), static_cast<const ST*>(k),
-                  static_cast<const ST*>(v), static_cast<ST*>(out), a);
+    if (kMode == kGlobalRows) a.groups = b * a.h * a.ngb;
+    launch_kernel(attn_fwd_kernel<In, D, kMode>, dim3(static_cast<uint32_t>(a.groups)),
+                  dim3(kThreads), 0, stream, static_cast<const ST*>(q), static_cast<const ST*>(k),
+                  static_cast<const ST*>(v), static_cast<ST*>(out), glob, a);
+}
+
+// Without global tokens one pass; with them the rows outside the global set (window and
+// global keys), then the global rows over every key - disjoint output rows, one stream.
+template <class In, int D>
+hipError_t launch_t(const void* q, const void* k, const void* v, void* out, const int32_t* glob,
+                    const AttnArgs& a, int64_t b, hipStream_t stream) {
+    if (a.ng == 0) {
+        launch_mode<In, D, kBand>(q, k, v, out, nullptr, a, b, stream);
+    } else {
+        launch_mode<In, D, kBandGlobal>(q, k, v, out, glob, a, b, stream);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        launch_mode<In, D, kGlobalRows>(q, k, v, out, glob, a, b, stream);
+    }
     return hipGetLastError();
 }
 
 template <class In>
-hipError_t launch_d(const void* q, const void* k, const void* v, void* out, const AttnArgs& a,
-                    int64_t d, hipStream_t stream) {
+hipError_t launch_d(const void* q, const void* k, const void* v, void* out, const int32_t* glob,
+                    const AttnArgs& a, int64_t b, int64_t d, hipStream_t stream) {
     switch (d) {
-    case 32: return launch_t<In, 32>(q, k, v, out, a, stream);
-    case 64: return launch_t<In, 64>(q, k, v, out, a, stream);
-    case 128: return launch_t<In, 128>(q, k, v, out, a, stream);
+    case 32: return launch_t<In, 32>(q, k, v, out, glob, a, b, stream);
+    case 64: return launch_t<In, 64>(q, k, v, out, glob, a, b, stream);
+    case 128: return launch_t<In, 128>(q, k, v, out, glob, a, b, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -344,15 +448,23 @@ bool attention_supported(const Problem& p, int dt, const void* q, const void* k,
     return a.groups < (int64_t(1) << 31);
 }
 
+// With global tokens the key range of a workgroup (64 + w + w_upper keys) must fit the
+// LDS bitmap of global keys.
+bool attention_global_supported(const Problem& p, int64_t ng) {
+    return 64 + p.w + p.wu <= int64_t(kBitWords) * 32 && ng >= 0 && ng <= p.n &&
+           p.b * p.h * ((ng + kRows - 1) / kRows) < (int64_t(1) << 31);
+}
+
 int64_t attention_workgroups(const Problem& p) { return make_args(p, 1.0f).groups; }
 
 hipError_t launch_attention(const void* q, const void* k, const void* v, void* out,
-                            const Problem& p, float scale, int dt, hipStream_t stream) {
-    const AttnArgs a = make_args(p, scale);
+                            const int32_t* glob, int64_t ng, const Problem& p, float scale,
+                            int dt, hipStream_t stream) {
+    const AttnArgs a = make_args(p, scale, ng);
     if (a.groups == 0) return hipSuccess;
     switch (dt) {
-    case kF16: return launch_d<F16>(q, k, v, out, a, p.d, stream);
-    case kBF16: return launch_d<BF16>(q, k, v, out, a, p.d, stream);
+    case kF16: return launch_d<F16>(q, k, v, out, glob, a, p.b, p.d, stream);
+    case kBF16: return launch_d<BF16>(q, k, v, out, glob, a, p.b, p.d, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -59,9 +59,12 @@ hipError_t launch_dropout(const void* probs, const float* rand, void* out, const
 // tensors): 256-thread workgroups of 64 class rows, keys staged 64 at a time.
 bool attention_supported(const Problem& p, int dt, const void* q, const void* k, const void* v,
                          const void* out);
+bool attention_global_supported(const Problem& p, int64_t ng);
 int64_t attention_workgroups(const Problem& p);
+// glob: ng int32 positions per batch on the device (ignored when ng == 0)
 hipError_t launch_attention(const void* q, const void* k, const void* v, void* out,
-                            const Problem& p, float scale, int dt, hipStream_t stream);
+                            const int32_t* glob, int64_t ng, const Problem& p, float scale,
+                            int dt, hipStream_t stream);
 
 // qk on MFMA (f16 / bf16 inputs, d in {32, 64, 128}, 16-byte aligned pointers).
 constexpr int kQkRows = 128;                 // rows per tile

@@ -37,7 +37,8 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for want in ("diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax",
                  "diagmm_banded_softmax_backward", "diagmm_banded_softmax_masked",
-                 "diagmm_banded_dropout", "diagmm_banded_attention", "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
+                 "diagmm_banded_dropout", "diagmm_banded_attention",
+                 "diagmm_banded_attention_global", "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
                  "diagmm_plan"):
         assert want in names
 
@@ -48,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dm.diagmm_abi_version() == 6
+    assert dm.diagmm_abi_version() == 7
     seen = set()
     for st in range(7):
         s = lib.diagmm_status_string(st).decode()
@@ -126,6 +127,14 @@ def test_validation_errors_are_reported_without_launching(lib):
     assert at(Q_, K_, V_, O_, 1, 8, 1, 48, 2, 2, 0, 0.125, 1, None) == ERR_UNSUPPORTED  # d
     assert at(Q_ + 2, K_, V_, O_, 1, 8, 1, 64, 2, 2, 0, 0.125, 1, None) == ERR_UNSUPPORTED
     assert "diagmm_banded_attention" in lib.diagmm_last_error().decode()
+    ag = lib.diagmm_banded_attention_global
+    G_ = FAKE + (1 << 39)
+    assert ag(Q_, K_, V_, O_, 0, 2, 1, 8, 1, 64, 2, 2, 0, 0.125, 1, None) == ERR_NULL
+    assert ag(Q_, K_, V_, O_, G_, 9, 1, 8, 1, 64, 2, 2, 0, 0.125, 1, None) == ERR_SHAPE   # ng > n
+    assert ag(Q_, K_, V_, O_, G_, -1, 1, 8, 1, 64, 2, 2, 0, 0.125, 1, None) == ERR_SHAPE
+    assert ag(Q_, K_, V_, G_ - 8, G_, 2, 1, 8, 1, 64, 2, 2, 0, 0.125, 1, None) == ERR_ALIAS
+    assert ag(Q_, K_, V_, O_, G_, 2, 1, 8, 1, 64, 9000, 9000, 0, 0.125, 1, None) == ERR_UNSUPPORTED
+    assert "diagmm_banded_attention_global" in lib.diagmm_last_error().decode()
 
 
 def test_empty_problems_are_noops(lib):

@@ -44,6 +44,7 @@ DILATIONS = (0, 3)
 K = W + WU + 1
 SCALE = 0.125
 E = 2  # bytes per f16 element
+NG = 8  # global tokens of the global-token timing (positions spread over the sequence)
 
 
 def in_range_per_head(n, w, wu, dil):
@@ -69,6 +70,10 @@ def op_costs(dil):
         "dropout": {"bytes": cnt * (E + 4) + band, "flops": 0},
         # attention in one pass: Q, K, V read and the output written; both products' flops
         "attention": {"bytes": 4 * dense, "flops": 4 * D * cnt},
+        # with NG global tokens: every row also reads the global keys (counted once per
+        # launch), the global rows attend every key
+        "attention_global": {"bytes": 4 * dense + B * NG * 4,
+                             "flops": 4 * D * (cnt + B * H * (N * NG + NG * N))},
     }
 
 
@@ -330,7 +335,9 @@ def main():
         t["dP"] = dm.diagmm_qk(t["do"], t["v"], W, WU, 0, 0.0)
         t["dS"] = torch.empty_like(t["dP"])
         t["rand"] = torch.rand(t["dP"].shape, generator=gen, device=dev, dtype=torch.float32)
-    for op in ("softmax_bwd", "softmax_masked", "dropout", "attention"):
+    glob = torch.tensor([[0] + [(j * N) // NG + 7 for j in range(1, NG - 1)] + [N - 1]],
+                        dtype=torch.int32, device=dev).expand(B, NG).contiguous()
+    for op in ("softmax_bwd", "softmax_masked", "dropout", "attention", "attention_global"):
         for dil in DILATIONS:
             def run(t):
                 if op == "softmax_bwd":
@@ -342,9 +349,12 @@ def main():
                 elif op == "dropout":
                     dm.diagmm_banded_dropout(t[f"S{dil}"], t["rand"], W, WU, dil, 0.1,
                                              out=t["dS"])
-                else:
+                elif op == "attention":
                     dm.diagmm_banded_attention(t["q"], t["k"], t["v"], W, WU, dil, SCALE,
                                                out=t[f"O{dil}"])
+                else:
+                    dm.diagmm_banded_attention_global(t["q"], t["k"], t["v"], glob, W, WU, dil,
+                                                      SCALE, out=t[f"O{dil}"])
             for i in range(args.warmup):
                 run(sets[i % len(sets)])
             torch.cuda.synchronize()
@@ -353,22 +363,25 @@ def main():
                 run(sets[i % len(sets)])
             torch.cuda.synchronize()
             dm.diagmm_timing_end()
-            recs = [ms for name, ms in dm.diagmm_timing_read() if name == op]
-            assert len(recs) == args.steps, (len(recs), args.steps)
-            ms = sum(recs) / len(recs)
+            tag = "attention" if op == "attention_global" else op
+            recs = [ms for name, ms in dm.diagmm_timing_read() if name == tag]
+            per_call = len(recs) // args.steps   # the global-token call runs two kernels
+            assert per_call >= 1 and len(recs) == per_call * args.steps, (len(recs), args.steps)
+            ms = sum(recs) / args.steps
             c = op_costs(dil)[op]
             extra[f"{op}_dil{dil}"] = {
                 "us": round(ms * 1e3, 2),
                 "GB/s": round(c["bytes"] / (ms * 1e-3) / 1e9, 1),
                 "bytes": c["bytes"],
             }
-            if op == "attention":
-                three = sum(per_op[f"{o}_dil{dil}"]["us"] for o in ("qk", "softmax", "pv"))
+            if op in ("attention", "attention_global"):
                 extra[f"{op}_dil{dil}"].update({
                     "TFLOP/s": round(c["flops"] / (ms * 1e-3) / 1e12, 2),
                     "flops": c["flops"],
-                    "three_calls_us": round(three, 2),
                 })
+            if op == "attention":
+                three = sum(per_op[f"{o}_dil{dil}"]["us"] for o in ("qk", "softmax", "pv"))
+                extra[f"{op}_dil{dil}"]["three_calls_us"] = round(three, 2)
     for t in sets:
         del t["dP"], t["dS"], t["rand"]
     ceiling = practical_ceiling(torch, dev, stream)

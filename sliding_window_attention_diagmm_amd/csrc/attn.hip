@@ -69,7 +69,7 @@ struct AttnArgs {
     int64_t groups;           // workgroups in the grid
     float scale_log2;         // scale * log2(e)
     int32_t ng;               // global tokens per batch (0: none)
-    int64_t ngb;              // 64-row blocks of global rows per (batch, head)
+    int64_t ngb;              // 16-row blocks of global rows per (batch, head)
 };
 
 // Kernel modes: the window only; the window plus the global keys for rows outside the
@@ -102,11 +102,15 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     using ST = typename In::T;
     using V = typename Mfma<In>::V;
     constexpr int kPieces = D / 8;                       // 16-byte pieces per row
-    constexpr int kStage = kKeys * kPieces / kThreads;   // pieces per thread per tensor
+    // the global-row mode splits the keys over the four waves: each wave stages its own
+    // blocks (64 threads) in its own LDS region
+    constexpr int kSplit = kMode == kGlobalRows ? 4 : 1;
+    constexpr int kStageThreads = kThreads / kSplit;
+    constexpr int kStage = kKeys * kPieces / kStageThreads;   // pieces per thread per tensor
     constexpr int kQk = D / 32;                          // MFMA K-steps over the channels
     constexpr int kCb = D / 16;                          // 16-channel output blocks
-    __shared__ __attribute__((aligned(16))) unsigned char klds[kKeys * 2 * D];
-    __shared__ __attribute__((aligned(16))) unsigned char vlds[kKeys * 2 * D];
+    __shared__ __attribute__((aligned(16))) unsigned char klds[kSplit * kKeys * 2 * D];
+    __shared__ __attribute__((aligned(16))) unsigned char vlds[kSplit * kKeys * 2 * D];
     __shared__ uint32_t gbits[kMode == kBandGlobal ? kBitWords : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -138,7 +142,8 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     const int64_t bb = bh / a.h, hh = bh - bb * a.h;
     const int len = kMode == kGlobalRows ? static_cast<int>(a.n)
                                          : static_cast<int>(a.cls_q + (r < a.cls_m ? 1 : 0));
-    const int t0 = static_cast<int>(qb) * kRows;
+    // global rows: blocks of 16, all four waves on the same rows
+    const int t0 = static_cast<int>(qb) * (kMode == kGlobalRows ? 16 : kRows);
     // element offset of class row t: base + t * step
     const int64_t base = ((bb * a.n + r) * a.h + hh) * D;
     const int64_t step = (kMode == kGlobalRows ? 1 : a.s) * a.h * D;
@@ -150,7 +155,7 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     };
 
     // ---- this lane's query row as the B operand of S^T (channels 32 kk + 8 grp .. +7)
-    const int tq = t0 + 16 * wv + col;
+    const int tq = t0 + (kMode == kGlobalRows ? 0 : 16 * wv) + col;
     const int tq_ld = kMode == kGlobalRows ? gpos(tq) : (tq < len ? tq : len - 1);
     V qop[kQk];
 #pragma unroll
@@ -162,11 +167,18 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     int u_lo = t0 - w > 0 ? t0 - w : 0;
     const int last_q = (t0 + kRows - 1 < len - 1) ? t0 + kRows - 1 : len - 1;
     int u_hi = (last_q + wu < len - 1) ? last_q + wu : len - 1;   // inclusive
+    int nblk = (u_hi - u_lo + kKeys) / kKeys;
     if (kMode == kGlobalRows) {
-        u_lo = 0;
+        // wave wv sweeps the wv-th quarter of the key blocks; the same count for every
+        // wave (blocks past the sequence are masked), so the barriers match
+        const int per = ((len + kKeys - 1) / kKeys + kSplit - 1) / kSplit;
+        u_lo = wv * per * kKeys;
         u_hi = len - 1;
+        nblk = per;
     }
-    const int nblk = (u_hi - u_lo + kKeys) / kKeys;
+    const int stid = kMode == kGlobalRows ? lane : tid;   // staging thread index
+    unsigned char* const kw = klds + (kMode == kGlobalRows ? wv : 0) * kKeys * 2 * D;
+    unsigned char* const vw = vlds + (kMode == kGlobalRows ? wv : 0) * kKeys * 2 * D;
 
     // global keys of this class inside the key range, as bits of u - u_lo
     if constexpr (kMode == kBandGlobal) {
@@ -190,7 +202,7 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     auto load_block = [&](int u0) {
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
-            const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
+            const int pc = stid + kStageThreads * i, row = pc / kPieces, ch = pc % kPieces;
             int u = u0 + row;
             u = u < len ? u : len - 1;
             const int64_t off = base + int64_t(u) * step + 8 * ch;
@@ -201,11 +213,11 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     auto store_block = [&](int u0) {
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
-            const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
+            const int pc = stid + kStageThreads * i, row = pc / kPieces, ch = pc % kPieces;
             const bool ok = u0 + row < len;
             const u32x4 z{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(klds + kpiece<D>(row, ch)) = ok ? kreg[i] : z;
-            *reinterpret_cast<u32x4*>(vlds + ring_piece<D>(row, ch)) = ok ? vreg[i] : z;
+            *reinterpret_cast<u32x4*>(kw + kpiece<D>(row, ch)) = ok ? kreg[i] : z;
+            *reinterpret_cast<u32x4*>(vw + ring_piece<D>(row, ch)) = ok ? vreg[i] : z;
         }
     };
 
@@ -252,8 +264,8 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
             s0[c] = s1[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < kQk; ++kk) {
-                const V a0 = *reinterpret_cast<const V*>(klds + kpiece<D>(32 * c + krow0, 4 * kk + grp));
-                const V a1 = *reinterpret_cast<const V*>(klds + kpiece<D>(32 * c + krow1, 4 * kk + grp));
+                const V a0 = *reinterpret_cast<const V*>(kw + kpiece<D>(32 * c + krow0, 4 * kk + grp));
+                const V a1 = *reinterpret_cast<const V*>(kw + kpiece<D>(32 * c + krow1, 4 * kk + grp));
                 s0[c] = Mfma<In>::run(a0, qop[kk], s0[c]);
                 s1[c] = Mfma<In>::run(a1, qop[kk], s1[c]);
             }
@@ -320,7 +332,7 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
             const u32x4 pb{pack2(p[0], p[1], In{}), pack2(p[2], p[3], In{}),
                            pack2(p[4], p[5], In{}), pack2(p[6], p[7], In{})};
             const V bop = __builtin_bit_cast(V, pb);
-            const unsigned char* rp = vlds + (32 * c + 8 * grp) * (2 * D);
+            const unsigned char* rp = vw + (32 * c + 8 * grp) * (2 * D);
 #pragma unroll
             for (int cb = 0; cb < kCb; ++cb) {
                 const V av = tr_read8<V, D>(rp + aoff[cb]);
@@ -355,12 +367,51 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     float l = l_run;
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    bool store = tq < len;
-    int64_t orow_t = tq;
     if constexpr (kMode == kGlobalRows) {
-        store = tq < ng;
-        orow_t = tq_ld;     // the token's position
-    } else if constexpr (kMode == kBandGlobal) {
+        // merge the four waves' partial softmax states of the same 16 rows: scale each
+        // by 2^(m_w - max m), add, divide (LDS is free: the loop ended on a barrier)
+        constexpr int S = kCb * 4 + 2;
+        float* mb = reinterpret_cast<float*>(klds);
+        float* mine = mb + (wv * 64 + lane) * S;
+#pragma unroll
+        for (int cb = 0; cb < kCb; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mine[cb * 4 + e] = acc[cb][e];
+        mine[kCb * 4] = m_run;
+        mine[kCb * 4 + 1] = l;
+        __syncthreads();
+        if (wv != 0 || tq >= ng) return;
+        float M = -__builtin_inff();
+#pragma unroll
+        for (int w4 = 0; w4 < kSplit; ++w4) M = fmaxf(M, mb[(w4 * 64 + lane) * S + kCb * 4]);
+        float L = 0.0f;
+        f32x4 A[kCb];
+#pragma unroll
+        for (int cb = 0; cb < kCb; ++cb) A[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w4 = 0; w4 < kSplit; ++w4) {
+            const float* o = mb + (w4 * 64 + lane) * S;
+            const float f = o[kCb * 4] == -__builtin_inff()
+                                ? 0.0f : __builtin_amdgcn_exp2f(o[kCb * 4] - M);
+            L += o[kCb * 4 + 1] * f;
+#pragma unroll
+            for (int cb = 0; cb < kCb; ++cb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) A[cb][e] += o[cb * 4 + e] * f;
+        }
+        const float inv = 1.0f / L;
+        ST* orow = out + base + int64_t(tq_ld) * step + 4 * grp;
+#pragma unroll
+        for (int cb = 0; cb < kCb; ++cb) {
+            const u32x2 o2{pack2(A[cb][0] * inv, A[cb][1] * inv, In{}),
+                           pack2(A[cb][2] * inv, A[cb][3] * inv, In{})};
+            *reinterpret_cast<u32x2*>(orow + 16 * cb) = o2;
+        }
+        return;
+    }
+    bool store = tq < len;
+    const int64_t orow_t = tq;
+    if constexpr (kMode == kBandGlobal) {
         store = store && !is_global_key(tq);   // global rows come from the global-row pass
     }
     if (store) {
@@ -390,7 +441,7 @@ AttnArgs make_args(const Problem& p, float scale, int64_t ng = 0) {
     a.groups = p.b * p.h * a.per_head;
     a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
     a.ng = static_cast<int32_t>(ng);
-    a.ngb = (ng + kRows - 1) / kRows;
+    a.ngb = (ng + 15) / 16;   // global rows are taken 16 per workgroup
     return a;
 }
 
@@ -452,7 +503,7 @@ bool attention_supported(const Problem& p, int dt, const void* q, const void* k,
 // LDS bitmap of global keys.
 bool attention_global_supported(const Problem& p, int64_t ng) {
     return 64 + p.w + p.wu <= int64_t(kBitWords) * 32 && ng >= 0 && ng <= p.n &&
-           p.b * p.h * ((ng + kRows - 1) / kRows) < (int64_t(1) << 31);
+           p.b * p.h * ((ng + 15) / 16) < (int64_t(1) << 31);
 }
 
 int64_t attention_workgroups(const Problem& p) { return make_args(p, 1.0f).groups; }

@@ -358,15 +358,15 @@ def main():
             for i in range(args.warmup):
                 run(sets[i % len(sets)])
             torch.cuda.synchronize()
-            dm.diagmm_timing_begin(args.steps)
+            per_call = 2 if op == "attention_global" else 1   # launches per call
+            dm.diagmm_timing_begin(args.steps * per_call)
             for i in range(args.steps):
                 run(sets[i % len(sets)])
             torch.cuda.synchronize()
             dm.diagmm_timing_end()
             tag = "attention" if op == "attention_global" else op
             recs = [ms for name, ms in dm.diagmm_timing_read() if name == tag]
-            per_call = len(recs) // args.steps   # the global-token call runs two kernels
-            assert per_call >= 1 and len(recs) == per_call * args.steps, (len(recs), args.steps)
+            assert len(recs) == per_call * args.steps, (len(recs), per_call, args.steps)
             ms = sum(recs) / args.steps
             c = op_costs(dil)[op]
             extra[f"{op}_dil{dil}"] = {

@@ -276,10 +276,17 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
         float mx = -__builtin_inff();
         const int lo = tq - w, hi = tq + wu;   // in-range keys of this query (and < len)
         const int tw = t0 + 16 * wv;           // this wave's first row
-        const bool inner = kMode == kGlobalRows
-                               ? u0 + kKeys - 1 < len
-                               : (kMode == kBand && u0 >= tw + 15 - w &&
-                                  u0 + kKeys - 1 <= tw + wu && u0 + kKeys - 1 < len);
+        // (with global tokens: a window block none of whose keys is global; the bitmap
+        // words covering keys u0 .. u0 + 63 lie inside the range when the window test holds)
+        auto no_global_keys = [&]() {
+            const int o = u0 - u_lo, wa = o >> 5, wb = (o + kKeys - 1) >> 5;
+            return (gbits[wa] | gbits[wa + 1] | gbits[wb]) == 0u;
+        };
+        bool inner;
+        if constexpr (kMode == kGlobalRows) inner = u0 + kKeys - 1 < len;
+        else
+            inner = !gl && u0 >= tw + 15 - w && u0 + kKeys - 1 <= tw + wu &&
+                    u0 + kKeys - 1 < len && (kMode == kBand || no_global_keys());
         if (inner) {
 #pragma unroll
             for (int c = 0; c < kChunks; ++c)

@@ -26,6 +26,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / 64;
 constexpr int kPer = 3;                        // pieces per lane in the group kernel
+constexpr int kMaskWin = 4096;                 // mask floats a workgroup stages (dilated rows)
 
 template <class T> struct Elem;
 template <> struct Elem<F16> {
@@ -122,11 +123,42 @@ softmax_masked_group_kernel(const typename T::T* scores, typename T::T* probs,
     // Without dilation a piece's slots have consecutive keys: a piece wholly in range reads
     // its mask values as one run (the loads merge into wide ones), the others element by
     // element.
+    // With dilation the keys of a piece are s apart: the workgroup first copies the
+    // contiguous run of mask values its rows can reach (flat positions mrow - w s ..
+    // mrow + w_upper s of its first and last row) into LDS with coalesced loads, when the
+    // run fits, and gathers from there.
+    __shared__ float mwin[kMaskWin];
+    int64_t lo = 0;
+    bool staged = false;
+    if (p.s > 1) {
+        const int64_t r0 = int64_t(blockIdx.x) * kWavesPerBlock * kRowsPerWave;
+        const int64_t r1 = (r0 + kWavesPerBlock * kRowsPerWave - 1 < nrows - 1)
+                               ? r0 + kWavesPerBlock * kRowsPerWave - 1 : nrows - 1;
+        const int64_t m0 = div32(rd.h, static_cast<uint32_t>(r0));
+        const int64_t m1 = div32(rd.h, static_cast<uint32_t>(r1));
+        lo = m0 - p.w * p.s;
+        lo = lo < 0 ? 0 : lo;
+        int64_t hi = m1 + p.wu * p.s;
+        hi = hi > p.b * p.n - 1 ? p.b * p.n - 1 : hi;
+        staged = hi - lo + 1 <= kMaskWin;            // the same for every thread
+        if (staged) {
+            for (int64_t x = threadIdx.x; x <= hi - lo; x += kThreads) mwin[x] = key_mask[lo + x];
+            __syncthreads();
+        }
+    }
     float mk[kPer][kVec];
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
         const int base = (t + L * q) * kVec - sh;
-        if (p.s == 1 && base >= rg.k_lo && base + kVec <= rg.k_hi) {
+        if (staged) {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                const int k = base + e;
+                const bool in = k >= rg.k_lo && k < rg.k_hi;
+                const int64_t off = in ? static_cast<int64_t>(k - p.w) * p.s : 0;
+                mk[q][e] = mwin[rg.mrow + off - lo];
+            }
+        } else if (p.s == 1 && base >= rg.k_lo && base + kVec <= rg.k_hi) {
             const float* mp = key_mask + rg.mrow + (base - p.w);   // consecutive, merged
 #pragma unroll
             for (int e = 0; e < kVec; ++e) mk[q][e] = mp[e];

@@ -58,6 +58,11 @@ template <> struct Mfma<BF16> {
 
 constexpr int kRows = 64;                   // class rows per workgroup, 16 per wave
 constexpr int kThreads = kRows / 16 * 64;
+// Workgroup size of a mode: the global-row pass splits the keys over 8 waves where their
+// LDS blocks fit (d <= 64), else over 4.
+__host__ __device__ constexpr int mode_threads(int mode, int d) {
+    return mode == 2 && d <= 64 ? 512 : kThreads;
+}
 constexpr int kKeys = 64;                   // keys per LDS block
 constexpr int kChunks = kKeys / 32;         // 32-key chunks per block
 
@@ -95,17 +100,18 @@ __device__ __forceinline__ uint32_t pack2(float a, float b, BF16) {
 }
 
 template <class In, int D, int kMode>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(mode_threads(kMode, D))
 attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __restrict__ k,
                 const typename In::T* __restrict__ v, typename In::T* __restrict__ out,
                 const int32_t* __restrict__ glob, AttnArgs a) {
     using ST = typename In::T;
     using V = typename Mfma<In>::V;
     constexpr int kPieces = D / 8;                       // 16-byte pieces per row
-    // the global-row mode splits the keys over the four waves: each wave stages its own
-    // blocks (64 threads) in its own LDS region
-    constexpr int kSplit = kMode == kGlobalRows ? 4 : 1;
-    constexpr int kStageThreads = kThreads / kSplit;
+    // the global-row mode splits the keys over the waves (8, or 4 for d = 128): each wave
+    // stages its own blocks (64 threads) in its own LDS region
+    constexpr int kT = mode_threads(kMode, D);
+    constexpr int kSplit = kMode == kGlobalRows ? kT / 64 : 1;
+    constexpr int kStageThreads = kT / kSplit;
     constexpr int kStage = kKeys * kPieces / kStageThreads;   // pieces per thread per tensor
     constexpr int kQk = D / 32;                          // MFMA K-steps over the channels
     constexpr int kCb = D / 16;                          // 16-channel output blocks
@@ -142,7 +148,7 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     const int64_t bb = bh / a.h, hh = bh - bb * a.h;
     const int len = kMode == kGlobalRows ? static_cast<int>(a.n)
                                          : static_cast<int>(a.cls_q + (r < a.cls_m ? 1 : 0));
-    // global rows: blocks of 16, all four waves on the same rows
+    // global rows: blocks of 16, all waves on the same rows
     const int t0 = static_cast<int>(qb) * (kMode == kGlobalRows ? 16 : kRows);
     // element offset of class row t: base + t * step
     const int64_t base = ((bb * a.n + r) * a.h + hh) * D;
@@ -169,7 +175,7 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     int u_hi = (last_q + wu < len - 1) ? last_q + wu : len - 1;   // inclusive
     int nblk = (u_hi - u_lo + kKeys) / kKeys;
     if (kMode == kGlobalRows) {
-        // wave wv sweeps the wv-th quarter of the key blocks; the same count for every
+        // wave wv sweeps the wv-th share of the key blocks; the same count for every
         // wave (blocks past the sequence are masked), so the barriers match
         const int per = ((len + kKeys - 1) / kKeys + kSplit - 1) / kSplit;
         u_lo = wv * per * kKeys;
@@ -375,7 +381,7 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     if constexpr (kMode == kGlobalRows) {
-        // merge the four waves' partial softmax states of the same 16 rows: scale each
+        // merge the waves' partial softmax states of the same 16 rows: scale each
         // by 2^(m_w - max m), add, divide (LDS is free: the loop ended on a barrier)
         constexpr int S = kCb * 4 + 2;
         float* mb = reinterpret_cast<float*>(klds);
@@ -458,7 +464,7 @@ void launch_mode(const void* q, const void* k, const void* v, void* out, const i
     using ST = typename In::T;
     if (kMode == kGlobalRows) a.groups = b * a.h * a.ngb;
     launch_kernel(attn_fwd_kernel<In, D, kMode>, dim3(static_cast<uint32_t>(a.groups)),
-                  dim3(kThreads), 0, stream, static_cast<const ST*>(q), static_cast<const ST*>(k),
+                  dim3(mode_threads(kMode, D)), 0, stream, static_cast<const ST*>(q), static_cast<const ST*>(k),
                   static_cast<const ST*>(v), static_cast<ST*>(out), glob, a);
 }
 

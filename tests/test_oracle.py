@@ -525,6 +525,36 @@ def test_dropout_keeps_by_comparison_and_scales():
                        oracle.convert(d64, torch.float16))
 
 
+def test_dropout_tie_drops():
+    """The page keeps a slot when its uniform is strictly greater than p (`gt`), so a
+    uniform equal to p, as the float32 value the call takes, drops; the float32 values
+    just above keep.  Uniform float32 draws almost never hit p exactly, so the ties are
+    planted: every third slot holds float32(p), the rest the next float32 up or down."""
+    n, w, wu = 40, 5, 5
+    K = w + wu + 1
+    g = datagen.rng(82)
+    S = datagen.normal(g, (1, n, 2, K), "f32")
+    P = oracle.softmax(S, w, wu, 0, out_dtype=torch.float64)
+    ones = torch.ones(1, n, 1, 1)
+    inr = (oracle.qk(ones, ones, w, wu, padding=0.0) == 1).expand_as(P)
+    for p in (0.1, 0.5):
+        pf = np.float32(p)
+        up = np.nextafter(pf, np.float32(1))
+        dn = np.nextafter(pf, np.float32(0))
+        idx = np.arange(P.numel()).reshape(P.shape) % 3
+        r = np.where(idx == 0, pf, np.where(idx == 1, up, dn)).astype(np.float32)
+        rand = torch.from_numpy(r)
+        out = oracle.dropout(P, rand, w, wu, 0, p=p, out_dtype=torch.float64)
+        tie = torch.from_numpy(idx == 0)
+        above = torch.from_numpy(idx == 1)
+        assert torch.all(out[tie] == 0)                    # rand == p drops
+        assert torch.all(out[~above] == 0)                 # rand < p drops
+        kept = above & inr
+        assert int(kept.sum()) > 0
+        np.testing.assert_allclose(out[kept].numpy(), (P[kept] / (1.0 - float(pf))).numpy(),
+                                   rtol=1e-15)
+
+
 # ---------------------------------------------------- softmax backward pins
 # The gradient of the banded softmax with respect to its stored scores is not printed
 # on the pages; it is the chain rule through their softmax recipe.  Three independent

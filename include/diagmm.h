@@ -252,7 +252,8 @@ typedef struct {
     int64_t strip_workgroups; /* pv, pvT: workgroups given to each strip (the row blocks of
                                  one residue class of one (batch, head)) when the tiles are
                                  split strip by strip; 0 when they are balanced over all
-                                 workgroups at once */
+                                 workgroups at once.  qk: the row ranges each strip is cut
+                                 into (a workgroup takes one range, or a run of them) */
 } diagmm_plan_t;
 
 diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,

@@ -84,6 +84,21 @@ hipError_t launch_qk_mfma(const void* q, const void* k, void* band, const Proble
                           const QkTilePlan& tp, int in_dt, int out_dt, uint32_t pad,
                           hipStream_t stream);
 
+// qk streaming (f16 / bf16 in and out, d = 64, 16-byte aligned pointers):
+// strips cut into ranges of at most 208 class rows, one workgroup per compute unit.
+struct QkStreamPlan {
+    int64_t g = 0;              // ranges per strip
+    int64_t ranges = 0;         // strips * g
+    int64_t workgroups = 0;
+    int64_t rows_per_range = 0; // longest range (class rows)
+    int64_t lds_bytes = 0;
+    bool ok = false;
+};
+QkStreamPlan plan_qk_stream(const Problem& p, int in_dt, int out_dt);
+hipError_t launch_qk_stream(const void* q, const void* k, void* band, const Problem& p,
+                            const QkStreamPlan& sp, int in_dt, uint32_t pad,
+                            hipStream_t stream);
+
 // pv on MFMA (f16 / bf16 inputs, d in {32, 64, 128}, 16-byte aligned pointers).
 constexpr int kPvRows = 64;
 constexpr int64_t kPvLdsBytes = 160 * 1024;

@@ -14,6 +14,13 @@ bool force_simple() {
     return e && std::strcmp(e, "simple") == 0;
 }
 
+// DIAGMM_QK=tiles keeps qk on the persistent tile kernel where the streaming one would
+// run (a comparison switch).
+static bool qk_tiles_forced() {
+    const char* e = std::getenv("DIAGMM_QK");
+    return e && std::strcmp(e, "tiles") == 0;
+}
+
 namespace {
 
 Plan simple_plan(const Problem& p, int64_t cols, const char* name) {
@@ -40,6 +47,21 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 Plan plan_qk(const Problem& p, int in_dt, int out_dt) {
     if (force_simple() || !mfma_dtype(in_dt) || !mfma_depth(p.d))
         return simple_plan(p, p.K, "qk_simple");
+    const QkStreamPlan sp = plan_qk_stream(p, in_dt, out_dt);
+    if (sp.ok && !qk_tiles_forced()) {
+        Plan pl;
+        pl.family = Family::kQkStream;
+        pl.kernel = "qk_stream";
+        pl.rows_per_tile = sp.rows_per_range;
+        pl.slots_per_tile = p.K;
+        pl.tiles = sp.ranges;
+        pl.workgroups = sp.workgroups;
+        pl.threads = 768;
+        pl.lds_bytes = sp.lds_bytes;
+        pl.residues = p.s < p.n ? p.s : (p.n > 0 ? p.n : 1);
+        pl.strip_wgs = sp.g;
+        return pl;
+    }
     const QkTilePlan tp = plan_qk_mfma(p, out_dt);
     if (!tp.ok) return simple_plan(p, p.K, "qk_simple");
     Plan pl;
@@ -122,7 +144,10 @@ Plan plan_softmax(const Problem& p, int in_dt, int out_dt) {
 
 hipError_t run_qk(const Plan& plan, const void* q, const void* k, void* band, const Problem& p,
                   int in_dt, int out_dt, uint32_t pad, hipStream_t stream) {
-    // The tiled kernel moves 16-byte pieces; other pointers take the general path.
+    // The tiled kernels move 16-byte pieces; other pointers take the general path.
+    if (plan.family == Family::kQkStream && aligned16(q) && aligned16(k) && aligned16(band))
+        return launch_qk_stream(q, k, band, p, plan_qk_stream(p, in_dt, out_dt), in_dt, pad,
+                                stream);
     if (plan.family == Family::kQkMfma && aligned16(q) && aligned16(k) && aligned16(band))
         return launch_qk_mfma(q, k, band, p, plan_qk_mfma(p, out_dt), in_dt, out_dt, pad, stream);
     return launch_qk_simple(q, k, band, p, in_dt, out_dt, pad, stream);

@@ -10,6 +10,7 @@ namespace diagmm {
 enum class Family {
     kSimple,      // element per thread (any shape)
     kQkMfma,      // qk: MFMA on dense 16x16 sub-tiles, LDS-staged band store
+    kQkStream,    // qk: balanced row ranges, keys streamed, staged 256-byte row runs
     kPvMfma,      // pv: band tile un-skewed into MFMA operands
     kPvTMfma,     // pvT: transposed band tile into MFMA operands
     kSoftmaxRow,  // softmax: one workgroup per band row

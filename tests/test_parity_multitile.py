@@ -39,7 +39,8 @@ def test_grid_cap_shapes_the_plan(monkeypatch):
     monkeypatch.setenv("DIAGMM_MAX_WORKGROUPS", "8")
     for mode in ("qk", "pv", "pvT"):
         pl = dm.diagmm_plan(mode, 1, 2048, 3, 64, 256, 256, 0, torch.float16)
-        assert pl["workgroups"] <= 8 and pl["tiles"] >= 4 * pl["workgroups"], (mode, pl)
+        # qk's units are row ranges of at most 208 rows (30 here), pv/pvT's 64-row tiles
+        assert pl["workgroups"] <= 8 and pl["tiles"] >= 3 * pl["workgroups"], (mode, pl)
 
 
 def test_strip_split_choice(monkeypatch):
@@ -63,7 +64,7 @@ def test_strip_split_choice(monkeypatch):
     for mode in ("pv", "pvT"):
         assert dm.diagmm_plan(mode, 2, 1100, 1, 64, 96, 30, 4,
                               torch.bfloat16)["strip_workgroups"] == 2
-    # qk takes the strip split whenever it does not lengthen the longest tile list
+    # qk cuts every strip into as many row ranges as the workgroups allow (one each)
     assert dm.diagmm_plan("qk", 2, 1100, 1, 64, 96, 30, 4,
                           torch.bfloat16)["strip_workgroups"] == 2
     monkeypatch.delenv("DIAGMM_MAX_WORKGROUPS")
@@ -106,9 +107,11 @@ def test_small_grid_matches_oracle(case, monkeypatch):
 
 
 def test_qk_takes_the_fewest_slot_chunks_when_tiles_suffice(monkeypatch):
-    """One chunk at the benchmark shape (384 tiles for 256 units); more only when the
-    fewest leave under 1.4 tiles per unit (a 65-slot band of 512 positions: 4 tiles)."""
+    """The persistent tile kernel (f32 outputs, or DIAGMM_QK=tiles): one chunk at the
+    benchmark shape (384 tiles for 256 units); more only when the fewest leave under 1.4
+    tiles per unit (a 65-slot band of 512 positions: 4 tiles)."""
     monkeypatch.delenv("DIAGMM_MAX_WORKGROUPS", raising=False)
+    monkeypatch.setenv("DIAGMM_QK", "tiles")
     for dil in (0, 3):
         pl = dm.diagmm_plan("qk", 1, 4096, 12, 64, 256, 256, dil, torch.float16)
         if pl["workgroups"] == 256:
@@ -117,3 +120,26 @@ def test_qk_takes_the_fewest_slot_chunks_when_tiles_suffice(monkeypatch):
     monkeypatch.setenv("DIAGMM_MAX_WORKGROUPS", "8")
     pl = dm.diagmm_plan("qk", 1, 512, 1, 64, 32, 32, 0, torch.float16)
     assert pl["tiles"] >= 8 and pl["slots_per_tile"] < 65, pl
+
+
+def test_qk_stream_plan_balances_row_ranges(monkeypatch):
+    """The streaming qk kernel (16-bit in and out) cuts every strip into the same number of
+    row ranges of at most 208 class rows: at n = 4096, h = 12 (one strip per head, three
+    per head at dilation 3) that is 252 ranges of at most 196 rows for 256 units, so no
+    unit stores more than 196 / 192 of the average; every range covers all K slots."""
+    monkeypatch.delenv("DIAGMM_MAX_WORKGROUPS", raising=False)
+    monkeypatch.delenv("DIAGMM_QK", raising=False)
+    for dil, g in ((0, 21), (3, 7)):
+        pl = dm.diagmm_plan("qk", 1, 4096, 12, 64, 256, 256, dil, torch.float16)
+        if pl["workgroups"] != 256:
+            continue
+        assert pl["kernel"] == "qk_stream", pl
+        assert pl["strip_workgroups"] == g and pl["tiles"] == 252, pl
+        assert pl["rows_per_tile"] == 196 and pl["slots_per_tile"] == 513, pl
+    # f32 outputs stay on the tile kernel
+    assert dm.diagmm_plan("qk", 1, 4096, 12, 64, 256, 256, 0, torch.float16,
+                          torch.float32)["kernel"] == "qk_mfma"
+    # a range's key window must fit LDS (15 chunks of 64 keys): K = 8193 at n = 32768 goes
+    # to the tile kernel, which cuts the slots into chunks
+    pl = dm.diagmm_plan("qk", 1, 32768, 12, 64, 4096, 4096, 0, torch.float16)
+    assert pl["kernel"] == "qk_mfma", pl

@@ -74,7 +74,7 @@ def _load():
                                            ci]
             lib.oracle_attention.argtypes = [vp, vp, vp, vp] + [i64] * 7 + [cd, ci, ci, vp, i64,
                                                                               ci]
-            lib.oracle_attention_global.argtypes = [vp, vp, vp, vp, i64, vp] + [i64] * 7 + [
+            lib.oracle_attention_global.argtypes = [vp] * 7 + [i64, vp] + [i64] * 7 + [
                 cd, ci, ci, vp, i64, ci]
             lib.oracle_softmax_masked.argtypes = [vp, vp, vp] + [i64] * 6 + [cd, cd, ci, ci, vp,
                                                                                  i64, ci]
@@ -190,23 +190,32 @@ def attention(q, k, v, w, w_upper, dilation=0, scale=1.0, out_dtype=None, rows=N
 
 
 def attention_global(q, k, v, glob, w, w_upper, dilation=0, scale=1.0, out_dtype=None,
-                     rows=None, threads=None):
+                     rows=None, threads=None, global_qkv=None):
     """Sliding-window attention with global tokens: ``glob`` is an integer [b, ng] tensor
-    of distinct global positions per batch.  A row outside them attends its window and
-    the global keys (each key once); a global row attends every key."""
+    of global positions per batch; its entries in [0, n) form the global set (a repeated
+    position counts once, others name no position).  A row outside the set attends its
+    window and the global keys (each key once) with q, k, v; a global row attends every
+    key with ``global_qkv`` = (GQ, GK, GV) (default: q, k, v)."""
     lib = _load()
     q, k, v = _check(q, "q"), _check(k, "k"), _check(v, "v")
     if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype):
         raise ValueError("oracle.attention_global: q, k, v differ in shape or dtype")
+    gp = [None, None, None]
+    if global_qkv is not None:
+        gq, gk, gv = (_check(t, "global_qkv") for t in global_qkv)
+        if not (gq.shape == gk.shape == gv.shape == q.shape
+                and gq.dtype == gk.dtype == gv.dtype == q.dtype):
+            raise ValueError("oracle.attention_global: global q, k, v differ from q")
+        gp = [_ptr(gq), _ptr(gk), _ptr(gv)]
     b, n, h, d = q.shape
     g = torch.as_tensor(glob, dtype=torch.int64).reshape(b, -1).contiguous()
     out_dtype = out_dtype or q.dtype
     rt, rp, nr = _rows(rows)
     shape = (b, n, h, d) if rt is None else (nr, h, d)
     out = torch.empty(shape, dtype=out_dtype)
-    st = lib.oracle_attention_global(_ptr(q), _ptr(k), _ptr(v), _ptr(g), g.shape[1], _ptr(out),
-                                     b, n, h, d, w, w_upper, dilation, float(scale),
-                                     _CODE[q.dtype], _CODE[out_dtype], rp, nr,
+    st = lib.oracle_attention_global(_ptr(q), _ptr(k), _ptr(v), gp[0], gp[1], gp[2], _ptr(g),
+                                     g.shape[1], _ptr(out), b, n, h, d, w, w_upper, dilation,
+                                     float(scale), _CODE[q.dtype], _CODE[out_dtype], rp, nr,
                                      threads or default_threads())
     if st:
         raise ValueError(f"oracle.attention_global: bad arguments ({st})")

@@ -499,23 +499,29 @@ int oracle_attention(const void* q, const void* kt, const void* v, void* out, in
 
 /* ------------------------------------------------------------------ global tokens
  * Sliding-window attention with global tokens (onnxruntime issue 12448: the
- * LongformerAttention op, a sliding window plus global tokens).  G_bb is a set of
- * positions of batch bb (glob[bb * ng + g], g < ng, distinct).  A row i outside G_bb
- * attends the keys of its window and every key in G_bb, each key once; a row in G_bb
- * attends every key of the sequence.  Both use the same Q, K, V:
- *     keys(i) = { j : i in G, or j in G, or j = i + (k - w) * s for a slot k },
- *     out[i] = sum_{j in keys(i)} softmax_j(scale * Q[i] . K[j]) V[j].
- * Written directly from that set, one row at a time in double. */
-int oracle_attention_global(const void* q, const void* kt, const void* v, const int64_t* glob,
-                            int64_t ng, void* out, int64_t b, int64_t n, int64_t h, int64_t d,
-                            int64_t w, int64_t wu, int64_t dil, double scale, int in_dt,
-                            int out_dt, const int64_t* rows, int64_t nrows, int nthreads)
+ * LongformerAttention op, a sliding window plus global tokens, whose inputs carry the
+ * Global_Q, Global_K and Global_V matrices beside Q, K and V - description, conclusion
+ * (d)).  G_bb is the set of positions glob[bb * ng + g], g < ng, that lie in [0, n): a
+ * position listed twice is one member, an entry outside [0, n) names no position.
+ * A row i outside G_bb attends the keys of its window and every key in G_bb, each key
+ * once, with Q, K and V:
+ *     keys(i) = { j : j in G, or j = i + (k - w) * s for a slot k },
+ *     out[i] = sum_{j in keys(i)} softmax_j(scale * Q[i] . K[j]) V[j];
+ * a row i in G_bb attends every key of the sequence with the global matrices:
+ *     out[i] = sum_{j < n} softmax_j(scale * GQ[i] . GK[j]) GV[j].
+ * gq, gk, gv NULL: the global rows use Q, K and V.  Written directly from those sets,
+ * one row at a time in double. */
+int oracle_attention_global(const void* q, const void* kt, const void* v, const void* gq,
+                            const void* gk, const void* gv, const int64_t* glob, int64_t ng,
+                            void* out, int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,
+                            int64_t wu, int64_t dil, double scale, int in_dt, int out_dt,
+                            const int64_t* rows, int64_t nrows, int nthreads)
 {
     int bad = or_check(b, n, h, d, w, wu, dil, in_dt, out_dt);
     if (bad) return bad;
     if (ng < 0 || (ng > 0 && !glob)) return 1;
-    for (int64_t i = 0; i < b * ng; ++i)
-        if (glob[i] < 0 || glob[i] >= n) return 1;
+    if ((gq || gk || gv) && !(gq && gk && gv)) return 1;
+    if (!gq) { gq = q; gk = kt; gv = v; }
     const int64_t s = or_stride(dil);
     if (!rows) nrows = b * n;
     int failed = 0;
@@ -525,7 +531,14 @@ int oracle_attention_global(const void* q, const void* kt, const void* v, const 
         double* x = (double*)malloc((size_t)n * sizeof(double));
         char* isg = (char*)calloc((size_t)n, 1);
         if (!x || !isg) { free(x); free(isg); failed = 1; continue; }
-        for (int64_t g = 0; g < ng; ++g) isg[glob[bb * ng + g]] = 1;
+        for (int64_t g = 0; g < ng; ++g) {
+            const int64_t pos = glob[bb * ng + g];
+            if (pos >= 0 && pos < n) isg[pos] = 1;
+        }
+        /* the matrices this row's scores and values come from */
+        const void* qm = isg[i] ? gq : q;
+        const void* km = isg[i] ? gk : kt;
+        const void* vm = isg[i] ? gv : v;
         for (int64_t hh = 0; hh < h; ++hh) {
             const int64_t qrow = ((bb * n + i) * h + hh) * d;
             double mx = -INFINITY;
@@ -536,8 +549,8 @@ int oracle_attention_global(const void* q, const void* kt, const void* v, const 
                 if (!(isg[i] || isg[j] || in_window)) continue;
                 double acc = 0.0;
                 for (int64_t c = 0; c < d; ++c)
-                    acc += or_load(q, qrow + c, in_dt) *
-                           or_load(kt, ((bb * n + j) * h + hh) * d + c, in_dt);
+                    acc += or_load(qm, qrow + c, in_dt) *
+                           or_load(km, ((bb * n + j) * h + hh) * d + c, in_dt);
                 x[j] = scale * acc;
                 if (x[j] > mx) mx = x[j];
             }
@@ -550,7 +563,7 @@ int oracle_attention_global(const void* q, const void* kt, const void* v, const 
                 double acc = 0.0;
                 for (int64_t j = 0; j < n; ++j)
                     if (x[j] != 0.0)
-                        acc += (x[j] / sum) * or_load(v, ((bb * n + j) * h + hh) * d + c, in_dt);
+                        acc += (x[j] / sum) * or_load(vm, ((bb * n + j) * h + hh) * d + c, in_dt);
                 or_store(out, (r * h + hh) * d + c, out_dt, acc);
             }
         }

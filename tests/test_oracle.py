@@ -752,21 +752,28 @@ def test_attention_row_list_equals_full():
 # set as a dense mask, no global tokens = the windowed attention, a global row = full
 # dense attention, and all rows global = full dense attention everywhere.
 
-def _dense_global(q, k, v, glob, w, wu, dil, scale):
+def _dense_global(q, k, v, glob, w, wu, dil, scale, gqkv=None):
+    """Dense float64 reference: the key set as a mask over all n x n pairs; the global
+    rows from (GQ, GK, GV) over every key.  ``glob`` is taken as given (a clean set)."""
     b, n = q.shape[:2]
     i = torch.arange(n)[:, None]
     j = torch.arange(n)[None, :]
     off = j - i
     s = max(dil, 1)
     win = (off % s == 0) & (off >= -w * s) & (off <= wu * s)
+    gq, gk, gv = gqkv if gqkv is not None else (q, k, v)
     outs = []
     for bb in range(b):
         isg = torch.zeros(n, dtype=torch.bool)
         isg[glob[bb]] = True
-        sel = win | isg[None, :] | isg[:, None]
+        sel = win | isg[None, :]
         sc = torch.einsum("ihd,jhd->hij", q[bb].double(), k[bb].double()) * scale
         p = torch.softmax(sc.masked_fill(~sel, float("-inf")), -1)
-        outs.append(torch.einsum("hij,jhd->ihd", p, v[bb].double()))
+        o = torch.einsum("hij,jhd->ihd", p, v[bb].double())
+        gsc = torch.einsum("ihd,jhd->hij", gq[bb].double(), gk[bb].double()) * scale
+        go = torch.einsum("hij,jhd->ihd", torch.softmax(gsc, -1), gv[bb].double())
+        o[isg] = go[isg]
+        outs.append(o)
     return torch.stack(outs)
 
 
@@ -780,6 +787,48 @@ def test_attention_global_matches_dense_masked_attention(shape):
                         for bb in range(b)])
     got = oracle.attention_global(q, k, v, glob, w, wu, dil, 0.6, out_dtype=torch.float64)
     assert torch.allclose(got, _dense_global(q, k, v, glob, w, wu, dil, 0.6), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("shape", [(2, 40, 2, 8, 3, 3, 0), (1, 50, 1, 8, 4, 0, 3)])
+def test_attention_global_separate_matrices(shape):
+    """The global rows take Global_Q, Global_K and Global_V (onnxruntime issue 12448,
+    conclusion (d)) over every key; the other rows keep Q, K and V, the global keys
+    included.  A dropped global matrix, or one used on the wrong rows, fails."""
+    b, n, h, d, w, wu, dil = shape
+    g = datagen.rng(1960 + n)
+    q, k, v, gq, gk, gv = (datagen.normal(g, (b, n, h, d), "f32") for _ in range(6))
+    glob = torch.stack([torch.from_numpy(datagen.rng(1970 + bb).choice(n, 5, replace=False))
+                        for bb in range(b)])
+    got = oracle.attention_global(q, k, v, glob, w, wu, dil, 0.6, out_dtype=torch.float64,
+                                  global_qkv=(gq, gk, gv))
+    ref = _dense_global(q, k, v, glob, w, wu, dil, 0.6, gqkv=(gq, gk, gv))
+    assert torch.allclose(got, ref, rtol=0, atol=1e-12)
+    # the same matrices given twice are the one-QKV form, bit for bit
+    assert torch.equal(oracle.attention_global(q, k, v, glob, w, wu, dil, 0.6,
+                                               out_dtype=torch.float64, global_qkv=(q, k, v)),
+                       oracle.attention_global(q, k, v, glob, w, wu, dil, 0.6,
+                                               out_dtype=torch.float64))
+
+
+def test_attention_global_position_list_is_a_set():
+    """Repeated positions count once and entries outside [0, n) name no position: the
+    result equals the dense reference on the cleaned set."""
+    b, n, h, d, w, wu, dil = 2, 30, 2, 8, 2, 3, 0
+    g = datagen.rng(1980)
+    q, k, v = (datagen.normal(g, (b, n, h, d), "f32") for _ in range(3))
+    messy = torch.tensor([[4, 4, 17, -1, 30, 4, 29, 1000],
+                          [0, -5, 0, 0, 12, 12, 31, 2]])
+    clean = [torch.tensor([4, 17, 29]), torch.tensor([0, 12, 2])]
+    got = oracle.attention_global(q, k, v, messy, w, wu, dil, 0.6, out_dtype=torch.float64)
+    ref = torch.cat([_dense_global(q[bb:bb + 1], k[bb:bb + 1], v[bb:bb + 1], [clean[bb]],
+                                   w, wu, dil, 0.6) for bb in range(b)])
+    assert torch.allclose(got, ref, rtol=0, atol=1e-12)
+    # every entry out of range: the plain windowed attention
+    junk = torch.tensor([[-3, n, n + 7], [-1, -1, 2 * n]])
+    assert torch.allclose(oracle.attention_global(q, k, v, junk, w, wu, dil, 0.6,
+                                                  out_dtype=torch.float64),
+                          oracle.attention(q, k, v, w, wu, dil, 0.6, out_dtype=torch.float64),
+                          rtol=0, atol=1e-14)
 
 
 def test_attention_global_special_cases():

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DIAGMM_ABI_VERSION 7
+#define DIAGMM_ABI_VERSION 8
 
 typedef enum {
     DIAGMM_F32 = 0,
@@ -200,23 +200,48 @@ diagmm_status_t diagmm_banded_attention(const void* q, const void* k, const void
 
 /*
  * diagmm_banded_attention_global - diagmm_banded_attention with global tokens, as in the
- * LongformerAttention op of onnxruntime issue 12448 (a sliding window plus global tokens).
- * global_pos is int32 [b][ng] on the device: the positions of batch bb's global tokens
- * (distinct; entries outside [0, n) are clamped into it, never read out of bounds).  A row
- * outside the global set attends the keys of its window and every global key, each key
- * once; a global row attends every key of the sequence.  One Q, K and V serve both.  ng =
- * 0 is diagmm_banded_attention.  Two kernels run in order on `stream` (the rows outside
- * the set, then the global rows).  ng outside [0, n] is DIAGMM_ERR_SHAPE; global_pos NULL
- * with ng > 0 is DIAGMM_ERR_NULL; out overlapping q, k, v or global_pos is
- * DIAGMM_ERR_ALIAS; besides the shapes diagmm_banded_attention refuses, windows with
- * 64 + w + w_upper > 16384 are DIAGMM_ERR_UNSUPPORTED.
+ * LongformerAttention op of onnxruntime issue 12448 (a sliding window plus global tokens,
+ * with Global_Q, Global_K and Global_V matrices beside Q, K and V: description and
+ * conclusion (d)).  global_pos is int32 [b][ng] on the device; batch bb's global set is
+ * the set of its entries that lie in [0, n) (a repeated position is one member, an entry
+ * outside [0, n) names none).  A row outside the set attends the keys of its window and
+ * every global key, each key once, with q, k and v; a global row attends every key of
+ * the sequence with global_q, global_k and global_v ([b][n][h][d] like q, read at the
+ * global positions and every key; all three NULL: q, k and v).  ng = 0 is
+ * diagmm_banded_attention.
+ *
+ * workspace: device memory of at least diagmm_banded_attention_global_workspace bytes,
+ * 256-byte aligned, owned by the caller, used by this call's two kernels on `stream`
+ * (the positions of the global rows and their partial softmax states); its
+ * contents on entry do not matter.  Calls sharing a workspace must be ordered on one
+ * stream.  NULL is allowed when that size is 0 (ng = 0).
+ *
+ * Errors: ng outside [0, n] is DIAGMM_ERR_SHAPE, and so is workspace_bytes below the
+ * size needed; a NULL pointer where data is needed, or one or two of the global matrices
+ * NULL, is DIAGMM_ERR_NULL; out overlapping any input or the workspace, or the workspace
+ * overlapping an input, is DIAGMM_ERR_ALIAS; besides the shapes diagmm_banded_attention
+ * refuses, windows with 64 + w + w_upper > 16384, n > 65536 with ng > 0, a workspace not
+ * 256-byte aligned or unaligned global matrices are DIAGMM_ERR_UNSUPPORTED.
  */
 diagmm_status_t diagmm_banded_attention_global(const void* q, const void* k, const void* v,
-                                               void* out, const int32_t* global_pos,
-                                               int64_t ng, int64_t b, int64_t n, int64_t h,
-                                               int64_t d, int64_t w, int64_t w_upper,
-                                               int64_t dilation, float scale,
-                                               diagmm_dtype_t dtype, void* stream);
+                                               const void* global_q, const void* global_k,
+                                               const void* global_v, void* out,
+                                               const int32_t* global_pos, int64_t ng,
+                                               int64_t b, int64_t n, int64_t h, int64_t d,
+                                               int64_t w, int64_t w_upper, int64_t dilation,
+                                               float scale, diagmm_dtype_t dtype,
+                                               void* workspace, int64_t workspace_bytes,
+                                               void* stream);
+
+/*
+ * Workspace bytes diagmm_banded_attention_global needs for these sizes (0 when ng = 0)
+ * in *bytes.  DIAGMM_ERR_SHAPE for sizes that call would refuse as such, DIAGMM_ERR_NULL
+ * for a NULL bytes.
+ */
+diagmm_status_t diagmm_banded_attention_global_workspace(int64_t b, int64_t n, int64_t h,
+                                                         int64_t d, int64_t w, int64_t w_upper,
+                                                         int64_t dilation, int64_t ng,
+                                                         int64_t* bytes);
 
 /* Static text for a status code. */
 const char* diagmm_status_string(diagmm_status_t status);

@@ -84,8 +84,10 @@ def load() -> ctypes.CDLL:
     lib.diagmm_banded_dropout.restype = ci
     lib.diagmm_banded_attention.argtypes = [vp, vp, vp, vp] + [i64] * 7 + [f32, ci, vp]
     lib.diagmm_banded_attention.restype = ci
-    lib.diagmm_banded_attention_global.argtypes = [vp, vp, vp, vp, vp] + [i64] * 8 + [f32, ci, vp]
+    lib.diagmm_banded_attention_global.argtypes = [vp] * 8 + [i64] * 8 + [f32, ci, vp, i64, vp]
     lib.diagmm_banded_attention_global.restype = ci
+    lib.diagmm_banded_attention_global_workspace.argtypes = [i64] * 8 + [ctypes.POINTER(i64)]
+    lib.diagmm_banded_attention_global_workspace.restype = ci
     lib.diagmm_status_string.argtypes = [ci]
     lib.diagmm_status_string.restype = ctypes.c_char_p
     lib.diagmm_last_error.argtypes = []
@@ -306,16 +308,25 @@ def diagmm_banded_attention(q, k, v, w, w_upper=None, dilation=0, scale=None, ou
 
 
 def diagmm_banded_attention_global(q, k, v, global_pos, w, w_upper=None, dilation=0,
-                                   scale=None, out=None):
+                                   scale=None, out=None, global_qkv=None):
     """``diagmm_banded_attention`` with global tokens: ``global_pos`` is int32 [b, ng] on
-    the GPU (distinct positions).  Rows outside the set attend their window and the global
-    keys (each key once); global rows attend every key."""
+    the GPU; its entries in [0, n) form the global set (a repeat counts once).  Rows
+    outside the set attend their window and the global keys (each key once) with q, k, v;
+    global rows attend every key with ``global_qkv`` = (GQ, GK, GV) (default q, k, v).
+    The call's workspace is allocated here, from torch's caching allocator."""
     lib = load()
     w, w_upper, dilation = _window(w, w_upper, dilation)
     q, k, v = _dense(q, "q"), _dense(k, "k"), _dense(v, "v")
     if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype
             and q.device == k.device == v.device):
         raise ValueError("q, k and v must have the same shape, dtype and device")
+    gptr = [None, None, None]
+    if global_qkv is not None:
+        gq, gk, gv = (_dense(t, "global_qkv") for t in global_qkv)
+        for t in (gq, gk, gv):
+            if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+                raise ValueError("global_qkv tensors must match q in shape, dtype and device")
+        gptr = [gq.data_ptr(), gk.data_ptr(), gv.data_ptr()]
     b, n, h, d = q.shape
     g = global_pos
     if (not isinstance(g, torch.Tensor) or g.dtype != torch.int32 or g.dim() != 2
@@ -324,10 +335,18 @@ def diagmm_banded_attention_global(q, k, v, global_pos, w, w_upper=None, dilatio
     if scale is None:
         scale = d ** -0.5
     res = _out(out, q.shape, q.dtype, q.device)
-    st = lib.diagmm_banded_attention_global(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                            res.data_ptr(), g.data_ptr(), g.shape[1], b, n, h,
-                                            d, w, w_upper, dilation, float(scale),
-                                            _DT[q.dtype], _stream(q.device))
+    need = ctypes.c_int64(0)
+    st = lib.diagmm_banded_attention_global_workspace(b, n, h, d, w, w_upper, dilation,
+                                                      g.shape[1], ctypes.byref(need))
+    if st:
+        _raise(lib, st)
+    ws = torch.empty(need.value + 256, dtype=torch.uint8, device=q.device) if need.value else None
+    ws_ptr = None if ws is None else (ws.data_ptr() + 255) // 256 * 256
+    st = lib.diagmm_banded_attention_global(q.data_ptr(), k.data_ptr(), v.data_ptr(), gptr[0],
+                                            gptr[1], gptr[2], res.data_ptr(), g.data_ptr(),
+                                            g.shape[1], b, n, h, d, w, w_upper, dilation,
+                                            float(scale), _DT[q.dtype], ws_ptr, need.value,
+                                            _stream(q.device))
     if st:
         _raise(lib, st)
     return res

@@ -352,38 +352,92 @@ diagmm_status_t diagmm_banded_attention(const void* q, const void* k, const void
         return fail(DIAGMM_ERR_UNSUPPORTED, "%s: needs f16 or bf16, d in {32, 64, 128} and "
                     "16-byte aligned tensors", fn);
     timing_set_op(kOpAttention);
-    return launched(fn, launch_attention(q, k, v, out, nullptr, 0, p, scale, dtype,
+    return launched(fn, launch_attention(q, k, v, nullptr, nullptr, nullptr, out, nullptr, 0,
+                                         nullptr, p, scale, dtype,
                                          static_cast<hipStream_t>(stream)));
 }
 
-diagmm_status_t diagmm_banded_attention_global(const void* q, const void* k, const void* v,
-                                               void* out, const int32_t* global_pos,
-                                               int64_t ng, int64_t b, int64_t n, int64_t h,
-                                               int64_t d, int64_t w, int64_t w_upper,
-                                               int64_t dilation, float scale,
-                                               diagmm_dtype_t dtype, void* stream) {
-    const char* fn = "diagmm_banded_attention_global";
-    Problem p;
-    int64_t de, be;
-    diagmm_status_t st = check_common(fn, b, n, h, d, w, w_upper, dilation, dtype, dtype, &p,
-                                      &de, &be);
+// Shared checks of the global-token call and its workspace query: the common sizes, ng
+// and the supported shapes; fills p, the dense element count and the workspace size.
+static diagmm_status_t check_global(const char* fn, int64_t b, int64_t n, int64_t h, int64_t d,
+                                    int64_t w, int64_t w_upper, int64_t dilation, int64_t ng,
+                                    int dtype, Problem* p, int64_t* de, int64_t* ws_bytes) {
+    int64_t be;
+    diagmm_status_t st = check_common(fn, b, n, h, d, w, w_upper, dilation, dtype, dtype, p, de,
+                                      &be);
     if (st != DIAGMM_OK) return st;
     if (ng < 0 || ng > n) return fail(DIAGMM_ERR_SHAPE, "%s: ng = %lld outside [0, n]", fn,
                                       static_cast<long long>(ng));
+    if (mul_checked(b, ng) < 0 || mul_checked(b, ng) > kLimit / 8)
+        return fail(DIAGMM_ERR_SHAPE, "%s: b * ng overflows", fn);
+    *ws_bytes = p->rows() * p->h == 0 ? 0 : attention_global_workspace(*p, ng);
+    return DIAGMM_OK;
+}
+
+diagmm_status_t diagmm_banded_attention_global_workspace(int64_t b, int64_t n, int64_t h,
+                                                         int64_t d, int64_t w, int64_t w_upper,
+                                                         int64_t dilation, int64_t ng,
+                                                         int64_t* bytes) {
+    const char* fn = "diagmm_banded_attention_global_workspace";
+    if (!bytes) return fail(DIAGMM_ERR_NULL, "%s: null bytes pointer", fn);
+    Problem p;
+    int64_t de, ws;
+    diagmm_status_t st = check_global(fn, b, n, h, d, w, w_upper, dilation, ng, kF16, &p, &de,
+                                      &ws);
+    if (st != DIAGMM_OK) return st;
+    *bytes = ws;
+    return ok();
+}
+
+diagmm_status_t diagmm_banded_attention_global(const void* q, const void* k, const void* v,
+                                               const void* global_q, const void* global_k,
+                                               const void* global_v, void* out,
+                                               const int32_t* global_pos, int64_t ng,
+                                               int64_t b, int64_t n, int64_t h, int64_t d,
+                                               int64_t w, int64_t w_upper, int64_t dilation,
+                                               float scale, diagmm_dtype_t dtype,
+                                               void* workspace, int64_t workspace_bytes,
+                                               void* stream) {
+    const char* fn = "diagmm_banded_attention_global";
+    Problem p;
+    int64_t de, need;
+    diagmm_status_t st = check_global(fn, b, n, h, d, w, w_upper, dilation, ng, dtype, &p, &de,
+                                      &need);
+    if (st != DIAGMM_OK) return st;
     if (p.rows() * p.h == 0) return ok();
-    if (!q || !k || !v || !out || (ng > 0 && !global_pos))
-        return fail(DIAGMM_ERR_NULL, "%s: null pointer", fn);
+    const int given = (global_q != nullptr) + (global_k != nullptr) + (global_v != nullptr);
+    if (!q || !k || !v || !out || (ng > 0 && !global_pos) || (given != 0 && given != 3) ||
+        (need > 0 && !workspace))
+        return fail(DIAGMM_ERR_NULL, "%s: null pointer (or only some of global_q, global_k, "
+                    "global_v)", fn);
+    if (workspace_bytes < need)
+        return fail(DIAGMM_ERR_SHAPE, "%s: workspace of %lld bytes, %lld needed", fn,
+                    static_cast<long long>(workspace_bytes), static_cast<long long>(need));
     const int64_t bytes = de * static_cast<int64_t>(elem_size(dtype));
-    for (const void* in : {q, k, v})
-        if (overlaps(out, bytes, in, bytes))
-            return fail(DIAGMM_ERR_ALIAS, "%s: out overlaps q, k or v", fn);
+    for (const void* in : {q, k, v, global_q, global_k, global_v})
+        if (in && overlaps(out, bytes, in, bytes))
+            return fail(DIAGMM_ERR_ALIAS, "%s: out overlaps an input", fn);
     if (ng > 0 && overlaps(out, bytes, global_pos, b * ng * 4))
         return fail(DIAGMM_ERR_ALIAS, "%s: out overlaps global_pos", fn);
-    if (!attention_supported(p, dtype, q, k, v, out) || !attention_global_supported(p, ng))
+    if (need > 0) {
+        if (overlaps(workspace, need, out, bytes) ||
+            overlaps(workspace, need, global_pos, b * ng * 4))
+            return fail(DIAGMM_ERR_ALIAS, "%s: workspace overlaps out or global_pos", fn);
+        for (const void* in : {q, k, v, global_q, global_k, global_v})
+            if (in && overlaps(workspace, need, in, bytes))
+                return fail(DIAGMM_ERR_ALIAS, "%s: workspace overlaps an input", fn);
+    }
+    const bool aligned = (need == 0 || (reinterpret_cast<uintptr_t>(workspace) & 255) == 0) &&
+                         (given == 0 || attention_supported(p, dtype, global_q, global_k,
+                                                            global_v, out));
+    if (!attention_supported(p, dtype, q, k, v, out) || !attention_global_supported(p, ng) ||
+        !aligned)
         return fail(DIAGMM_ERR_UNSUPPORTED, "%s: needs f16 or bf16, d in {32, 64, 128}, "
-                    "16-byte aligned tensors and 64 + w + w_upper <= 16384", fn);
+                    "16-byte aligned tensors, a 256-byte aligned workspace, "
+                    "64 + w + w_upper <= 16384 and n <= 65536", fn);
     timing_set_op(kOpAttention);
-    return launched(fn, launch_attention(q, k, v, out, global_pos, ng, p, scale, dtype,
+    return launched(fn, launch_attention(q, k, v, global_q, global_k, global_v, out, global_pos,
+                                         ng, workspace, p, scale, dtype,
                                          static_cast<hipStream_t>(stream)));
 }
 

@@ -30,6 +30,24 @@
 // 4 g .. 4 g + 3 of each 16-channel block - all of one query row, so the online
 // softmax's rescaling is per lane.  Row maxima and sums combine the four lane groups of a
 // query with two cross-lane steps.
+//
+// Global tokens (onnxruntime issue 12448: the LongformerAttention op, a sliding window
+// plus global tokens, with Global_Q, Global_K and Global_V beside Q, K and V).  Two
+// launches.  The first holds two kinds of workgroups, and each starts by building the
+// batch's global set in LDS from the position list: a bitmap of the listed positions in
+// [0, n) (a repeat sets one bit) and the exclusive prefix counts of its words, so that
+// the set's size is known and its r-th member (in position order) is found by a binary
+// search over the counts.  Band workgroups are the one-pass kernel's with the global keys
+// added: a second bitmap marks the global keys inside the workgroup's key range (left
+// out of its window blocks), the global keys are staged 64 at a time in set order and
+// attended first, and rows at global positions are not stored.  Global-row workgroups
+// take 64 global rows (4 waves x 16, ranks 64 rb ..) of one (batch, head) over one range
+// of kr keys, with the global matrices, and write the range's partial softmax state
+// (running maximum, running sum, unnormalised output per row) to the workspace; they come
+// first in the grid, so their short ranges run beside the band workgroups.  The second
+// launch merges the nsplit states of each block of global rows and stores the rows (the
+// kernel boundary orders it after every partial state; a merge inside the first launch
+// would need a device-scope release per workgroup, which writes back a whole L2).
 #include "launch.hpp"
 #include "ring.hpp"
 
@@ -39,6 +57,7 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -56,29 +75,94 @@ template <> struct Mfma<BF16> {
     }
 };
 
-constexpr int kRows = 64;                   // class rows per workgroup, 16 per wave
+constexpr int kRows = 64;                   // query rows per workgroup, 16 per wave
 constexpr int kThreads = kRows / 16 * 64;
-// Workgroup size of a mode: the global-row pass splits the keys over 8 waves where their
-// LDS blocks fit (d <= 64), else over 4.
-__host__ __device__ constexpr int mode_threads(int mode, int d) {
-    return mode == 2 && d <= 64 ? 512 : kThreads;
-}
 constexpr int kKeys = 64;                   // keys per LDS block
 constexpr int kChunks = kKeys / 32;         // 32-key chunks per block
+constexpr int64_t kMaxGlobalN = int64_t(1) << 16;   // the LDS global set: 2 n bits <= 16 KB
+constexpr int kMaxSplit = 32;               // key ranges per block of global rows, at most
 
 struct AttnArgs {
     int64_t n, h, w, wu, s;
     int64_t cls_q, cls_m;     // n = cls_q s + cls_m: class r has cls_q + (r < cls_m) rows
     int64_t nqb_hi, nqb_lo;   // 64-row blocks of a long / short class
-    int64_t per_head;         // workgroups per (batch, head)
-    int64_t groups;           // workgroups in the grid
+    int64_t per_head;         // band workgroups per (batch, head)
+    int64_t groups;           // band workgroups
     float scale_log2;         // scale * log2(e)
-    int32_t ng;               // global tokens per batch (0: none)
-    int64_t ngb;              // 16-row blocks of global rows per (batch, head)
+    int32_t ng;               // entries of the position list per batch (0: no global tokens)
+    int32_t nrb;              // 64-row blocks of global rows per (batch, head)
+    int32_t nsplit;           // key ranges per block of global rows
+    int32_t kr;               // keys per range, a multiple of 64
+    int64_t rows_used;        // global-row workgroups: b h nrb nsplit
+    int64_t rows_groups;      // the same rounded up to a multiple of 8 (first in the grid)
 };
 
+// The global side of a call: the position list, the global rows' matrices and the
+// workspace.
+template <class T> struct GlobalIn {
+    const int32_t* glob;      // [b][ng] listed positions
+    const T* gq;
+    const T* gk;
+    const T* gv;
+    int32_t* gpos;            // [b h nrb][64]: position of each global row, -1 past the set
+    float* part_acc;          // [b h nrb nsplit 64][d]: unnormalised outputs of a range
+    float* part_ml;           // [b h nrb nsplit 64][2]: running maximum (log2), running sum
+};
+
+// The global set of batch bb in LDS: gmap (nw words, bit x = position x listed) and gpre
+// (exclusive prefix popcounts of the words); returns its size.  wsum: 4 words of LDS.
+__device__ __forceinline__ int build_set(const int32_t* __restrict__ glob, int64_t bb, int ng,
+                                         int n, uint32_t* gmap, uint32_t* gpre, uint32_t* wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nw = (n + 31) >> 5;
+    for (int i = tid; i < nw; i += kThreads) gmap[i] = 0u;
+    __syncthreads();
+    for (int g = tid; g < ng; g += kThreads) {
+        const int x = glob[bb * ng + g];
+        if (x >= 0 && x < n) atomicOr(&gmap[x >> 5], 1u << (x & 31));
+    }
+    __syncthreads();
+    // thread t counts words [w0, w1); a scan within each wave, then over the 4 wave totals
+    const int per = (nw + kThreads - 1) / kThreads;
+    const int w0 = tid * per < nw ? tid * per : nw;
+    const int w1 = w0 + per < nw ? w0 + per : nw;
+    int cnt = 0;
+    for (int i = w0; i < w1; ++i) cnt += __builtin_popcount(gmap[i]);
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+    }
+    if (lane == 63) wsum[wave] = static_cast<uint32_t>(incl);
+    __syncthreads();
+    int off = incl - cnt;
+    for (int wv = 0; wv < wave; ++wv) off += static_cast<int>(wsum[wv]);
+    for (int i = w0; i < w1; ++i) {
+        gpre[i] = static_cast<uint32_t>(off);
+        off += __builtin_popcount(gmap[i]);
+    }
+    const int total = static_cast<int>(wsum[0] + wsum[1] + wsum[2] + wsum[3]);
+    __syncthreads();
+    return total;
+}
+
+// Member `rank` (< the set's size) of the set in position order.
+__device__ __forceinline__ int set_member(const uint32_t* gmap, const uint32_t* gpre, int nw,
+                                          int rank) {
+    int lo = 0, hi = nw - 1;                  // the last word whose prefix count <= rank
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (static_cast<int>(gpre[mid]) <= rank) lo = mid;
+        else hi = mid - 1;
+    }
+    uint32_t word = gmap[lo];
+    for (int j = rank - static_cast<int>(gpre[lo]); j > 0; --j) word &= word - 1u;
+    return 32 * lo + __builtin_ctz(word);
+}
+
 // Kernel modes: the window only; the window plus the global keys for rows outside the
-// global set (global query rows are not stored); the global rows, each over every key.
+// global set (global query rows are not stored); global rows over one key range.
 constexpr int kBand = 0, kBandGlobal = 1, kGlobalRows = 2;
 constexpr int kBitWords = 512;   // LDS bitmap of global keys in a workgroup's key range
 
@@ -99,99 +183,115 @@ __device__ __forceinline__ uint32_t pack2(float a, float b, BF16) {
     return static_cast<uint32_t>(BF16::from_f32(a)) | (static_cast<uint32_t>(BF16::from_f32(b)) << 16);
 }
 
+// XCD-aware workgroup order: the dispatcher deals workgroups to the 8 XCDs in turn, so
+// XCD x gets a contiguous range of ids (neighbouring row blocks share their keys in L2).
+__device__ __forceinline__ int64_t xcd_order(int64_t bid, int64_t g) {
+    const int64_t per = g / 8, rem = g % 8;
+    const int64_t x = bid % 8, loc = bid / 8;
+    return x * per + (x < rem ? x : rem) + loc;
+}
+
+// One workgroup of any mode: `id` is its unit (band: (batch, head, class, row block);
+// global rows: (batch, head, row block, key range)).  gbits: kBitWords words of LDS for
+// the band-global mode; gmap, gpre: the global set (n bits each), wsum: 4 words (modes
+// with global tokens only).
 template <class In, int D, int kMode>
-__global__ void __launch_bounds__(mode_threads(kMode, D))
-attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __restrict__ k,
-                const typename In::T* __restrict__ v, typename In::T* __restrict__ out,
-                const int32_t* __restrict__ glob, AttnArgs a) {
+__device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
+                                          const typename In::T* __restrict__ k,
+                                          const typename In::T* __restrict__ v,
+                                          typename In::T* __restrict__ out,
+                                          const GlobalIn<typename In::T>& gi, const AttnArgs& a,
+                                          int64_t id, unsigned char* klds, unsigned char* vlds,
+                                          uint32_t* gbits, uint32_t* gmap, uint32_t* gpre,
+                                          uint32_t* wsum) {
     using ST = typename In::T;
     using V = typename Mfma<In>::V;
+    constexpr bool kRowsMode = kMode == kGlobalRows;
     constexpr int kPieces = D / 8;                       // 16-byte pieces per row
-    // the global-row mode splits the keys over the waves (8, or 4 for d = 128): each wave
-    // stages its own blocks (64 threads) in its own LDS region
-    constexpr int kT = mode_threads(kMode, D);
-    constexpr int kSplit = kMode == kGlobalRows ? kT / 64 : 1;
-    constexpr int kStageThreads = kT / kSplit;
-    constexpr int kStage = kKeys * kPieces / kStageThreads;   // pieces per thread per tensor
+    constexpr int kStage = kKeys * kPieces / kThreads;   // pieces per thread per tensor
     constexpr int kQk = D / 32;                          // MFMA K-steps over the channels
     constexpr int kCb = D / 16;                          // 16-channel output blocks
-    __shared__ __attribute__((aligned(16))) unsigned char klds[kSplit * kKeys * 2 * D];
-    __shared__ __attribute__((aligned(16))) unsigned char vlds[kSplit * kKeys * 2 * D];
-    __shared__ uint32_t gbits[kMode == kBandGlobal ? kBitWords : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
+    const int ng = a.ng;
 
-    // ---- workgroup -> (batch, head, residue class, row block), XCD-aware: the dispatcher
-    // deals workgroups to the 8 XCDs in turn, so XCD x gets a contiguous range of ids.
-    int64_t id;
-    {
-        const int64_t g = a.groups, per = g / 8, rem = g % 8;
-        const int64_t x = blockIdx.x % 8, loc = blockIdx.x / 8;
-        id = x * per + (x < rem ? x : rem) + loc;
-    }
-    const int64_t units = kMode == kGlobalRows ? a.ngb : a.per_head;
-    const int64_t bh = id / units;
-    int64_t rest = id - bh * units;
-    int64_t r, qb;
-    if (kMode == kGlobalRows) {
-        r = 0;              // the whole sequence as one undilated class, queries gathered
-        qb = rest;
-    } else if (rest < a.cls_m * a.nqb_hi) {
-        r = rest / a.nqb_hi;
-        qb = rest - r * a.nqb_hi;
+    // ---- the unit
+    int64_t bh, r = 0;
+    int rb = 0, split = 0, t0, len, ngd = 0;
+    if constexpr (kRowsMode) {
+        split = static_cast<int>(id % a.nsplit);
+        const int64_t rest = id / a.nsplit;
+        rb = static_cast<int>(rest % a.nrb);
+        bh = rest / a.nrb;
+        t0 = kRows * rb;                                  // ranks in the global set
+        len = static_cast<int>(a.n);
     } else {
-        rest -= a.cls_m * a.nqb_hi;
-        r = a.cls_m + rest / a.nqb_lo;
-        qb = rest - (r - a.cls_m) * a.nqb_lo;
+        int64_t qb;
+        bh = id / a.per_head;
+        int64_t rest = id - bh * a.per_head;
+        if (rest < a.cls_m * a.nqb_hi) {
+            r = rest / a.nqb_hi;
+            qb = rest - r * a.nqb_hi;
+        } else {
+            rest -= a.cls_m * a.nqb_hi;
+            r = a.cls_m + rest / a.nqb_lo;
+            qb = rest - (r - a.cls_m) * a.nqb_lo;
+        }
+        t0 = static_cast<int>(qb) * kRows;
+        len = static_cast<int>(a.cls_q + (r < a.cls_m ? 1 : 0));
     }
     const int64_t bb = bh / a.h, hh = bh - bb * a.h;
-    const int len = kMode == kGlobalRows ? static_cast<int>(a.n)
-                                         : static_cast<int>(a.cls_q + (r < a.cls_m ? 1 : 0));
-    // global rows: blocks of 16, all waves on the same rows
-    const int t0 = static_cast<int>(qb) * (kMode == kGlobalRows ? 16 : kRows);
-    // element offset of class row t: base + t * step
+    const int nw = static_cast<int>((a.n + 31) >> 5);
+    if constexpr (kMode != kBand)
+        ngd = build_set(gi.glob, bb, ng, static_cast<int>(a.n), gmap, gpre, wsum);
+    if constexpr (kRowsMode) {
+        // the first key range's workgroup records the positions of its 64 rows
+        if (split == 0 && tid < kRows)
+            gi.gpos[(bh * a.nrb + rb) * kRows + tid] =
+                t0 + tid < ngd ? set_member(gmap, gpre, nw, t0 + tid) : -1;
+        if (t0 >= ngd) return;                            // no global rows here (uniform)
+    }
+    // element offset of class row t (global rows: sequence position t): base + t * step
     const int64_t base = ((bb * a.n + r) * a.h + hh) * D;
-    const int64_t step = (kMode == kGlobalRows ? 1 : a.s) * a.h * D;
-    const int ng = a.ng;
-    // position of global token g of this batch, clamped into the sequence
-    auto gpos = [&](int g) {
-        int x = glob[bb * ng + (g < ng ? g : ng - 1)];
-        return x < 0 ? 0 : (x >= a.n ? static_cast<int>(a.n) - 1 : x);
-    };
+    const int64_t step = (kRowsMode ? 1 : a.s) * a.h * D;
 
     // ---- this lane's query row as the B operand of S^T (channels 32 kk + 8 grp .. +7)
-    const int tq = t0 + (kMode == kGlobalRows ? 0 : 16 * wv) + col;
-    const int tq_ld = kMode == kGlobalRows ? gpos(tq) : (tq < len ? tq : len - 1);
+    const int tq = t0 + 16 * wv + col;                    // class row, or rank in the set
+    int tq_ld;
+    if constexpr (kRowsMode) tq_ld = set_member(gmap, gpre, nw, tq < ngd ? tq : ngd - 1);
+    else tq_ld = tq < len ? tq : len - 1;
+    const ST* const qsrc = kRowsMode ? gi.gq : q;
+    const ST* const ksrc = kRowsMode ? gi.gk : k;
+    const ST* const vsrc = kRowsMode ? gi.gv : v;
     V qop[kQk];
 #pragma unroll
     for (int kk = 0; kk < kQk; ++kk)
-        qop[kk] = *reinterpret_cast<const V*>(q + base + int64_t(tq_ld) * step + 32 * kk + 8 * grp);
+        qop[kk] = *reinterpret_cast<const V*>(qsrc + base + int64_t(tq_ld) * step + 32 * kk + 8 * grp);
+    // a wave whose 16 rows are all past the rows (global rows: past the set) stages its
+    // share of every block but computes nothing
+    const bool wave_live = kRowsMode ? t0 + 16 * wv < ngd : t0 + 16 * wv < len;
 
-    const int w = kMode == kGlobalRows ? 0 : static_cast<int>(a.w);
-    const int wu = kMode == kGlobalRows ? 0 : static_cast<int>(a.wu);
-    int u_lo = t0 - w > 0 ? t0 - w : 0;
-    const int last_q = (t0 + kRows - 1 < len - 1) ? t0 + kRows - 1 : len - 1;
-    int u_hi = (last_q + wu < len - 1) ? last_q + wu : len - 1;   // inclusive
-    int nblk = (u_hi - u_lo + kKeys) / kKeys;
-    if (kMode == kGlobalRows) {
-        // wave wv sweeps the wv-th share of the key blocks; the same count for every
-        // wave (blocks past the sequence are masked), so the barriers match
-        const int per = ((len + kKeys - 1) / kKeys + kSplit - 1) / kSplit;
-        u_lo = wv * per * kKeys;
-        u_hi = len - 1;
-        nblk = per;
+    const int w = kRowsMode ? 0 : static_cast<int>(a.w);
+    const int wu = kRowsMode ? 0 : static_cast<int>(a.wu);
+    int u_lo, u_hi, nblk;
+    if constexpr (kRowsMode) {
+        u_lo = split * a.kr;
+        u_hi = (u_lo + a.kr < len ? u_lo + a.kr : len) - 1;
+    } else {
+        u_lo = t0 - w > 0 ? t0 - w : 0;
+        const int last_q = (t0 + kRows - 1 < len - 1) ? t0 + kRows - 1 : len - 1;
+        u_hi = (last_q + wu < len - 1) ? last_q + wu : len - 1;   // inclusive
     }
-    const int stid = kMode == kGlobalRows ? lane : tid;   // staging thread index
-    unsigned char* const kw = klds + (kMode == kGlobalRows ? wv : 0) * kKeys * 2 * D;
-    unsigned char* const vw = vlds + (kMode == kGlobalRows ? wv : 0) * kKeys * 2 * D;
+    nblk = (u_hi - u_lo + kKeys) / kKeys;
 
     // global keys of this class inside the key range, as bits of u - u_lo
     if constexpr (kMode == kBandGlobal) {
         for (int i = tid; i < kBitWords; i += kThreads) gbits[i] = 0u;
         __syncthreads();
         for (int g = tid; g < ng; g += kThreads) {
-            const int x = gpos(g);
+            const int x = gi.glob[bb * ng + g];
+            if (x < 0 || x >= a.n) continue;
             const int u = x / static_cast<int>(a.s);
             if (x - u * static_cast<int>(a.s) == r && u >= u_lo && u <= u_hi)
                 atomicOr(&gbits[(u - u_lo) >> 5], 1u << ((u - u_lo) & 31));
@@ -208,31 +308,33 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     auto load_block = [&](int u0) {
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
-            const int pc = stid + kStageThreads * i, row = pc / kPieces, ch = pc % kPieces;
+            const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
             int u = u0 + row;
             u = u < len ? u : len - 1;
             const int64_t off = base + int64_t(u) * step + 8 * ch;
-            kreg[i] = *reinterpret_cast<const u32x4*>(k + off);
-            vreg[i] = *reinterpret_cast<const u32x4*>(v + off);
+            kreg[i] = *reinterpret_cast<const u32x4*>(ksrc + off);
+            vreg[i] = *reinterpret_cast<const u32x4*>(vsrc + off);
         }
     };
     auto store_block = [&](int u0) {
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
-            const int pc = stid + kStageThreads * i, row = pc / kPieces, ch = pc % kPieces;
+            const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
             const bool ok = u0 + row < len;
             const u32x4 z{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(kw + kpiece<D>(row, ch)) = ok ? kreg[i] : z;
-            *reinterpret_cast<u32x4*>(vw + ring_piece<D>(row, ch)) = ok ? vreg[i] : z;
+            *reinterpret_cast<u32x4*>(klds + kpiece<D>(row, ch)) = ok ? kreg[i] : z;
+            *reinterpret_cast<u32x4*>(vlds + ring_piece<D>(row, ch)) = ok ? vreg[i] : z;
         }
     };
 
-    // a block of global keys: tokens 64 gb .. 64 gb + 63 of this batch (zeros past ng)
+    // a block of global keys: ranks 64 gb .. 64 gb + 63 of the set (zeros past its size)
     auto load_gblock = [&](int gb) {
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
             const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
-            const int64_t off = ((bb * a.n + gpos(kKeys * gb + row)) * a.h + hh) * D + 8 * ch;
+            const int g = kKeys * gb + row;
+            const int x = set_member(gmap, gpre, nw, g < ngd ? g : ngd - 1);
+            const int64_t off = ((bb * a.n + x) * a.h + hh) * D + 8 * ch;
             kreg[i] = *reinterpret_cast<const u32x4*>(k + off);
             vreg[i] = *reinterpret_cast<const u32x4*>(v + off);
         }
@@ -241,7 +343,7 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
             const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
-            const bool ok = kKeys * gb + row < ng;
+            const bool ok = kKeys * gb + row < ngd;
             const u32x4 z{0u, 0u, 0u, 0u};
             *reinterpret_cast<u32x4*>(klds + kpiece<D>(row, ch)) = ok ? kreg[i] : z;
             *reinterpret_cast<u32x4*>(vlds + ring_piece<D>(row, ch)) = ok ? vreg[i] : z;
@@ -260,7 +362,7 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     // K rows of this lane's A operand within a 32-key chunk: tile 0 and tile 1
     const int krow0 = 8 * (col >> 2) + (col & 3), krow1 = krow0 + 4;
 
-    // gl: the staged block holds global keys u0 .. u0 + 63 (token indices), not window keys
+    // gl: the staged block holds global keys (ranks u0 .. u0 + 63 of the set)
     auto compute_block = [&](int u0, bool gl) {
 
         // ---- scores: lane (col, grp) gets S[query tq][keys u0 + 32 c + 8 grp + 0..7]
@@ -270,8 +372,8 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
             s0[c] = s1[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < kQk; ++kk) {
-                const V a0 = *reinterpret_cast<const V*>(kw + kpiece<D>(32 * c + krow0, 4 * kk + grp));
-                const V a1 = *reinterpret_cast<const V*>(kw + kpiece<D>(32 * c + krow1, 4 * kk + grp));
+                const V a0 = *reinterpret_cast<const V*>(klds + kpiece<D>(32 * c + krow0, 4 * kk + grp));
+                const V a1 = *reinterpret_cast<const V*>(klds + kpiece<D>(32 * c + krow1, 4 * kk + grp));
                 s0[c] = Mfma<In>::run(a0, qop[kk], s0[c]);
                 s1[c] = Mfma<In>::run(a1, qop[kk], s1[c]);
             }
@@ -289,7 +391,7 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
             return (gbits[wa] | gbits[wa + 1] | gbits[wb]) == 0u;
         };
         bool inner;
-        if constexpr (kMode == kGlobalRows) inner = u0 + kKeys - 1 < len;
+        if constexpr (kRowsMode) inner = u0 + kKeys - 1 < len;
         else
             inner = !gl && u0 >= tw + 15 - w && u0 + kKeys - 1 <= tw + wu &&
                     u0 + kKeys - 1 < len && (kMode == kBand || no_global_keys());
@@ -309,9 +411,9 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
                     const int u = u0 + 32 * c + 8 * grp + e;
                     const float sv = e < 4 ? s0[c][e] : s1[c][e - 4];
                     bool ok;
-                    if constexpr (kMode == kGlobalRows) ok = u < len;
+                    if constexpr (kRowsMode) ok = u < len;
                     else if constexpr (kMode == kBandGlobal)
-                        ok = gl ? u < ng : (u >= lo && u <= hi && u < len && !is_global_key(u));
+                        ok = gl ? u < ngd : (u >= lo && u <= hi && u < len && !is_global_key(u));
                     else ok = u >= lo && u <= hi && u < len;
                     x[c][e] = ok ? sv * a.scale_log2 : -__builtin_inff();
                     mx = fmaxf(mx, x[c][e]);
@@ -345,7 +447,7 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
             const u32x4 pb{pack2(p[0], p[1], In{}), pack2(p[2], p[3], In{}),
                            pack2(p[4], p[5], In{}), pack2(p[6], p[7], In{})};
             const V bop = __builtin_bit_cast(V, pb);
-            const unsigned char* rp = vw + (32 * c + 8 * grp) * (2 * D);
+            const unsigned char* rp = vlds + (32 * c + 8 * grp) * (2 * D);
 #pragma unroll
             for (int cb = 0; cb < kCb; ++cb) {
                 const V av = tr_read8<V, D>(rp + aoff[cb]);
@@ -357,12 +459,12 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     // The next block's loads overlap this block's compute (a clamped repeat of the last
     // block when there is none, so the loads are unconditional).
     if constexpr (kMode == kBandGlobal) {
-        const int ngb = (ng + kKeys - 1) / kKeys;
+        const int ngb = (ngd + kKeys - 1) / kKeys;
         for (int gb = 0; gb < ngb; ++gb) {
             load_gblock(gb);
             store_gblock(gb);
             __syncthreads();
-            compute_block(kKeys * gb, true);
+            if (wave_live) compute_block(kKeys * gb, true);
             __syncthreads();
         }
     }
@@ -372,64 +474,32 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
         store_block(u0);
         __syncthreads();
         load_block(blk + 1 < nblk ? u0 + kKeys : u0);
-        compute_block(u0, false);
+        if (wave_live) compute_block(u0, false);
         __syncthreads();
     }
 
-    // ---- normalise and store: lane (col, grp) holds channels 16 cb + 4 grp .. +3
     float l = l_run;
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    if constexpr (kMode == kGlobalRows) {
-        // merge the waves' partial softmax states of the same 16 rows: scale each
-        // by 2^(m_w - max m), add, divide (LDS is free: the loop ended on a barrier)
-        constexpr int S = kCb * 4 + 2;
-        float* mb = reinterpret_cast<float*>(klds);
-        float* mine = mb + (wv * 64 + lane) * S;
+    if constexpr (kRowsMode) {
+        // ---- this range's partial state of the rows (merged by the second launch)
+        if (tq < ngd) {
+            const int64_t slot = ((bh * a.nrb + rb) * a.nsplit + split) * kRows + 16 * wv + col;
+            float* pa = gi.part_acc + slot * D + 4 * grp;
 #pragma unroll
-        for (int cb = 0; cb < kCb; ++cb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) mine[cb * 4 + e] = acc[cb][e];
-        mine[kCb * 4] = m_run;
-        mine[kCb * 4 + 1] = l;
-        __syncthreads();
-        if (wv != 0 || tq >= ng) return;
-        float M = -__builtin_inff();
-#pragma unroll
-        for (int w4 = 0; w4 < kSplit; ++w4) M = fmaxf(M, mb[(w4 * 64 + lane) * S + kCb * 4]);
-        float L = 0.0f;
-        f32x4 A[kCb];
-#pragma unroll
-        for (int cb = 0; cb < kCb; ++cb) A[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w4 = 0; w4 < kSplit; ++w4) {
-            const float* o = mb + (w4 * 64 + lane) * S;
-            const float f = o[kCb * 4] == -__builtin_inff()
-                                ? 0.0f : __builtin_amdgcn_exp2f(o[kCb * 4] - M);
-            L += o[kCb * 4 + 1] * f;
-#pragma unroll
-            for (int cb = 0; cb < kCb; ++cb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) A[cb][e] += o[cb * 4 + e] * f;
-        }
-        const float inv = 1.0f / L;
-        ST* orow = out + base + int64_t(tq_ld) * step + 4 * grp;
-#pragma unroll
-        for (int cb = 0; cb < kCb; ++cb) {
-            const u32x2 o2{pack2(A[cb][0] * inv, A[cb][1] * inv, In{}),
-                           pack2(A[cb][2] * inv, A[cb][3] * inv, In{})};
-            *reinterpret_cast<u32x2*>(orow + 16 * cb) = o2;
+            for (int cb = 0; cb < kCb; ++cb) *reinterpret_cast<f32x4*>(pa + 16 * cb) = acc[cb];
+            if (grp == 0) *reinterpret_cast<f32x2*>(gi.part_ml + 2 * slot) = f32x2{m_run, l};
         }
         return;
     }
+    // ---- normalise and store: lane (col, grp) holds channels 16 cb + 4 grp .. +3
     bool store = tq < len;
-    const int64_t orow_t = tq;
     if constexpr (kMode == kBandGlobal) {
-        store = store && !is_global_key(tq);   // global rows come from the global-row pass
+        store = store && !is_global_key(tq);   // global rows come from the global-row units
     }
     if (store) {
         const float inv = 1.0f / l;
-        ST* orow = out + base + orow_t * step + 4 * grp;
+        ST* orow = out + base + int64_t(tq) * step + 4 * grp;
 #pragma unroll
         for (int cb = 0; cb < kCb; ++cb) {
             const u32x2 o{pack2(acc[cb][0] * inv, acc[cb][1] * inv, In{}),
@@ -439,8 +509,102 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
     }
 }
 
+template <class In, int D>
+__global__ void __launch_bounds__(kThreads)
+attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __restrict__ k,
+                const typename In::T* __restrict__ v, typename In::T* __restrict__ out,
+                AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char klds[kKeys * 2 * D];
+    __shared__ __attribute__((aligned(16))) unsigned char vlds[kKeys * 2 * D];
+    __shared__ uint32_t gbits[1];
+    const GlobalIn<typename In::T> none{};
+    attn_body<In, D, kBand>(q, k, v, out, none, a, xcd_order(blockIdx.x, a.groups), klds, vlds,
+                            gbits, nullptr, nullptr, nullptr);
+}
+
+// The global-row units (rows_groups workgroups, the padding ones idle), then the band
+// workgroups with the global keys.  Dynamic LDS: the global set (2 ceil(n / 32) words).
+template <class In, int D>
+__global__ void __launch_bounds__(kThreads)
+attn_global_kernel(const typename In::T* __restrict__ q, const typename In::T* __restrict__ k,
+                   const typename In::T* __restrict__ v, typename In::T* __restrict__ out,
+                   GlobalIn<typename In::T> gi, AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char klds[kKeys * 2 * D];
+    __shared__ __attribute__((aligned(16))) unsigned char vlds[kKeys * 2 * D];
+    __shared__ uint32_t gbits[kBitWords];
+    __shared__ uint32_t wsum[4];
+    extern __shared__ uint32_t gdyn[];
+    uint32_t* const gmap = gdyn;
+    uint32_t* const gpre = gdyn + ((a.n + 31) >> 5);
+    const int64_t bid = blockIdx.x;
+    if (bid < a.rows_groups) {
+        if (bid < a.rows_used)
+            attn_body<In, D, kGlobalRows>(q, k, v, out, gi, a, bid, klds, vlds, gbits, gmap, gpre,
+                                          wsum);
+        return;
+    }
+    attn_body<In, D, kBandGlobal>(q, k, v, out, gi, a, xcd_order(bid - a.rows_groups, a.groups),
+                                  klds, vlds, gbits, gmap, gpre, wsum);
+}
+
+// The global rows: block blockIdx.x = (batch, head, row block) merges its nsplit partial
+// states per row and stores the rows.  Every load of a phase is independent of the others
+// (the states of all rows and ranges at once, then the outputs), so the merge costs a few
+// memory latencies whatever nsplit is.
+template <class In, int D>
+__global__ void __launch_bounds__(kThreads)
+attn_gmerge_kernel(typename In::T* __restrict__ out, GlobalIn<typename In::T> gi, AttnArgs a) {
+    using ST = typename In::T;
+    constexpr int kQuads = D / 4;
+    __shared__ float fac[kRows * kMaxSplit];             // per (row, range): exp2(m - M), then
+    __shared__ float lsum[kRows * kMaxSplit];            // its running sum
+    __shared__ float inv_l[kRows];
+    __shared__ int pos_s[kRows];
+    const int tid = threadIdx.x;
+    const int ns = a.nsplit;
+    const int64_t blk_id = blockIdx.x;
+    const int64_t bh = blk_id / a.nrb, bb = bh / a.h, hh = bh - bb * a.h;
+    const int64_t slot0 = blk_id * ns * kRows;           // row 0 of range 0
+    if (tid < kRows) pos_s[tid] = gi.gpos[blk_id * kRows + tid];
+    for (int i = tid; i < kRows * ns; i += kThreads) {
+        const int sp = i / kRows, rr = i - sp * kRows;
+        const f32x2 ml =
+            *reinterpret_cast<const f32x2*>(gi.part_ml + 2 * (slot0 + int64_t(sp) * kRows + rr));
+        fac[rr * kMaxSplit + sp] = ml[0];
+        lsum[rr * kMaxSplit + sp] = ml[1];
+    }
+    __syncthreads();
+    if (tid < kRows && pos_s[tid] >= 0) {
+        float* f = fac + tid * kMaxSplit;
+        float M = -__builtin_inff();
+        for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, f[sp]);
+        float L = 0.0f;
+        for (int sp = 0; sp < ns; ++sp) {
+            f[sp] = f[sp] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(f[sp] - M);
+            L += lsum[tid * kMaxSplit + sp] * f[sp];
+        }
+        inv_l[tid] = 1.0f / L;
+    }
+    __syncthreads();
+    for (int it = tid; it < kRows * kQuads; it += kThreads) {
+        const int rr = it / kQuads, c4 = it - rr * kQuads;
+        const int pos = pos_s[rr];
+        if (pos < 0) continue;
+        const float* f = fac + rr * kMaxSplit;
+        const float* pa = gi.part_acc + (slot0 + rr) * D + 4 * c4;
+        f32x4 A{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int sp = 0; sp < ns; ++sp)
+            A += f[sp] * *reinterpret_cast<const f32x4*>(pa + int64_t(sp) * kRows * D);
+        const float inv = inv_l[rr];
+        ST* orow = out + ((bb * a.n + pos) * a.h + hh) * D + 4 * c4;
+        *reinterpret_cast<u32x2*>(orow) =
+            u32x2{pack2(A[0] * inv, A[1] * inv, In{}), pack2(A[2] * inv, A[3] * inv, In{})};
+    }
+}
+
 AttnArgs make_args(const Problem& p, float scale, int64_t ng = 0) {
-    AttnArgs a;
+    AttnArgs a{};
     a.n = p.n;
     a.h = p.h;
     a.w = p.w;
@@ -454,43 +618,85 @@ AttnArgs make_args(const Problem& p, float scale, int64_t ng = 0) {
     a.groups = p.b * p.h * a.per_head;
     a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
     a.ng = static_cast<int32_t>(ng);
-    a.ngb = (ng + 15) / 16;   // global rows are taken 16 per workgroup
+    if (ng > 0 && p.n > 0) {
+        // key ranges: about 256 global-row workgroups in all (a few 64-key blocks each),
+        // never an empty range
+        a.nrb = static_cast<int32_t>((ng + kRows - 1) / kRows);
+        const int64_t units = p.b * p.h * a.nrb;
+        const int64_t blocks = (p.n + kKeys - 1) / kKeys;
+        int64_t nsplit = (256 + units - 1) / units;
+        nsplit = nsplit < blocks ? nsplit : blocks;
+        nsplit = nsplit < kMaxSplit ? nsplit : kMaxSplit;
+        const int64_t kr = (blocks + nsplit - 1) / nsplit * kKeys;
+        a.kr = static_cast<int32_t>(kr);
+        a.nsplit = static_cast<int32_t>((p.n + kr - 1) / kr);
+        a.rows_used = units * a.nsplit;
+        a.rows_groups = (a.rows_used + 7) / 8 * 8;
+    }
     return a;
 }
 
-template <class In, int D, int kMode>
-void launch_mode(const void* q, const void* k, const void* v, void* out, const int32_t* glob,
-                 AttnArgs a, int64_t b, hipStream_t stream) {
-    using ST = typename In::T;
-    if (kMode == kGlobalRows) a.groups = b * a.h * a.ngb;
-    launch_kernel(attn_fwd_kernel<In, D, kMode>, dim3(static_cast<uint32_t>(a.groups)),
-                  dim3(mode_threads(kMode, D)), 0, stream, static_cast<const ST*>(q), static_cast<const ST*>(k),
-                  static_cast<const ST*>(v), static_cast<ST*>(out), glob, a);
+// Workspace of the global-token form: the positions of the global rows and their
+// partial states; each part 256-byte aligned.
+struct GlobalWs {
+    int64_t pos, acc, ml, total;
+};
+GlobalWs ws_layout(const Problem& p, int64_t ng) {
+    GlobalWs w{};
+    if (ng <= 0) return w;
+    const AttnArgs a = make_args(p, 1.0f, ng);
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t blocks = p.b * p.h * a.nrb;
+    const int64_t slots = blocks * int64_t(a.nsplit) * kRows;
+    w.pos = 0;
+    w.acc = w.pos + up(blocks * kRows * 4);
+    w.ml = w.acc + up(slots * p.d * 4);
+    w.total = w.ml + up(slots * 2 * 4);
+    return w;
 }
 
-// Without global tokens one pass; with them the rows outside the global set (window and
-// global keys), then the global rows over every key - disjoint output rows, one stream.
 template <class In, int D>
-hipError_t launch_t(const void* q, const void* k, const void* v, void* out, const int32_t* glob,
-                    const AttnArgs& a, int64_t b, hipStream_t stream) {
+hipError_t launch_t(const void* q, const void* k, const void* v, const void* gq,
+                    const void* gk, const void* gv, void* out, const int32_t* glob,
+                    unsigned char* ws, const AttnArgs& a, int64_t b, const GlobalWs& wl,
+                    hipStream_t stream) {
+    using ST = typename In::T;
     if (a.ng == 0) {
-        launch_mode<In, D, kBand>(q, k, v, out, nullptr, a, b, stream);
-    } else {
-        launch_mode<In, D, kBandGlobal>(q, k, v, out, glob, a, b, stream);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        launch_mode<In, D, kGlobalRows>(q, k, v, out, glob, a, b, stream);
+        launch_kernel(attn_fwd_kernel<In, D>, dim3(static_cast<uint32_t>(a.groups)),
+                      dim3(kThreads), 0, stream, static_cast<const ST*>(q),
+                      static_cast<const ST*>(k), static_cast<const ST*>(v),
+                      static_cast<ST*>(out), a);
+        return hipGetLastError();
     }
+    GlobalIn<ST> gi;
+    gi.glob = glob;
+    gi.gq = static_cast<const ST*>(gq);
+    gi.gk = static_cast<const ST*>(gk);
+    gi.gv = static_cast<const ST*>(gv);
+    gi.gpos = reinterpret_cast<int32_t*>(ws + wl.pos);
+    gi.part_acc = reinterpret_cast<float*>(ws + wl.acc);
+    gi.part_ml = reinterpret_cast<float*>(ws + wl.ml);
+    const size_t set_lds = static_cast<size_t>((a.n + 31) / 32) * 2 * 4;
+    launch_kernel(attn_global_kernel<In, D>,
+                  dim3(static_cast<uint32_t>(a.rows_groups + a.groups)), dim3(kThreads), set_lds,
+                  stream, static_cast<const ST*>(q), static_cast<const ST*>(k),
+                  static_cast<const ST*>(v), static_cast<ST*>(out), gi, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    launch_kernel(attn_gmerge_kernel<In, D>, dim3(static_cast<uint32_t>(b * a.h * a.nrb)),
+                  dim3(kThreads), 0, stream, static_cast<ST*>(out), gi, a);
     return hipGetLastError();
 }
 
 template <class In>
-hipError_t launch_d(const void* q, const void* k, const void* v, void* out, const int32_t* glob,
-                    const AttnArgs& a, int64_t b, int64_t d, hipStream_t stream) {
+hipError_t launch_d(const void* q, const void* k, const void* v, const void* gq,
+                    const void* gk, const void* gv, void* out, const int32_t* glob,
+                    unsigned char* ws, const AttnArgs& a, int64_t b, int64_t d,
+                    const GlobalWs& wl, hipStream_t stream) {
     switch (d) {
-    case 32: return launch_t<In, 32>(q, k, v, out, glob, a, b, stream);
-    case 64: return launch_t<In, 64>(q, k, v, out, glob, a, b, stream);
-    case 128: return launch_t<In, 128>(q, k, v, out, glob, a, b, stream);
+    case 32: return launch_t<In, 32>(q, k, v, gq, gk, gv, out, glob, ws, a, b, wl, stream);
+    case 64: return launch_t<In, 64>(q, k, v, gq, gk, gv, out, glob, ws, a, b, wl, stream);
+    case 128: return launch_t<In, 128>(q, k, v, gq, gk, gv, out, glob, ws, a, b, wl, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -512,23 +718,40 @@ bool attention_supported(const Problem& p, int dt, const void* q, const void* k,
     return a.groups < (int64_t(1) << 31);
 }
 
-// With global tokens the key range of a workgroup (64 + w + w_upper keys) must fit the
-// LDS bitmap of global keys.
+// With global tokens: the key range of a band workgroup (64 + w + w_upper keys) must fit
+// its LDS bitmap of global keys, the sequence the LDS global set (n <= 2^16), and
+// the whole grid 2^31 workgroups.
 bool attention_global_supported(const Problem& p, int64_t ng) {
-    return 64 + p.w + p.wu <= int64_t(kBitWords) * 32 && ng >= 0 && ng <= p.n &&
-           p.b * p.h * ((ng + 15) / 16) < (int64_t(1) << 31);
+    if (ng == 0) return true;
+    if (!(64 + p.w + p.wu <= int64_t(kBitWords) * 32 && ng > 0 && ng <= p.n &&
+          p.n <= kMaxGlobalN))
+        return false;
+    const AttnArgs a = make_args(p, 1.0f, ng);
+    return a.rows_groups + a.groups < (int64_t(1) << 31) && p.b < (int64_t(1) << 31);
+}
+
+int64_t attention_global_workspace(const Problem& p, int64_t ng) {
+    return ws_layout(p, ng).total;
 }
 
 int64_t attention_workgroups(const Problem& p) { return make_args(p, 1.0f).groups; }
 
-hipError_t launch_attention(const void* q, const void* k, const void* v, void* out,
-                            const int32_t* glob, int64_t ng, const Problem& p, float scale,
+hipError_t launch_attention(const void* q, const void* k, const void* v, const void* gq,
+                            const void* gk, const void* gv, void* out, const int32_t* glob,
+                            int64_t ng, void* workspace, const Problem& p, float scale,
                             int dt, hipStream_t stream) {
     const AttnArgs a = make_args(p, scale, ng);
     if (a.groups == 0) return hipSuccess;
+    const GlobalWs wl = ws_layout(p, ng);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    if (!gq) {
+        gq = q;
+        gk = k;
+        gv = v;
+    }
     switch (dt) {
-    case kF16: return launch_d<F16>(q, k, v, out, glob, a, p.b, p.d, stream);
-    case kBF16: return launch_d<BF16>(q, k, v, out, glob, a, p.b, p.d, stream);
+    case kF16: return launch_d<F16>(q, k, v, gq, gk, gv, out, glob, ws, a, p.b, p.d, wl, stream);
+    case kBF16: return launch_d<BF16>(q, k, v, gq, gk, gv, out, glob, ws, a, p.b, p.d, wl, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -60,10 +60,16 @@ hipError_t launch_dropout(const void* probs, const float* rand, void* out, const
 bool attention_supported(const Problem& p, int dt, const void* q, const void* k, const void* v,
                          const void* out);
 bool attention_global_supported(const Problem& p, int64_t ng);
+// Workspace bytes of the global-token form (0 when ng == 0): the positions of the global
+// rows and their partial softmax states.
+int64_t attention_global_workspace(const Problem& p, int64_t ng);
 int64_t attention_workgroups(const Problem& p);
-// glob: ng int32 positions per batch on the device (ignored when ng == 0)
-hipError_t launch_attention(const void* q, const void* k, const void* v, void* out,
-                            const int32_t* glob, int64_t ng, const Problem& p, float scale,
+// glob: ng int32 positions per batch on the device (ignored when ng == 0); gq, gk, gv:
+// the global rows' matrices (NULL: q, k, v); workspace: attention_global_workspace bytes,
+// 256-byte aligned, on the device (ignored when ng == 0).
+hipError_t launch_attention(const void* q, const void* k, const void* v, const void* gq,
+                            const void* gk, const void* gv, void* out, const int32_t* glob,
+                            int64_t ng, void* workspace, const Problem& p, float scale,
                             int dt, hipStream_t stream);
 
 // qk on MFMA (f16 / bf16 inputs, d in {32, 64, 128}, 16-byte aligned pointers).

@@ -38,7 +38,8 @@ def test_header_declares_the_calls():
     for want in ("diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax",
                  "diagmm_banded_softmax_backward", "diagmm_banded_softmax_masked",
                  "diagmm_banded_dropout", "diagmm_banded_attention",
-                 "diagmm_banded_attention_global", "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
+                 "diagmm_banded_attention_global", "diagmm_banded_attention_global_workspace",
+                 "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
                  "diagmm_plan"):
         assert want in names
 
@@ -49,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dm.diagmm_abi_version() == 7
+    assert dm.diagmm_abi_version() == 8
     seen = set()
     for st in range(7):
         s = lib.diagmm_status_string(st).decode()
@@ -129,11 +130,31 @@ def test_validation_errors_are_reported_without_launching(lib):
     assert "diagmm_banded_attention" in lib.diagmm_last_error().decode()
     ag = lib.diagmm_banded_attention_global
     G_ = FAKE + (1 << 39)
-    assert ag(Q_, K_, V_, O_, 0, 2, 1, 8, 1, 64, 2, 2, 0, 0.125, 1, None) == ERR_NULL
-    assert ag(Q_, K_, V_, O_, G_, 9, 1, 8, 1, 64, 2, 2, 0, 0.125, 1, None) == ERR_SHAPE   # ng > n
-    assert ag(Q_, K_, V_, O_, G_, -1, 1, 8, 1, 64, 2, 2, 0, 0.125, 1, None) == ERR_SHAPE
-    assert ag(Q_, K_, V_, G_ - 8, G_, 2, 1, 8, 1, 64, 2, 2, 0, 0.125, 1, None) == ERR_ALIAS
-    assert ag(Q_, K_, V_, O_, G_, 2, 1, 8, 1, 64, 9000, 9000, 0, 0.125, 1, None) == ERR_UNSUPPORTED
+    W_ = FAKE + (1 << 40)                       # a 256-byte aligned workspace
+    need = ctypes.c_int64(-1)
+    wsq = lib.diagmm_banded_attention_global_workspace
+    assert wsq(1, 8, 1, 64, 2, 2, 0, 2, ctypes.byref(need)) == OK and need.value > 0
+    assert wsq(1, 8, 1, 64, 2, 2, 0, 0, ctypes.byref(need)) == OK and need.value == 0
+    assert wsq(1, 8, 1, 64, 2, 2, 0, 9, ctypes.byref(need)) == ERR_SHAPE
+    assert wsq(1, 8, 1, 64, 2, 2, 0, 2, None) == ERR_NULL
+    assert wsq(1, 8, 1, 64, 2, 2, 0, 2, ctypes.byref(need)) == OK
+    NW = need.value
+
+    def agc(q=Q_, k=K_, v=V_, gq=None, gk=None, gv=None, o=O_, g=G_, ng=2, n=8, w=2,
+            ws=W_, wsb=NW, d=64, dt=1):
+        return ag(q, k, v, gq, gk, gv, o, g, ng, 1, n, 1, d, w, w, 0, 0.125, dt, ws, wsb, None)
+    assert agc(g=0) == ERR_NULL
+    assert agc(ws=0) == ERR_NULL
+    assert agc(gq=Q_ + (1 << 35)) == ERR_NULL                 # one global matrix of three
+    assert agc(ng=9) == ERR_SHAPE                             # ng > n
+    assert agc(ng=-1) == ERR_SHAPE
+    assert agc(wsb=NW - 1) == ERR_SHAPE                       # workspace too small
+    assert agc(o=G_ - 8) == ERR_ALIAS                         # out over global_pos
+    assert agc(ws=O_) == ERR_ALIAS                            # workspace over out
+    assert agc(ws=K_) == ERR_ALIAS                            # workspace over k
+    assert agc(ws=W_ + 16) == ERR_UNSUPPORTED                 # workspace not 256-aligned
+    assert agc(w=9000) == ERR_UNSUPPORTED
+    assert agc(gq=Q_ + (1 << 35) + 2, gk=Q_ + (1 << 36), gv=Q_ + (1 << 37)) == ERR_UNSUPPORTED
     assert "diagmm_banded_attention_global" in lib.diagmm_last_error().decode()
 
 

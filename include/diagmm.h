@@ -234,6 +234,24 @@ diagmm_status_t diagmm_banded_attention_global(const void* q, const void* k, con
                                                void* stream);
 
 /*
+ * diagmm_banded_attention_global_noalloc - diagmm_banded_attention_global for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same operation and checks, with no workspace
+ * argument.  The workspace is a static 32 MiB device array of the library (one per GPU,
+ * held until the process ends); the call allocates nothing.  Sizes that need more than
+ * 32 MiB of workspace (diagmm_banded_attention_global_workspace) are
+ * DIAGMM_ERR_UNSUPPORTED.  All calls of a process on one GPU share that GPU's array:
+ * calls that may overlap in time there (on different streams, or from threads without
+ * ordering between them) race and must not be issued.  The array is found on the calling
+ * thread's current device, which must be the device of `stream`.
+ */
+diagmm_status_t diagmm_banded_attention_global_noalloc(
+    const void* q, const void* k, const void* v, const void* global_q, const void* global_k,
+    const void* global_v, void* out, const int32_t* global_pos, int64_t ng, int64_t b,
+    int64_t n, int64_t h, int64_t d, int64_t w, int64_t w_upper, int64_t dilation, float scale,
+    diagmm_dtype_t dtype, void* stream);
+
+/*
  * Workspace bytes diagmm_banded_attention_global needs for these sizes (0 when ng = 0)
  * in *bytes.  DIAGMM_ERR_SHAPE for sizes that call would refuse as such, DIAGMM_ERR_NULL
  * for a NULL bytes.

@@ -25,7 +25,8 @@ import torch
 
 __all__ = ["diagmm_qk", "diagmm_pv", "diagmm_pvT", "diagmm_banded_softmax",
            "diagmm_banded_softmax_backward", "diagmm_banded_dropout", "diagmm_banded_attention",
-           "diagmm_banded_attention_global", "diagmm_plan",
+           "diagmm_banded_attention_global", "diagmm_banded_attention_global_noalloc",
+           "diagmm_plan",
            "diagmm_timing_begin", "diagmm_timing_end", "diagmm_timing_read",
            "diagmm_abi_version", "library_path", "load", "DiagmmError"]
 
@@ -88,6 +89,8 @@ def load() -> ctypes.CDLL:
     lib.diagmm_banded_attention_global.restype = ci
     lib.diagmm_banded_attention_global_workspace.argtypes = [i64] * 8 + [ctypes.POINTER(i64)]
     lib.diagmm_banded_attention_global_workspace.restype = ci
+    lib.diagmm_banded_attention_global_noalloc.argtypes = [vp] * 8 + [i64] * 8 + [f32, ci, vp]
+    lib.diagmm_banded_attention_global_noalloc.restype = ci
     lib.diagmm_status_string.argtypes = [ci]
     lib.diagmm_status_string.restype = ctypes.c_char_p
     lib.diagmm_last_error.argtypes = []
@@ -347,6 +350,42 @@ def diagmm_banded_attention_global(q, k, v, global_pos, w, w_upper=None, dilatio
                                             g.shape[1], b, n, h, d, w, w_upper, dilation,
                                             float(scale), _DT[q.dtype], ws_ptr, need.value,
                                             _stream(q.device))
+    if st:
+        _raise(lib, st)
+    return res
+
+
+def diagmm_banded_attention_global_noalloc(q, k, v, global_pos, w, w_upper=None, dilation=0,
+                                           scale=None, out=None, global_qkv=None):
+    """``diagmm_banded_attention_global`` through the library's allocation-free entry point:
+    its workspace is the library's static per-GPU array (calls on one GPU must not overlap
+    in time); only ``out`` is allocated here, and only when it is not given."""
+    lib = load()
+    w, w_upper, dilation = _window(w, w_upper, dilation)
+    q, k, v = _dense(q, "q"), _dense(k, "k"), _dense(v, "v")
+    if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype
+            and q.device == k.device == v.device):
+        raise ValueError("q, k and v must have the same shape, dtype and device")
+    gptr = [None, None, None]
+    if global_qkv is not None:
+        gq, gk, gv = (_dense(t, "global_qkv") for t in global_qkv)
+        for t in (gq, gk, gv):
+            if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+                raise ValueError("global_qkv tensors must match q in shape, dtype and device")
+        gptr = [gq.data_ptr(), gk.data_ptr(), gv.data_ptr()]
+    b, n, h, d = q.shape
+    g = global_pos
+    if (not isinstance(g, torch.Tensor) or g.dtype != torch.int32 or g.dim() != 2
+            or g.shape[0] != b or g.device != q.device or not g.is_contiguous()):
+        raise ValueError("global_pos must be a contiguous int32 [b, ng] tensor on q's device")
+    if scale is None:
+        scale = d ** -0.5
+    res = _out(out, q.shape, q.dtype, q.device)
+    with torch.cuda.device(q.device):
+        st = lib.diagmm_banded_attention_global_noalloc(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), gptr[0], gptr[1], gptr[2], res.data_ptr(),
+            g.data_ptr(), g.shape[1], b, n, h, d, w, w_upper, dilation, float(scale),
+            _DT[q.dtype], _stream(q.device))
     if st:
         _raise(lib, st)
     return res

@@ -5,6 +5,7 @@
 #include <cstdlib>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/diagmm.h"
 #include "launch.hpp"
@@ -389,16 +390,15 @@ diagmm_status_t diagmm_banded_attention_global_workspace(int64_t b, int64_t n, i
     return ok();
 }
 
-diagmm_status_t diagmm_banded_attention_global(const void* q, const void* k, const void* v,
-                                               const void* global_q, const void* global_k,
-                                               const void* global_v, void* out,
-                                               const int32_t* global_pos, int64_t ng,
-                                               int64_t b, int64_t n, int64_t h, int64_t d,
-                                               int64_t w, int64_t w_upper, int64_t dilation,
-                                               float scale, diagmm_dtype_t dtype,
-                                               void* workspace, int64_t workspace_bytes,
-                                               void* stream) {
-    const char* fn = "diagmm_banded_attention_global";
+// The global-token call on a given workspace (validated here).
+static diagmm_status_t attention_global_impl(const char* fn, const void* q, const void* k,
+                                             const void* v, const void* global_q,
+                                             const void* global_k, const void* global_v,
+                                             void* out, const int32_t* global_pos, int64_t ng,
+                                             int64_t b, int64_t n, int64_t h, int64_t d,
+                                             int64_t w, int64_t w_upper, int64_t dilation,
+                                             float scale, diagmm_dtype_t dtype, void* workspace,
+                                             int64_t workspace_bytes, void* stream) {
     Problem p;
     int64_t de, need;
     diagmm_status_t st = check_global(fn, b, n, h, d, w, w_upper, dilation, ng, dtype, &p, &de,
@@ -439,6 +439,82 @@ diagmm_status_t diagmm_banded_attention_global(const void* q, const void* k, con
     return launched(fn, launch_attention(q, k, v, global_q, global_k, global_v, out, global_pos,
                                          ng, workspace, p, scale, dtype,
                                          static_cast<hipStream_t>(stream)));
+}
+
+diagmm_status_t diagmm_banded_attention_global(const void* q, const void* k, const void* v,
+                                               const void* global_q, const void* global_k,
+                                               const void* global_v, void* out,
+                                               const int32_t* global_pos, int64_t ng,
+                                               int64_t b, int64_t n, int64_t h, int64_t d,
+                                               int64_t w, int64_t w_upper, int64_t dilation,
+                                               float scale, diagmm_dtype_t dtype,
+                                               void* workspace, int64_t workspace_bytes,
+                                               void* stream) {
+    return attention_global_impl("diagmm_banded_attention_global", q, k, v, global_q, global_k,
+                                 global_v, out, global_pos, ng, b, n, h, d, w, w_upper,
+                                 dilation, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- allocation-free form
+// A file-scope device array serves as the workspace of the global-token call for callers
+// that cannot allocate.  Each GPU the library runs on holds its own copy for the life of
+// the process; its address on a device is looked up once per device, with that device
+// current, and only that address is handed to kernels (the array's name is a host-side
+// stand-in).  Calls on one GPU share the array: calls that overlap in time race.
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the current device (looked up on the first call there).
+static diagmm_status_t scratch_address(const char* fn, void** out) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DIAGMM_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(DIAGMM_ERR_UNSUPPORTED, "%s: device %d (at most %d devices)", fn, dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t s = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (s != hipSuccess || !ptr)
+            return fail(DIAGMM_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn,
+                        dev, hipGetErrorString(s));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DIAGMM_OK;
+}
+
+diagmm_status_t diagmm_banded_attention_global_noalloc(
+    const void* q, const void* k, const void* v, const void* global_q, const void* global_k,
+    const void* global_v, void* out, const int32_t* global_pos, int64_t ng, int64_t b,
+    int64_t n, int64_t h, int64_t d, int64_t w, int64_t w_upper, int64_t dilation, float scale,
+    diagmm_dtype_t dtype, void* stream) {
+    const char* fn = "diagmm_banded_attention_global_noalloc";
+    Problem p;
+    int64_t de, need;
+    diagmm_status_t st = check_global(fn, b, n, h, d, w, w_upper, dilation, ng, dtype, &p, &de,
+                                      &need);
+    if (st != DIAGMM_OK) return st;
+    if (p.rows() * p.h == 0) return ok();
+    if (need > kScratchBytes)
+        return fail(DIAGMM_ERR_UNSUPPORTED, "%s: needs %lld bytes of scratch, the static "
+                    "scratch holds %lld (use diagmm_banded_attention_global with a workspace)",
+                    fn, static_cast<long long>(need), static_cast<long long>(kScratchBytes));
+    if (!q || !k || !v || !out || (ng > 0 && !global_pos))
+        return fail(DIAGMM_ERR_NULL, "%s: null pointer", fn);
+    void* ws = nullptr;
+    if (need > 0) {
+        st = scratch_address(fn, &ws);
+        if (st != DIAGMM_OK) return st;
+    }
+    return attention_global_impl(fn, q, k, v, global_q, global_k, global_v, out, global_pos, ng,
+                                 b, n, h, d, w, w_upper, dilation, scale, dtype, ws,
+                                 need > 0 ? kScratchBytes : 0, stream);
 }
 
 diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,

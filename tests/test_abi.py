@@ -39,6 +39,7 @@ def test_header_declares_the_calls():
                  "diagmm_banded_softmax_backward", "diagmm_banded_softmax_masked",
                  "diagmm_banded_dropout", "diagmm_banded_attention",
                  "diagmm_banded_attention_global", "diagmm_banded_attention_global_workspace",
+                 "diagmm_banded_attention_global_noalloc",
                  "diagmm_status_string", "diagmm_last_error", "diagmm_abi_version",
                  "diagmm_plan"):
         assert want in names
@@ -156,6 +157,23 @@ def test_validation_errors_are_reported_without_launching(lib):
     assert agc(w=9000) == ERR_UNSUPPORTED
     assert agc(gq=Q_ + (1 << 35) + 2, gk=Q_ + (1 << 36), gv=Q_ + (1 << 37)) == ERR_UNSUPPORTED
     assert "diagmm_banded_attention_global" in lib.diagmm_last_error().decode()
+
+
+def test_noalloc_call_rejects_before_touching_the_device(lib):
+    """The allocation-free global-token call checks sizes before any HIP call: ng outside
+    [0, n] and a workspace need beyond its 32 MiB static array are refused (b=8, h=16,
+    d=128, 512 global rows per batch needs just over 32 MiB); an empty problem is a no-op."""
+    na = lib.diagmm_banded_attention_global_noalloc
+    need = ctypes.c_int64(0)
+    assert lib.diagmm_banded_attention_global_workspace(8, 512, 16, 128, 4, 4, 0, 512,
+                                                        ctypes.byref(need)) == OK
+    assert need.value > 32 << 20
+    assert na(0, 0, 0, None, None, None, 0, 0, 512, 8, 512, 16, 128, 4, 4, 0, 0.1, 1,
+              None) == ERR_UNSUPPORTED
+    assert "scratch" in lib.diagmm_last_error().decode()
+    assert na(0, 0, 0, None, None, None, 0, 0, 9, 1, 8, 1, 64, 2, 2, 0, 0.1, 1,
+              None) == ERR_SHAPE
+    assert na(0, 0, 0, None, None, None, 0, 0, 0, 1, 0, 1, 64, 2, 2, 0, 0.1, 1, None) == OK
 
 
 def test_empty_problems_are_noops(lib):

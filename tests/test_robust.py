@@ -138,3 +138,115 @@ def test_tiled_kernels_agree_with_element_kernels(shape, monkeypatch):
     for name, a, s in zip(("qk", "pv", "pvT", "softmax"), fast, slow):
         check_close(a.cpu(), s.cpu().double(), q.dtype, name + " tiled vs element",
                     abs_tol=None if q.dtype == torch.float32 else 2e-3)
+
+
+# ---------------------------------------------------------------- the newer calls
+# The softmax backward, the masked softmax, the dropout, the one-pass attention and the
+# global-token attention (both entry points): nothing written outside the output, bitwise
+# reruns, out-of-range band slots never read, in place = out of place.
+
+def _band_inputs(shape, seed):
+    b, n, h, d, w, wu, dil, dt = shape
+    g = datagen.rng(seed)
+    K = w + wu + 1
+    p = datagen.softmax_rows(g, (b, n, h, K), dt).cuda()
+    dp = datagen.normal(g, (b, n, h, K), dt).cuda()
+    rand = datagen.uniform(g, (b, n, h, K)).cuda()
+    mask = torch.ones((b, n), dtype=torch.float32)
+    mask[:, ::7] = 0.0
+    return p, dp, rand, mask.cuda()
+
+
+def _glob(b, n):
+    """Positions with a repeat and entries outside [0, n) (the set is {0, 5, n // 2, n - 1})."""
+    row = [0, 5, n // 2, 5, -3, n - 1, n + 9]
+    return torch.tensor([row] * b, dtype=torch.int32, device="cuda")
+
+
+def _newer_calls(shape, seed):
+    """(name, fn(out=None) -> tensor, output shape, output dtype) for every newer call
+    the shape's dtype supports."""
+    import sliding_window_attention_diagmm_amd as dm
+    b, n, h, d, w, wu, dil, dt = shape
+    p, dp, rand, mask = _band_inputs(shape, seed)
+    q, k, _ = _inp(shape, seed + 1)
+    v = k.flip(1).contiguous()
+    K = w + wu + 1
+    calls = [
+        ("softmax_bwd", lambda out=None: dm.diagmm_banded_softmax_backward(
+            p, dp, w, wu, dil, 0.5, out=out), (b, n, h, K), p.dtype),
+        ("softmax_masked", lambda out=None: dm.diagmm_banded_softmax(
+            dp, w, wu, dil, 0.5, out=out, key_mask=mask), (b, n, h, K), p.dtype),
+        ("dropout", lambda out=None: dm.diagmm_banded_dropout(p, rand, w, wu, dil, 0.25, out=out),
+         (b, n, h, K), p.dtype),
+    ]
+    if q.dtype != torch.float32:
+        glob = _glob(b, n)
+        gq, gk, gv = q.flip(2).contiguous(), k.flip(2).contiguous(), v.flip(2).contiguous()
+        calls += [
+            ("attention", lambda out=None: dm.diagmm_banded_attention(
+                q, k, v, w, wu, dil, 0.125, out=out), (b, n, h, d), q.dtype),
+            ("attention_global", lambda out=None: dm.diagmm_banded_attention_global(
+                q, k, v, glob, w, wu, dil, 0.125, out=out, global_qkv=(gq, gk, gv)),
+             (b, n, h, d), q.dtype),
+            ("attention_global_noalloc", lambda out=None: dm.diagmm_banded_attention_global_noalloc(
+                q, k, v, glob, w, wu, dil, 0.125, out=out, global_qkv=(gq, gk, gv)),
+             (b, n, h, d), q.dtype),
+        ]
+    return calls
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_newer_calls_write_nothing_outside_outputs(shape):
+    for name, fn, oshape, odt in _newer_calls(shape, 10):
+        print(f"guard check: {name} {shape}", flush=True)
+        buf, out, ref, g, ne = _guarded(oshape, odt)
+        fn(out=out)
+        torch.cuda.synchronize()
+        _guards_intact(buf, ref, g, ne)
+        assert torch.isfinite(out.float()).all(), f"{name}: an output element was not written"
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_newer_calls_bitwise_deterministic_reruns(shape):
+    for name, fn, _, _ in _newer_calls(shape, 20):
+        a = fn()
+        b2 = fn()
+        torch.cuda.synchronize()
+        assert_bits_equal(a, b2, name + " rerun")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_newer_band_calls_ignore_out_of_range_slots(shape):
+    import sliding_window_attention_diagmm_amd as dm
+    b, n, h, d, w, wu, dil, dt = shape
+    p, dp, rand, mask = _band_inputs(shape, 30)
+    inr = in_range_mask(b, n, h, w, wu, dil).cuda()
+    bad = torch.tensor(float("nan"), dtype=p.dtype, device="cuda")
+    pp, dpp = torch.where(inr, p, bad), torch.where(inr, dp, bad)
+    assert_bits_equal(dm.diagmm_banded_softmax_backward(pp, dpp, w, wu, dil, 0.5),
+                      dm.diagmm_banded_softmax_backward(p, dp, w, wu, dil, 0.5), "softmax_bwd")
+    assert_bits_equal(dm.diagmm_banded_softmax(dpp, w, wu, dil, 0.5, key_mask=mask),
+                      dm.diagmm_banded_softmax(dp, w, wu, dil, 0.5, key_mask=mask),
+                      "softmax_masked")
+    assert_bits_equal(dm.diagmm_banded_dropout(pp, rand, w, wu, dil, 0.25),
+                      dm.diagmm_banded_dropout(p, rand, w, wu, dil, 0.25), "dropout")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_inplace_backward_and_dropout_match_out_of_place(shape):
+    import sliding_window_attention_diagmm_amd as dm
+    b, n, h, d, w, wu, dil, dt = shape
+    p, dp, rand, mask = _band_inputs(shape, 40)
+    ref = dm.diagmm_banded_softmax_backward(p, dp, w, wu, dil, 0.5)
+    for which in ("probs", "dprobs"):
+        pc, dpc = p.clone(), dp.clone()
+        tgt = pc if which == "probs" else dpc
+        got = dm.diagmm_banded_softmax_backward(pc, dpc, w, wu, dil, 0.5, out=tgt)
+        assert got.data_ptr() == tgt.data_ptr()
+        assert_bits_equal(got, ref, f"softmax_bwd in place over {which}")
+    ref = dm.diagmm_banded_dropout(p, rand, w, wu, dil, 0.25)
+    pc = p.clone()
+    got = dm.diagmm_banded_dropout(pc, rand, w, wu, dil, 0.25, out=pc)
+    assert got.data_ptr() == pc.data_ptr()
+    assert_bits_equal(got, ref, "dropout in place")

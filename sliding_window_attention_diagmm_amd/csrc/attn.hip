@@ -78,6 +78,9 @@ template <> struct Mfma<BF16> {
 constexpr int kRows = 64;                   // query rows per workgroup, 16 per wave
 constexpr int kThreads = kRows / 16 * 64;
 constexpr int kKeys = 64;                   // keys per LDS block
+// Workgroups per CU the register allocation must allow: 4 (4 waves per SIMD, at most 128
+// registers a lane) for d <= 64, where that needs no spills; d = 128 keeps the default.
+__host__ __device__ constexpr int attn_min_groups(int d) { return d <= 64 ? 4 : 1; }
 constexpr int kChunks = kKeys / 32;         // 32-key chunks per block
 constexpr int64_t kMaxGlobalN = int64_t(1) << 16;   // the LDS global set: 2 n bits <= 16 KB
 constexpr int kMaxSplit = 32;               // key ranges per block of global rows, at most
@@ -510,7 +513,7 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
 }
 
 template <class In, int D>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, attn_min_groups(D))
 attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __restrict__ k,
                 const typename In::T* __restrict__ v, typename In::T* __restrict__ out,
                 AttnArgs a) {
@@ -525,7 +528,7 @@ attn_fwd_kernel(const typename In::T* __restrict__ q, const typename In::T* __re
 // The global-row units (rows_groups workgroups, the padding ones idle), then the band
 // workgroups with the global keys.  Dynamic LDS: the global set (2 ceil(n / 32) words).
 template <class In, int D>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, attn_min_groups(D))
 attn_global_kernel(const typename In::T* __restrict__ q, const typename In::T* __restrict__ k,
                    const typename In::T* __restrict__ v, typename In::T* __restrict__ out,
                    GlobalIn<typename In::T> gi, AttnArgs a) {

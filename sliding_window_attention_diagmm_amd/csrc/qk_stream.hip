@@ -27,10 +27,15 @@
 // element, for the row's own slots only, at the end of the range.  Keys outside the
 // sequence take the padding constant; values are rounded to nearest even.
 //
-// Keys.  Four loader waves fetch the range's key window in chunks of 64 keys, up to four
-// chunks in flight, and count each chunk written into LDS in a per-chunk counter.  A
-// compute wave starts a step as soon as the counter of the step's last chunk is full: no
-// barrier, no wave waits for another compute wave, and compute waves only store while
+// Keys.  Four loader waves stream the range's key window through a ring of 1024 key
+// rows (16 chunks of 64 keys, plus a copy of the chunk in ring slot 0 past slot 15, so
+// that a step's 128 rows are always contiguous), up to four chunks in flight.  Each ring
+// slot counts the loader waves that have written their part into it (four per chunk), and
+// each compute wave, where the window is longer than the ring, the steps it has finished;
+// a compute wave starts step j when slot (j + 1) mod 16 has counted chunk j + 1 in full,
+// and a loader wave writes chunk c >= 16 only once every compute wave has finished step
+// c - 16, the last to read the chunk c replaces (a window of up to 16 chunks never waits).
+// No barrier inside a range; the waits are bounded.  Compute waves only store while
 // loader waves only load (a wave's vector memory counter covers its loads and stores
 // alike, in issue order, so mixing them would make loads wait behind stores).
 #include <type_traits>
@@ -77,19 +82,21 @@ constexpr int kClassRows = 26;                   // rows of one class in a range
 constexpr int kMaxRange = 8 * kClassRows;        // 208 class rows per range
 constexpr int kStep = 64;                        // key columns per step = keys per chunk
 constexpr int kPartRows = 32;                   // rows t of a class: two query sets of 16
-constexpr int kWinChunks = 14;                   // key chunks the LDS window holds
+constexpr int kRingChunks = 16;                  // key chunks the LDS ring holds
+constexpr int kRingRows = kRingChunks * kStep;   // 1024 key rows (+ 64 mirrored)
+constexpr uint32_t kAllDone = 1u << 30;          // a compute wave's count once it is done
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kBufWord3 = 0x00020000;            // raw 32-bit buffer access (gfx9 word 3)
 constexpr int kBufDrop = static_cast<int>(0x80000000u);   // offset past every range
 
-// LDS: the key window (kWinChunks chunks of 64 rows), the compute waves' head and tail
-// pieces, and one readiness counter per chunk.
-__host__ __device__ constexpr int win_bytes(int d) { return kWinChunks * kStep * d * 2; }
+// LDS: the key ring, the compute waves' head and tail pieces, and the progress counters
+// (one per ring slot, one per compute wave).
+__host__ __device__ constexpr int win_bytes(int d) { return (kRingRows + kStep) * d * 2; }
 // A row's head and tail pieces (shared with the neighbouring band rows in HBM) are kept
 // aside during the sweep and written element by element at the end of the range.
 constexpr int kPartWave = kPartRows * 2 * 16;
 __host__ __device__ constexpr int lds_bytes(int d) {
-    return win_bytes(d) + kComputeWaves * kPartWave + kWinChunks * 4;
+    return win_bytes(d) + kComputeWaves * kPartWave + (kRingChunks + kComputeWaves) * 4;
 }
 static_assert(lds_bytes(64) <= kLdsBytes, "LDS budget");
 
@@ -129,6 +136,7 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
     unsigned char* const win = lds;
     unsigned char* const part_all = lds + win_bytes(D);
     uint32_t* const ready = reinterpret_cast<uint32_t*>(part_all + kComputeWaves * kPartWave);
+    uint32_t* const done = ready + kRingChunks;
 
     // Every argument is read here, before the first branch, so that the argument block
     // arrives in one round trip rather than one per use site.
@@ -150,8 +158,23 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
     const uint32_t rbeg = rank * rq + (rank < rrem ? rank : rrem);
     const uint32_t rend = rbeg + rq + (rank < rrem ? 1u : 0u);
 
-    if (tid < kWinChunks) ready[tid] = 0u;
+    if (tid < kRingChunks + kComputeWaves) ready[tid] = 0u;
     __syncthreads();
+    // Bounded waits on the progress counters: a wait that never ends gives up after ~2^22
+    // polls rather than hang.
+    auto wait_min = [&](const uint32_t* cnt, int m, uint32_t need) {
+        for (int it = 0; it < (1 << 22); ++it) {
+            uint32_t lo = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            for (int i = 1; i < m; ++i) {
+                const uint32_t v =
+                    __hip_atomic_load(cnt + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                lo = v < lo ? v : lo;
+            }
+            if (lo >= need) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+    };
 
     for (uint32_t rg = rbeg; rg < rend; ++rg) {
         // Range rg: strip sigma = rg / g (batch, head, class), part j of g.
@@ -173,16 +196,18 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
         const int nr_max = L > 0 ? (L + 7) / 8 : 0;
         // Steps: every class sweeps from at most 7 columns before its first row to the end
         // of its last row; the widest class (class 0) bounds them all.  Step j reads key
-        // chunks j and j + 1 (window rows 64 j .. 64 j + 127, i.e. keys U0 - 8 + row).
+        // chunks j and j + 1 (window rows 64 j .. 64 j + 127, i.e. keys U0 - 8 + row), which
+        // sit in ring rows 64 (j mod 16) .. + 127 (past row 1023: the copy of slot 0).
         const int S = nr_max > 0 ? (8 * (nr_max - 1) + K + 7 + kStep - 1) / kStep : 0;
         if (S == 0) continue;
         const int C = S + 1;                                 // chunks of the window
 
         if (!computes) {
             // ---------------------------------------------------------------- loaders
-            // Chunk c = keys U0 - 8 + 64 c .. + 63 into window rows 64 c ..; when a loader
-            // wave has written its part of chunk c it counts itself in ready[c].  Chunks go
-            // in order, so ready[c] = kLoadWaves means chunks 0 .. c are all in.
+            // Chunk c = keys U0 - 8 + 64 c .. + 63 into ring rows 64 (c mod 16) ..; a loader
+            // wave writes its part of chunk c once every compute wave has finished step
+            // c - 16 (chunks past the ring's first fill only), then counts it.  Chunks go in
+            // order.
             const int lt = tid - kComputeWaves * 64;
             const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<typename In::T*>(ks), 0, n_r * qk_bytes, kBufWord3);
@@ -206,14 +231,22 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
             };
             auto put = [&](int chunk, const u32x4* buf) {
                 if (chunk >= C) return;
-                unsigned char* const base = win + chunk * kStep * kRowBytes;
+                if (chunk >= kRingChunks)
+                    wait_min(done, kComputeWaves, static_cast<uint32_t>(chunk - kRingChunks + 1));
+                unsigned char* const base = win + (chunk & (kRingChunks - 1)) * kStep * kRowBytes;
 #pragma unroll
                 for (int p = 0; p < kPer; ++p) *reinterpret_cast<u32x4*>(base + poff[p]) = buf[p];
+                if (chunk >= kRingChunks && (chunk & (kRingChunks - 1)) == 0) {
+                    // slot 0's copy past slot 15, read by the steps that cross the ring's end
+#pragma unroll
+                    for (int p = 0; p < kPer; ++p)
+                        *reinterpret_cast<u32x4*>(win + kRingRows * kRowBytes + poff[p]) = buf[p];
+                }
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the writes are done
                 if (lane == 0)
-                    __hip_atomic_fetch_add(ready + chunk, 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+                    __hip_atomic_fetch_add(ready + (chunk & (kRingChunks - 1)), 1u,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             };
             // Register sets in rotation (chunk c in set c mod kSets).  Chunks 0 and 1 are
             // requested alone, so that they are not queued behind the rest of the window at
@@ -265,8 +298,9 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
             // Lane group grp holds, after pairing, columns 8 sj .. 8 sj + 7 of a block pair.
             const int sj = ((grp & 1) << 1) | (grp >> 1);
             const uint32_t padw = (a.pad & 0xffffu) | (a.pad << 16);
-            // A operands: block rows start at window rows = xs + 8 (mod 8), so the swizzle of
-            // this lane's row is fixed; per block only the window row of its first key moves.
+            // A operands: this lane reads ring row r0 + col of a block whose first row is
+            // r0 = xs + 8 (mod 8), so the swizzle of its row is fixed (row mod 8) and only
+            // the block's first row moves.
             int aoff[kDC];
 #pragma unroll
             for (int dc = 0; dc < kDC; ++dc)
@@ -320,11 +354,12 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
             // One step: the four blocks at columns x0 .. x0 + 63: window reads, the MFMAs of
             // both query sets (the second set's rows past the class are computed and
             // dropped), rounding, stores.
-            auto sweep = [&](auto edge, int x0) {
+            // xr: the ring row of column x0's key minus 8 (x0 moved into the step's slot).
+            auto sweep = [&](auto edge, int x0, int xr) {
                 V kf[4][kDC];
 #pragma unroll
                 for (int bk = 0; bk < 4; ++bk) {
-                    const int r0 = x0 + 8 + 16 * bk;
+                    const int r0 = xr + 8 + 16 * bk;
 #pragma unroll
                     for (int dc = 0; dc < kDC; ++dc)
                         kf[bk][dc] = *reinterpret_cast<const V*>(win + r0 * kRowBytes + aoff[dc]);
@@ -394,27 +429,28 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
                 }
             };
 
-            // Steps run as soon as their keys are in: wait for chunk j + 1 (bounded: a wait
-            // that never ends gives up after ~2^22 polls rather than hang), then sweep.  No
-            // wave waits for another compute wave.
+            // Steps run as soon as their keys are in (every loader wave past chunk j + 1);
+            // after the step the wave counts it (its window reads are done: the MFMAs used
+            // them).  No wave waits for another compute wave.
             for (int j = 0; j < J; ++j) {
-                const uint32_t* f = ready + (j + 1);
-                for (int it = 0; it < (1 << 22); ++it) {
-                    if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >=
-                        static_cast<uint32_t>(kLoadWaves))
-                        break;
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                asm volatile("" ::: "memory");
+                wait_min(ready + ((j + 1) & (kRingChunks - 1)), 1,
+                         static_cast<uint32_t>(kLoadWaves * ((j + 1) / kRingChunks + 1)));
                 const int x0 = xs + kStep * j;
+                const int xr = xs + kStep * (j & (kRingChunks - 1));
                 const int u = U0 + x0;                       // keys of the step: u .. u + 63
-                if (u >= 0 && u + kStep <= n_r) sweep(std::false_type{}, x0);
-                else sweep(std::true_type{}, x0);
+                if (u >= 0 && u + kStep <= n_r) sweep(std::false_type{}, x0, xr);
+                else sweep(std::true_type{}, x0, xr);
+                if (lane == 0 && C > kRingChunks)
+                    __hip_atomic_store(done + c, static_cast<uint32_t>(j + 1), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
             }
+            if (lane == 0 && C > kRingChunks)
+                __hip_atomic_store(done + c, kAllDone, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
             write_edges();
         }
         __syncthreads();                                     // the window is free again
-        if (tid < kWinChunks) ready[tid] = 0u;
+        if (tid < kRingChunks + kComputeWaves) ready[tid] = 0u;
         __syncthreads();
     }
 }
@@ -442,16 +478,10 @@ QkStreamPlan plan_qk_stream(const Problem& p, int in_dt, int out_dt) {
     const int64_t res = p.s < p.n ? p.s : (p.n > 0 ? p.n : 1);
     const int64_t strips = p.b * p.h * res;
     const int64_t longest = ceil_div(p.n, p.s);
-    if (strips < 1 || longest < 1 || p.K > kWinChunks * kStep || p.K < 8) return sp;
-    // The window of a range (its rows plus the K - 1 keys around them, in 64-key chunks,
-    // plus one) must fit kWinChunks: at most max_rows rows per range.
-    const int64_t max_nr = (kWinChunks - 1) * kStep - p.K - 7;   // 8 (nr - 1) <= this
-    if (max_nr < 0) return sp;
-    int64_t max_rows = 8 * (max_nr / 8 + 1);
-    max_rows = max_rows < kMaxRange ? max_rows : kMaxRange;
+    if (strips < 1 || longest < 1 || p.K < 8) return sp;
     const int64_t cus = device_cus();
     int64_t g = cus / strips;
-    const int64_t need = ceil_div(longest, max_rows);
+    const int64_t need = ceil_div(longest, kMaxRange);
     g = g > need ? g : need;
     g = g < longest ? g : longest;                  // no empty ranges
     sp.g = g;
@@ -465,15 +495,12 @@ QkStreamPlan plan_qk_stream(const Problem& p, int in_dt, int out_dt) {
     sp.lds_bytes = lds_bytes(static_cast<int>(p.d));
     const int64_t row_elems = p.s * p.h * p.K;
     const int64_t span = ((sp.rows_per_range - 1) * row_elems + p.K) * 2;
-    const int64_t nr = ceil_div(sp.rows_per_range, 8);
-    const int64_t steps = ceil_div(8 * (nr - 1) + p.K + 7, kStep);
     // 32-bit arithmetic: band offsets within a range (below the drop offset 2^31), key
-    // offsets within a strip, positions and ranges
+    // offsets within a strip, columns of a sweep, positions and ranges
     const int64_t strip_bytes = (ceil_div(p.n, p.s) + 1) * p.s * p.h * p.d * 2;
-    sp.ok = sp.lds_bytes <= kLdsBytes && sp.rows_per_range <= max_rows &&
-            steps + 1 <= kWinChunks && sp.ranges < (int64_t(1) << 31) &&
-            span < (int64_t(1) << 31) - 64 &&
-            p.n < (int64_t(1) << 30) && p.w < (int64_t(1) << 30) &&
+    sp.ok = sp.lds_bytes <= kLdsBytes && sp.rows_per_range <= kMaxRange &&
+            sp.ranges < (int64_t(1) << 31) && span < (int64_t(1) << 31) - 64 &&
+            p.n < (int64_t(1) << 30) && p.w < (int64_t(1) << 30) && p.K < (int64_t(1) << 28) &&
             strip_bytes < (int64_t(1) << 31) && p.b * p.h < (int64_t(1) << 31);
     return sp;
 }

@@ -79,6 +79,8 @@ def op_costs(dil):
         "softmax_bwd": {"bytes": 2 * cnt * E + band, "flops": 0},
         # the softmax with the per-key mask: the softmax's bytes and the [b, n] f32 mask
         "softmax_masked": {"bytes": cnt * E + band + B * N * 4, "flops": 0},
+        # the plain softmax out of place (the masked call's setting, without the mask)
+        "softmax_oop": {"bytes": cnt * E + band, "flops": 0},
         # dropout: P and its float32 random numbers on the in-range slots, the band written
         "dropout": {"bytes": cnt * (E + 4) + band, "flops": 0},
         # attention in one pass: Q, K, V read and the output written; both products' flops
@@ -477,7 +479,8 @@ def main():
         t["rand"] = torch.rand(t["dP"].shape, generator=gen, device=dev, dtype=torch.float32)
     glob = torch.tensor([[0] + [(j * N) // NG + 7 for j in range(1, NG - 1)] + [N - 1]],
                         dtype=torch.int32, device=dev).expand(B, NG).contiguous()
-    for op in ("softmax_bwd", "softmax_masked", "dropout", "attention", "attention_global"):
+    for op in ("softmax_bwd", "softmax_masked", "softmax_oop", "dropout", "attention",
+               "attention_global"):
         for dil in DILATIONS:
             def run(t):
                 if op == "softmax_bwd":
@@ -486,6 +489,9 @@ def main():
                 elif op == "softmax_masked":
                     dm.diagmm_banded_softmax(t[f"S{dil}"], W, WU, dil, SCALE, out=t["dS"],
                                              key_mask=key_mask)
+                elif op == "softmax_oop":
+                    # the plain softmax on the masked call's inputs and output, for the ratio
+                    dm.diagmm_banded_softmax(t[f"S{dil}"], W, WU, dil, SCALE, out=t["dS"])
                 elif op == "dropout":
                     dm.diagmm_banded_dropout(t[f"S{dil}"], t["rand"], W, WU, dil, 0.1,
                                              out=t["dS"])
@@ -500,7 +506,7 @@ def main():
                 run(sets[i % len(sets)])
             torch.cuda.synchronize()
             per_call = 2 if op == "attention_global" else 1   # launches per call
-            tag = "attention" if op == "attention_global" else op
+            tag = {"attention_global": "attention", "softmax_oop": "softmax"}.get(op, op)
             phase("extra")
             recs = timed_launches(dm, torch, lambda i: run(sets[i % len(sets)]), args.steps,
                                   tag, per_call)

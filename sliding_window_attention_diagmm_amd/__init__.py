@@ -51,7 +51,7 @@ class _Plan(ctypes.Structure):
                 ("slots_per_tile", ctypes.c_int64), ("tiles", ctypes.c_int64),
                 ("workgroups", ctypes.c_int64), ("threads", ctypes.c_int64),
                 ("lds_bytes", ctypes.c_int64), ("residues", ctypes.c_int64),
-                ("strip_workgroups", ctypes.c_int64)]
+                ("strip_workgroups", ctypes.c_int64), ("interleaved", ctypes.c_int64)]
 
 
 _lib = None
@@ -405,7 +405,8 @@ def diagmm_plan(mode, b, n, h, d, w, w_upper=None, dilation=0, in_dtype=torch.fl
     return {"kernel": pl.kernel.decode(), "rows_per_tile": pl.rows_per_tile,
             "slots_per_tile": pl.slots_per_tile, "tiles": pl.tiles,
             "workgroups": pl.workgroups, "threads": pl.threads, "lds_bytes": pl.lds_bytes,
-            "residues": pl.residues, "strip_workgroups": pl.strip_workgroups}
+            "residues": pl.residues, "strip_workgroups": pl.strip_workgroups,
+            "interleaved": pl.interleaved}
 
 
 def diagmm_timing_begin(capacity: int) -> None:

@@ -590,6 +590,7 @@ diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d
     out->lds_bytes = plan.lds_bytes;
     out->residues = plan.residues;
     out->strip_workgroups = plan.strip_wgs;
+    out->interleaved = plan.interleaved;
     return ok();
 }
 

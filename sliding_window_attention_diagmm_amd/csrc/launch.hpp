@@ -27,6 +27,8 @@ hipError_t launch_softmax_wave(const void* scores, void* probs, const Problem& p
 
 // DIAGMM_KERNEL=simple: the general kernels only (debugging and comparison switch).
 bool force_simple();
+// DIAGMM_PVT_ORDER=interleaved / contiguous: pvT's tile order forced (1 / 2), else 0.
+int pvt_order_forced();
 
 // Banded softmax backward (one dtype for probs, dprobs and dscores): the group / wave
 // kernel when `fast` (softmax_bwd_fast), else one workgroup per row.
@@ -114,6 +116,7 @@ struct PvTilePlan {
     int64_t lds_bytes = 0;
     int64_t workgroups = 0;
     int64_t strip_wgs = 0;  // workgroups per strip with the strip split, 0 = flat split
+    bool interleave = false;  // pvT: units dealt round-robin over each XCD's workgroups
     bool ok = false;
 };
 

@@ -1,4 +1,4 @@
-// diagmm_pvT on MFMA with persistent, sliding workgroups.
+// diagmm_pvT on MFMA with persistent workgroups.
 //
 //   out[j][c] = sum over (i, k) with i + k - w = j of G[i][k] * X[i][c]
 //
@@ -32,6 +32,18 @@
 // the channel blocks, and for every 32-row chunk of the window its columns reach issues
 // one v_mfma_f32_16x16x32_{f16,bf16} per channel block.  Lane (j = lane % 16,
 // g = lane / 16) accumulates out[j0 + 16 jb + j][16 cb + 4 g .. +3].
+//
+// Order.  Neighbouring tiles of a residue class read the same 128-byte lines of each band
+// row: the parallelogram of a tile starts and ends inside a line of every row it crosses,
+// and the tile next to it reads the rest of that line.  On the flat split the tiles of
+// each XCD can therefore be dealt round-robin over its workgroups (tiles lo + j + m nwg / 8
+// for its j-th workgroup), so neighbouring tiles run at the same time and the lines they
+// share are fetched from HBM once while they sit in the XCD's L2; a workgroup's
+// consecutive tiles are then apart, and each tile loads its whole X window.  That is done
+// where a round of tiles over the XCD reads more band lines than its L2 holds (the shared
+// lines would be gone by the workgroup's next tile).  Otherwise, and on the strip split,
+// a workgroup keeps a contiguous run of tiles, its window sliding by 64 rows from one to
+// the next.
 //
 // Pipelining.  The next tile's band pieces (and, when the window slides, its 64 new X
 // rows) load into registers while the current tile computes.
@@ -84,6 +96,7 @@ struct PvTArgs {
     int64_t band_elems;
     TileDecode dc;         // whole tiles (units) over workgroups, unit -> coordinates
     Div32 chunks;          // item -> (unit, chunk)
+    int32_t interleave;    // units interleaved over each XCD's workgroups (flat split)
 };
 
 struct Item {
@@ -123,12 +136,13 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
     const int jb = wave >> 1;                               // this wave's column block
     const int cb0 = (wave & 1) * kCBPerWave;                // first channel block
 
-    uint32_t item, iend;
+    // Items: the chunks of this workgroup's units, the units taken as a sequence
+    // ufirst + ustride m (interleaved over the XCD's workgroups on the flat split).
+    uint32_t item = 0, iend, ufirst, ustride;
     {
-        uint32_t ub, ue;
-        unit_range(a.dc, xcd_rank(blockIdx.x, a.nwg), &ub, &ue);
-        item = ub * a.chunks.d;
-        iend = ue * a.chunks.d;
+        uint32_t cnt;
+        unit_seq(a.dc, blockIdx.x, a.nwg, a.interleave != 0, &ufirst, &cnt, &ustride);
+        iend = cnt * a.chunks.d;
     }
     // Zero the X ring once: window rows past the current window are read (and multiplied
     // by exact zeros), so no slot may ever hold a non-finite pattern.
@@ -136,8 +150,9 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
         reinterpret_cast<u32x4*>(xr_)[q] = u32x4{0u, 0u, 0u, 0u};
 
     auto describe = [&](uint32_t id, Item* it) {
-        const uint32_t unit = div32(a.chunks, id);
-        const int kc = static_cast<int>(id - unit * a.chunks.d);
+        const uint32_t m = div32(a.chunks, id);
+        const int kc = static_cast<int>(id - m * a.chunks.d);
+        const uint32_t unit = ufirst + m * ustride;
         TileId t = decode_fast(a.dc, unit);
         t.kb = kc;
         it->t = t;
@@ -467,7 +482,7 @@ hipError_t launch_typed(const void* band, const void* x, void* out, bool out_f32
     PvTArgs a{p.n, p.h, p.K, p.w, p.s, tp.grid, static_cast<int32_t>(l.ring),
               static_cast<int32_t>(l.ring_off), static_cast<uint32_t>(tp.workgroups),
               p.rows() * p.h * p.K, unit_decode(tp, p),
-              make_div32(static_cast<uint32_t>(tp.grid.nkb))};
+              make_div32(static_cast<uint32_t>(tp.grid.nkb)), tp.interleave ? 1 : 0};
     auto kern = pvt_mfma_kernel<In, D>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -508,6 +523,16 @@ PvTilePlan plan_pvt_mfma(const Problem& p) {
         tp.strip_wgs = pick_strip_split(tp.grid.tiles / tp.grid.nkb / per_strip, per_strip,
                                         kRows, ceil_div(p.n, p.s) - (per_strip - 1) * kRows,
                                         tp.workgroups);
+    // Tile order on the flat split: a workgroup's next tile shares lines with its current
+    // one, but by then every workgroup of the XCD has read a whole tile's band lines
+    // (2 lines of each of its 64 + KC - 1 window rows, every chunk of the tile).  Where that
+    // round exceeds the XCD's L2 (4 MB), the shared lines are gone before they are read
+    // again: deal the tiles round-robin instead (each tile then loads its whole X window).
+    const int64_t round_bytes = (tp.workgroups / kXcds) * tp.grid.nkb *
+                                (kRows + tp.grid.kb - 1) * 256;
+    const int forced = pvt_order_forced();
+    tp.interleave = tp.strip_wgs == 0 && tp.workgroups % kXcds == 0 &&
+                    (forced ? forced == 1 : round_bytes > (int64_t(4) << 20));
     tp.ok = tp.grid.tiles <= kMaxTiles && ceil_div(p.n, p.s) < (int64_t(1) << 30) &&
             p.K < (int64_t(1) << 30) && p.w < (int64_t(1) << 30) && l.bytes <= kPvLdsBytes &&
             tp.workgroups >= 1 && (p.d == 32 || p.d == 64 || p.d == 128);

@@ -21,6 +21,15 @@ static bool qk_tiles_forced() {
     return e && std::strcmp(e, "tiles") == 0;
 }
 
+// DIAGMM_PVT_ORDER=interleaved / contiguous overrides pvT's choice of tile order on the
+// flat split (a testing and comparison switch): 1 and 2, else 0.
+int pvt_order_forced() {
+    const char* e = std::getenv("DIAGMM_PVT_ORDER");
+    if (!e) return 0;
+    if (std::strcmp(e, "interleaved") == 0) return 1;
+    return std::strcmp(e, "contiguous") == 0 ? 2 : 0;
+}
+
 namespace {
 
 Plan simple_plan(const Problem& p, int64_t cols, const char* name) {
@@ -115,6 +124,7 @@ Plan plan_pvT(const Problem& p, int in_dt, int out_dt) {
     pl.lds_bytes = tp.lds_bytes;
     pl.residues = tp.grid.res;
     pl.strip_wgs = tp.strip_wgs;
+    pl.interleaved = tp.interleave ? 1 : 0;
     return pl;
 }
 

@@ -220,4 +220,30 @@ __host__ __device__ inline void unit_range(const TileDecode& dc, uint32_t rank,
     *end = *begin + dc.unit_base + (rank < dc.unit_rem ? 1u : 0u);
 }
 
+// The units of workgroup wg as an arithmetic sequence first, first + stride, ... (count
+// terms).  Interleaved (flat split, nwg a multiple of 8 only): XCD x = wg mod 8 owns the
+// units [U x / 8, U (x + 1) / 8) of the U in all, and its j-th workgroup (j = wg / 8) takes
+// every (nwg / 8)-th of them from the j-th on, so that at any moment the XCD's workgroups
+// hold neighbouring units and read the cache lines those share while they are in its L2.
+// Otherwise the contiguous range of unit_range for the workgroup's XCD rank.
+__host__ __device__ inline void unit_seq(const TileDecode& dc, uint32_t wg, uint32_t nwg,
+                                         bool interleave, uint32_t* first, uint32_t* count,
+                                         uint32_t* stride) {
+    if (interleave && dc.strip_wgs == 0 && nwg % kXcds == 0) {
+        const uint64_t units = static_cast<uint64_t>(dc.unit_base) * nwg + dc.unit_rem;
+        const uint32_t x = wg % kXcds, j = wg / kXcds, per = nwg / kXcds;
+        const uint32_t lo = static_cast<uint32_t>(units * x / kXcds);
+        const uint32_t hi = static_cast<uint32_t>(units * (x + 1) / kXcds);
+        *first = lo + j;
+        *stride = per;
+        *count = lo + j < hi ? (hi - lo - j + per - 1) / per : 0u;
+        return;
+    }
+    uint32_t b, e;
+    unit_range(dc, xcd_rank(wg, nwg), &b, &e);
+    *first = b;
+    *count = e - b;
+    *stride = 1;
+}
+
 }  // namespace diagmm

@@ -41,7 +41,7 @@ int main() {
         for (uint32_t n : ns)
             if (n <= nmax && check_div(d, n)) return 1;
     }
-    // decode_fast / class_len_fast / unit_range against the reference forms
+    // decode_fast / class_len_fast / unit_range / unit_seq against the reference forms
     struct Case { int64_t b, n, h, K, s, rows, slots, nwg; };
     const Case cases[] = {{1, 4096, 12, 513, 1, 64, 513, 256}, {1, 4096, 12, 513, 3, 64, 513, 256},
                           {2, 1000, 3, 97, 7, 32, 40, 37},   {3, 5, 2, 9, 9, 64, 513, 8},
@@ -76,6 +76,36 @@ int main() {
         if (expect != g.tiles) {
             std::printf("unit_range covers %u of %lld\n", expect, (long long)g.tiles);
             return 1;
+        }
+        // unit_seq, interleaved and contiguous: every unit exactly once, each XCD's units
+        // a contiguous range shared out to +-1 among its workgroups
+        for (bool il : {true, false}) {
+            std::vector<int> seen(static_cast<size_t>(g.tiles), 0);
+            for (uint32_t wg = 0; wg < static_cast<uint32_t>(nwg); ++wg) {
+                uint32_t f, cnt, st;
+                unit_seq(dc, wg, static_cast<uint32_t>(nwg), il, &f, &cnt, &st);
+                for (uint32_t m = 0; m < cnt; ++m) {
+                    const uint64_t u = f + uint64_t(m) * st;
+                    if (u >= static_cast<uint64_t>(g.tiles) || seen[u]++) {
+                        std::printf("unit_seq bad at wg %u (interleave %d)\n", wg, int(il));
+                        return 1;
+                    }
+                }
+                if (il && nwg % kXcds == 0) {
+                    const uint64_t lo = uint64_t(g.tiles) * (wg % kXcds) / kXcds;
+                    const uint64_t hi = uint64_t(g.tiles) * (wg % kXcds + 1) / kXcds;
+                    const uint64_t per = nwg / kXcds, span = hi - lo;
+                    if (cnt < span / per || cnt > span / per + 1 || (cnt && (f < lo || f >= hi))) {
+                        std::printf("unit_seq unbalanced at wg %u\n", wg);
+                        return 1;
+                    }
+                }
+            }
+            for (int64_t t = 0; t < g.tiles; ++t)
+                if (seen[t] != 1) {
+                    std::printf("unit_seq misses unit %lld (interleave %d)\n", (long long)t, int(il));
+                    return 1;
+                }
         }
     }
     std::printf("ok\n");

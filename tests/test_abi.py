@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dm.diagmm_abi_version() == 8
+    assert dm.diagmm_abi_version() == 9
     seen = set()
     for st in range(7):
         s = lib.diagmm_status_string(st).decode()

@@ -297,10 +297,11 @@ typedef struct {
                                  split strip by strip; 0 when they are balanced over all
                                  workgroups at once.  qk: the row ranges each strip is cut
                                  into (a workgroup takes one range, or a run of them) */
-    int64_t interleaved;    /* pvT: 1 when each XCD's tiles are dealt round-robin over its
-                               workgroups (neighbouring tiles at the same time, sharing the
-                               band's cache lines in L2), 0 when a workgroup takes a
-                               contiguous run of tiles; 0 for the other modes */
+    int64_t interleaved;    /* pv, pvT: 1 when each XCD's tiles are dealt round-robin over
+                               its workgroups (neighbouring tiles run at the same time and
+                               share the cache lines they both read in L2), 0 when a
+                               workgroup takes a contiguous run of tiles; 0 for the other
+                               modes */
 } diagmm_plan_t;
 
 diagmm_status_t diagmm_plan(int mode, int64_t b, int64_t n, int64_t h, int64_t d, int64_t w,

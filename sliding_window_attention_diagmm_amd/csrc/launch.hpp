@@ -27,8 +27,9 @@ hipError_t launch_softmax_wave(const void* scores, void* probs, const Problem& p
 
 // DIAGMM_KERNEL=simple: the general kernels only (debugging and comparison switch).
 bool force_simple();
-// DIAGMM_PVT_ORDER=interleaved / contiguous: pvT's tile order forced (1 / 2), else 0.
-int pvt_order_forced();
+// DIAGMM_TILE_ORDER=interleaved / contiguous: the tile order of pv and pvT forced (1 / 2),
+// else 0.
+int tile_order_forced();
 
 // Banded softmax backward (one dtype for probs, dprobs and dscores): the group / wave
 // kernel when `fast` (softmax_bwd_fast), else one workgroup per row.
@@ -116,7 +117,7 @@ struct PvTilePlan {
     int64_t lds_bytes = 0;
     int64_t workgroups = 0;
     int64_t strip_wgs = 0;  // workgroups per strip with the strip split, 0 = flat split
-    bool interleave = false;  // pvT: units dealt round-robin over each XCD's workgroups
+    bool interleave = false;  // units dealt round-robin over each XCD's workgroups
     bool ok = false;
 };
 

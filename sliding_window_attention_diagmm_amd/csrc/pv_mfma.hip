@@ -1,4 +1,4 @@
-// diagmm_pv on MFMA with persistent, sliding workgroups.
+// diagmm_pv on MFMA with persistent workgroups.
 //
 //   out[t][c] = sum over in-range slots k of P[t][k] * V[t + k - w][c]
 //
@@ -10,8 +10,11 @@
 // one (batch, head); when the band is wider than a slot chunk (KC slots, set by the LDS
 // budget) the tile is processed chunk by chunk with the accumulators kept in registers.
 // A chunk's slots reach the W = 64 + KC - 1 keys u0 .. u0 + W - 1 (u0 = t0 + k0 - w).
-// One 512-thread workgroup per compute unit walks a contiguous range of whole tiles, chunk
-// by chunk; single-chunk tiles that continue a strip slide the key window by 64.
+// One 512-thread workgroup per compute unit walks its whole tiles chunk by chunk: a
+// contiguous range, where single-chunk tiles that continue a strip slide the key window
+// by 64; or, for tiles of several chunks (each chunk loads its own window, and the next
+// tile's windows overlap them but for 64 keys), each XCD's tiles dealt round-robin over
+// its workgroups, so that neighbouring tiles read their windows from L2 at the same time.
 //
 // LDS.  V is kept row-major in a ring of key slots (keys outside the sequence are
 // written as zeros), each row's 16-byte pieces XOR-swizzled by slot, so new rows go in
@@ -84,6 +87,7 @@ struct PvArgs {
     int64_t band_elems;    // elements of the band tensor
     TileDecode dc;         // whole tiles (units) over workgroups, unit -> coordinates
     Div32 chunks;          // item -> (unit, chunk)
+    int32_t interleave;    // units interleaved over each XCD's workgroups (flat split)
 };
 
 // One work item = (tile, chunk); items run with the chunk fastest, so a tile's chunks
@@ -122,13 +126,14 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
     const int rb = wave >> 1;                               // this wave's query block
     const int cb0 = (wave & 1) * kCBPerWave;                // first channel block
 
-    // Whole tiles per workgroup (a tile's chunks share its accumulators), items = chunks.
-    uint32_t item, iend;
+    // Whole tiles per workgroup (a tile's chunks share its accumulators), items = chunks;
+    // the tiles are taken as a sequence ufirst + ustride m (interleaved over the XCD's
+    // workgroups on the flat split).
+    uint32_t item = 0, iend, ufirst, ustride;
     {
-        uint32_t ub, ue;
-        unit_range(a.dc, xcd_rank(blockIdx.x, a.nwg), &ub, &ue);
-        item = ub * a.chunks.d;
-        iend = ue * a.chunks.d;
+        uint32_t cnt;
+        unit_seq(a.dc, blockIdx.x, a.nwg, a.interleave != 0, &ufirst, &cnt, &ustride);
+        iend = cnt * a.chunks.d;
     }
     // Zero the V ring once: window columns past the current window are read (and
     // multiplied by exact zeros), so no slot may ever hold a non-finite pattern.
@@ -136,8 +141,9 @@ pv_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* __
         reinterpret_cast<u32x4*>(vr)[x] = u32x4{0u, 0u, 0u, 0u};
 
     auto describe = [&](uint32_t id, Item* it) {
-        const uint32_t unit = div32(a.chunks, id);
-        const int kc = static_cast<int>(id - unit * a.chunks.d);
+        const uint32_t m = div32(a.chunks, id);
+        const int kc = static_cast<int>(id - m * a.chunks.d);
+        const uint32_t unit = ufirst + m * ustride;
         TileId t = decode_fast(a.dc, unit);
         t.kb = kc;
         it->t = t;
@@ -491,7 +497,8 @@ hipError_t launch_typed(const void* band, const void* v, void* out, bool out_f32
     PvArgs a{p.n, p.h, p.K, p.w, p.s, tp.grid, static_cast<int32_t>(l.rsp),
              static_cast<int32_t>(l.ring), static_cast<int32_t>(l.ring_off),
              static_cast<uint32_t>(tp.workgroups), p.rows() * p.h * p.K,
-             unit_decode(tp, p), make_div32(static_cast<uint32_t>(tp.grid.nkb))};
+             unit_decode(tp, p), make_div32(static_cast<uint32_t>(tp.grid.nkb)),
+             tp.interleave ? 1 : 0};
     auto kern = pv_mfma_kernel<In, D>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -533,6 +540,18 @@ PvTilePlan plan_pv_mfma(const Problem& p) {
         tp.strip_wgs = pick_strip_split(tp.grid.tiles / tp.grid.nkb / per_strip, per_strip,
                                         kRows, ceil_div(p.n, p.s) - (per_strip - 1) * kRows,
                                         tp.workgroups);
+    // Tile order on the flat split.  A tile of one chunk continues the previous tile's key
+    // window (it slides by 64 rows in LDS); a tile of several chunks loads a new window
+    // per chunk, and the next tile's windows overlap them all but 64 rows.  When the
+    // XCD's workgroups read more windows in one round of tiles than its L2 (4 MB) holds,
+    // a workgroup's next tile finds them gone: deal the tiles round-robin instead, so
+    // that neighbouring tiles read their windows at the same time.
+    const int64_t round_bytes = (tp.workgroups / kXcds) * tp.grid.nkb *
+                                (kRows + tp.grid.kb - 1) * p.d * 2;
+    const int forced = tile_order_forced();
+    tp.interleave = tp.strip_wgs == 0 && tp.workgroups % kXcds == 0 &&
+                    (forced ? forced == 1
+                            : tp.grid.nkb > 1 && round_bytes > (int64_t(4) << 20));
     tp.ok = tp.grid.tiles <= kMaxTiles && ceil_div(p.n, p.s) < (int64_t(1) << 30) &&
             p.K < (int64_t(1) << 30) && l.bytes <= kPvLdsBytes && tp.workgroups >= 1 &&
             p.s * p.h * p.K < (int64_t(1) << 32) &&

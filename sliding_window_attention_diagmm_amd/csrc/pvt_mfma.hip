@@ -530,7 +530,7 @@ PvTilePlan plan_pvt_mfma(const Problem& p) {
     // again: deal the tiles round-robin instead (each tile then loads its whole X window).
     const int64_t round_bytes = (tp.workgroups / kXcds) * tp.grid.nkb *
                                 (kRows + tp.grid.kb - 1) * 256;
-    const int forced = pvt_order_forced();
+    const int forced = tile_order_forced();
     tp.interleave = tp.strip_wgs == 0 && tp.workgroups % kXcds == 0 &&
                     (forced ? forced == 1 : round_bytes > (int64_t(4) << 20));
     tp.ok = tp.grid.tiles <= kMaxTiles && ceil_div(p.n, p.s) < (int64_t(1) << 30) &&

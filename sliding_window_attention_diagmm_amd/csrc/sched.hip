@@ -21,10 +21,10 @@ static bool qk_tiles_forced() {
     return e && std::strcmp(e, "tiles") == 0;
 }
 
-// DIAGMM_PVT_ORDER=interleaved / contiguous overrides pvT's choice of tile order on the
-// flat split (a testing and comparison switch): 1 and 2, else 0.
-int pvt_order_forced() {
-    const char* e = std::getenv("DIAGMM_PVT_ORDER");
+// DIAGMM_TILE_ORDER=interleaved / contiguous overrides the choice of tile order of pv and
+// pvT on the flat split (a testing and comparison switch): 1 and 2, else 0.
+int tile_order_forced() {
+    const char* e = std::getenv("DIAGMM_TILE_ORDER");
     if (!e) return 0;
     if (std::strcmp(e, "interleaved") == 0) return 1;
     return std::strcmp(e, "contiguous") == 0 ? 2 : 0;
@@ -104,6 +104,7 @@ Plan plan_pv(const Problem& p, int in_dt, int out_dt) {
     pl.lds_bytes = tp.lds_bytes;
     pl.residues = tp.grid.res;
     pl.strip_wgs = tp.strip_wgs;
+    pl.interleaved = tp.interleave ? 1 : 0;
     return pl;
 }
 

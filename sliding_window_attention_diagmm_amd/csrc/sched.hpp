@@ -28,7 +28,7 @@ struct Plan {
     int64_t lds_bytes = 0;
     int64_t residues = 1;        // s: rows i = r (mod s) form independent problems
     int64_t strip_wgs = 0;       // workgroups per strip (strip split), 0 = flat split
-    int64_t interleaved = 0;     // pvT: tiles dealt round-robin over each XCD's workgroups
+    int64_t interleaved = 0;     // pv, pvT: tiles dealt round-robin over each XCD's workgroups
 };
 
 Plan plan_qk(const Problem& p, int in_dt, int out_dt);

@@ -144,13 +144,13 @@ def test_qk_stream_plan_balances_row_ranges(monkeypatch):
     assert pl["kernel"] == "qk_stream" and pl["slots_per_tile"] == 8193, pl
 
 
-def test_pvt_tile_order(monkeypatch):
+def test_tile_order(monkeypatch):
     """pvT deals each XCD's tiles round-robin over its workgroups (neighbouring tiles at the
     same time) where a round of contiguous runs would read more band lines than an XCD's
     4 MB L2 holds before a workgroup's next tile reuses them: at n = 4096, h = 12, 513
     slots (32 workgroups x 576 window rows x 256 bytes = 4.7 MB) and at 8193 slots (16
-    chunks a tile); not at 257 slots (320 rows, 2.6 MB), nor on the strip split, nor for
-    pv."""
+    chunks a tile); not at 257 slots (320 rows, 2.6 MB), nor on the strip split.  pv does
+    the same for tiles of several chunks only (one-chunk tiles slide their key window)."""
     monkeypatch.delenv("DIAGMM_MAX_WORKGROUPS", raising=False)
     pl = dm.diagmm_plan("pvT", 1, 4096, 12, 64, 256, 256, 0, torch.float16)
     if pl["workgroups"] == 256:
@@ -162,14 +162,18 @@ def test_pvt_tile_order(monkeypatch):
     pl3 = dm.diagmm_plan("pvT", 1, 4096, 12, 64, 256, 256, 3, torch.float16)
     if pl3["strip_workgroups"]:
         assert pl3["interleaved"] == 0, pl3
+    # pv: one-chunk tiles slide their key window, several-chunk tiles are interleaved
     assert dm.diagmm_plan("pv", 1, 4096, 12, 64, 256, 256, 0, torch.float16)["interleaved"] == 0
+    if pl["workgroups"] == 256:
+        assert dm.diagmm_plan("pv", 1, 32768, 12, 64, 4096, 4096, 0,
+                              torch.float16)["interleaved"] == 1
     # a grid that is not a multiple of the 8 XCDs keeps contiguous runs
     monkeypatch.setenv("DIAGMM_MAX_WORKGROUPS", "44")
     assert dm.diagmm_plan("pvT", 1, 4096, 12, 64, 256, 256, 0, torch.float16)["interleaved"] == 0
 
 
 # (b, n, h, d, w, w_upper, dilation, in, out, workgroups): flat splits whose workgroups are
-# a multiple of 8, so pvT can run with each XCD's tiles dealt round-robin
+# a multiple of 8, so pv and pvT can run with each XCD's tiles dealt round-robin
 ORDER_CASES = [
     (1, 2048, 3, 64, 256, 256, 0, "f16", "f16", 16),   # 96 tiles: 12 per XCD, 6 per 2 wgs
     (2, 1100, 2, 64, 128, 40, 2, "bf16", "f32", 24),   # ragged class ends, 3 wgs per XCD
@@ -181,15 +185,19 @@ ORDER_CASES = [
 @pytest.mark.gpu
 @pytest.mark.parametrize("order", ["interleaved", "contiguous"])
 @pytest.mark.parametrize("case", ORDER_CASES, ids=_ids)
-def test_pvt_orders_match_oracle(case, order, monkeypatch):
+def test_tile_orders_match_oracle(case, order, monkeypatch):
     b, n, h, d, w, wu, dil, ind, outd, wg = case
     monkeypatch.setenv("DIAGMM_MAX_WORKGROUPS", str(wg))
-    monkeypatch.setenv("DIAGMM_PVT_ORDER", order)
-    pl = dm.diagmm_plan("pvT", b, n, h, d, w, wu, dil, DT[ind], DT[outd])
-    assert pl["kernel"] == "pvT_mfma" and pl["strip_workgroups"] == 0, pl
-    assert pl["interleaved"] == (order == "interleaved"), pl
+    monkeypatch.setenv("DIAGMM_TILE_ORDER", order)
+    for mode in ("pv", "pvT"):
+        pl = dm.diagmm_plan(mode, b, n, h, d, w, wu, dil, DT[ind], DT[outd])
+        assert pl["kernel"] == mode + "_mfma" and pl["strip_workgroups"] == 0, pl
+        assert pl["interleaved"] == (order == "interleaved"), pl
     g = datagen.rng(91)
     x = datagen.normal(g, (b, n, h, d), ind, 1.0 / math.sqrt(d))
     probs = datagen.softmax_rows(g, (b, n, h, w + wu + 1), ind)
-    got = dm.diagmm_pvT(probs.cuda(), x.cuda(), w, wu, dil, out_dtype=DT[outd]).cpu()
+    pc, xc = probs.cuda(), x.cuda()
+    got = dm.diagmm_pvT(pc, xc, w, wu, dil, out_dtype=DT[outd]).cpu()
     check_close(got, oracle.pvT(probs, x, w, wu, dil, out_dtype=torch.float64), DT[ind], "pvT")
+    got = dm.diagmm_pv(pc, xc, w, wu, dil, out_dtype=DT[outd]).cpu()
+    check_close(got, oracle.pv(probs, x, w, wu, dil, out_dtype=torch.float64), DT[ind], "pv")

@@ -1,11 +1,12 @@
-// Banded softmax: a group of lanes per band row (a whole wavefront for long rows).
+// Banded softmax: a group of lanes per band row (a wavefront, or a workgroup of four,
+// for long rows).
 //
 // The row (K slots, contiguous in [b][n][h][K]) is read once as aligned 16-byte pieces
 // into registers; the at most two pieces it shares with the neighbouring rows are read
 // and written element by element for this row's own slots only, so rows never touch
 // each other's data and the softmax may run in place.  Slots whose key lies outside the
 // sequence are masked by index (they hold -inf before the max and exactly +0 after).
-// The row max and the sum of exponentials are wavefront reductions; each exponential
+// The row max and the sum of exponentials are group reductions; each exponential
 // is computed once and kept in registers until the normalised values are written.
 //
 // Recipe (csarofeen/pytorch issue 2096, first fusion repro): scale, row max, subtract,
@@ -286,6 +287,129 @@ hipError_t launch_g(const void* scores, void* probs, const Problem& p, float sca
     return hipGetLastError();
 }
 
+// Long rows: a workgroup of 256 lanes per row, lane t holding pieces t, t + 256, ..
+// (P of them), loaded whole as in the group kernel.  The row max and sum combine the four
+// wavefronts through LDS.  A wavefront per row would hold 8 P' = 136 values a lane at
+// 8193 slots and run one wavefront per SIMD; here P = 5 and several rows share a SIMD.
+template <class T, int P>
+__global__ void __launch_bounds__(kThreads)
+softmax_block_kernel(const typename T::T* scores, typename T::T* probs, Problem p, float scale,
+                     int64_t nrows, RowDiv rd) {
+    using ST = typename T::T;
+    constexpr int kVec = 16 / sizeof(ST);
+    constexpr int kWaves = kThreads / 64;
+    __shared__ float red[2][kWaves];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t row = blockIdx.x;
+    const uint32_t bn = div32(rd.h, static_cast<uint32_t>(row));          // b * n + i
+    const int64_t i = bn - div32(rd.n, bn) * rd.n.d;
+    const int64_t lo_off = div32(rd.s, static_cast<uint32_t>(i));
+    const int64_t hi_off = div32(rd.s, static_cast<uint32_t>(p.n - 1 - i));
+    const int k_lo = static_cast<int>(p.w - (lo_off < p.w ? lo_off : p.w));
+    const int k_hi = static_cast<int>(p.w + (hi_off < p.wu ? hi_off : p.wu) + 1);
+    const int K = static_cast<int>(p.K);
+    const int64_t total = nrows * p.K;
+    const int64_t g = row * p.K;                       // first element of the row
+    const int sh = static_cast<int>(g & (kVec - 1));
+    const int nc = (sh + K + kVec - 1) / kVec;
+    const ST* src = scores + (g - sh);                 // 16-byte aligned
+    ST* dst = probs + (g - sh);
+
+    u32x4 raw[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int c = t + kThreads * q;
+        raw[q] = u32x4{0u, 0u, 0u, 0u};
+        if (c < nc && g - sh + (c + 1) * kVec <= total)
+            raw[q] = *reinterpret_cast<const u32x4*>(src + c * kVec);
+    }
+    if (g + K + kVec > total) {                        // the row ends within a piece of the end
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const int c = t + kThreads * q;
+            if (c < nc && g - sh + (c + 1) * kVec > total) {
+                const int b = K - (c * kVec - sh);
+                raw[q] = load_piece_elems<ST>(src + c * kVec, 0, b < kVec ? b : kVec);
+            }
+        }
+    }
+    float x[P][kVec];
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int c = t + kThreads * q;
+        const int base = c * kVec - sh;                // slot of element 0
+        const uint32_t d0 = raw[q][0], d1 = raw[q][1], d2 = raw[q][2], d3 = raw[q][3];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            const int k = base + e;
+            const bool in = c < nc && k >= k_lo && k < k_hi;
+            const uint32_t d = kVec == 8 ? (e < 2 ? d0 : e < 4 ? d1 : e < 6 ? d2 : d3)
+                                         : (e == 0 ? d0 : e == 1 ? d1 : e == 2 ? d2 : d3);
+            x[q][e] = in ? scale * Elem<T>::get(d, e & 1) : -INFINITY;
+            m = fmaxf(m, x[q][e]);
+        }
+    }
+    m = wave_max(m);
+    if (lane == 0) red[0][wave] = m;
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) m = fmaxf(m, red[0][v]);
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < P; ++q)
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            x[q][e] = __expf(x[q][e] - m);             // exp(-inf) = +0 for masked slots
+            sum += x[q][e];
+        }
+    sum = wave_sum(sum);
+    if (lane == 0) red[1][wave] = sum;
+    __syncthreads();
+    sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) sum += red[1][v];
+    const float inv = 1.f / sum;
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int c = t + kThreads * q;
+        if (c >= nc) continue;
+        const int base = c * kVec - sh;
+        uint32_t o0, o1, o2, o3;
+        if constexpr (kVec == 8) {
+            o0 = Elem<T>::bits(x[q][0] * inv) | (Elem<T>::bits(x[q][1] * inv) << 16);
+            o1 = Elem<T>::bits(x[q][2] * inv) | (Elem<T>::bits(x[q][3] * inv) << 16);
+            o2 = Elem<T>::bits(x[q][4] * inv) | (Elem<T>::bits(x[q][5] * inv) << 16);
+            o3 = Elem<T>::bits(x[q][6] * inv) | (Elem<T>::bits(x[q][7] * inv) << 16);
+        } else {
+            o0 = Elem<T>::bits(x[q][0] * inv);
+            o1 = Elem<T>::bits(x[q][1] * inv);
+            o2 = Elem<T>::bits(x[q][2] * inv);
+            o3 = Elem<T>::bits(x[q][3] * inv);
+        }
+        if (base >= 0 && base + kVec <= K) {
+            *reinterpret_cast<u32x4*>(dst + c * kVec) = u32x4{o0, o1, o2, o3};
+        } else {
+            const int a = base < 0 ? -base : 0;
+            const int b = K - base < kVec ? K - base : kVec;
+            store_part<ST>(dst + c * kVec, o0, o1, o2, o3, a, b);
+        }
+    }
+}
+
+template <class T, int P>
+hipError_t launch_b(const void* scores, void* probs, const Problem& p, float scale,
+                    hipStream_t stream) {
+    const int64_t nrows = p.rows() * p.h;
+    launch_kernel((softmax_block_kernel<T, P>), dim3(static_cast<uint32_t>(nrows)),
+                  dim3(kThreads), 0, stream, static_cast<const typename T::T*>(scores),
+                  static_cast<typename T::T*>(probs), p, scale, nrows,
+                  RowDiv{make_div32(static_cast<uint32_t>(p.h)),
+                         make_div32(static_cast<uint32_t>(p.n)),
+                         make_div32(static_cast<uint32_t>(p.s))});
+    return hipGetLastError();
+}
+
 template <class T, int P>
 hipError_t launch_p(const void* scores, void* probs, const Problem& p, float scale,
                     hipStream_t stream) {
@@ -315,7 +439,8 @@ hipError_t launch_t(const void* scores, void* probs, const Problem& p, float sca
     if (pieces <= 64 * 2) return launch_p<T, 2>(scores, probs, p, scale, stream);
     if (pieces <= 64 * 4) return launch_p<T, 4>(scores, probs, p, scale, stream);
     if (pieces <= 64 * 8) return launch_p<T, 8>(scores, probs, p, scale, stream);
-    if (pieces <= 64 * 17) return launch_p<T, 17>(scores, probs, p, scale, stream);
+    if (pieces <= kThreads * 5) return launch_b<T, 5>(scores, probs, p, scale, stream);
+    if (pieces <= kThreads * 9) return launch_b<T, 9>(scores, probs, p, scale, stream);
     return hipErrorInvalidValue;
 }
 
@@ -326,7 +451,7 @@ bool softmax_wave_supported(const Problem& p, int in_dt, int out_dt) {
     const int64_t kvec = in_dt == kF32 ? 4 : 8;
     const int64_t pieces = (p.K + 2 * kvec - 2) / kvec;
     const int64_t grid = (p.rows() * p.h + kRowsPerBlock - 1) / kRowsPerBlock;
-    return pieces <= 64 * 17 && grid < (int64_t(1) << 31) && p.K < (int64_t(1) << 30) &&
+    return pieces <= kThreads * 9 && grid < (int64_t(1) << 31) && p.K < (int64_t(1) << 30) &&
            p.rows() * p.h < (int64_t(1) << 31);
 }
 

@@ -142,3 +142,31 @@ def test_integer_inputs_are_exact(dt):
         assert_bits_equal(got, oracle.pv(p, q, w, wu, dil, out_dtype=odt), "pv ints")
         got = dm.diagmm_pvT(p.cuda(), q.cuda(), w, wu, dil, out_dtype=odt).cpu()
         assert_bits_equal(got, oracle.pvT(p, q, w, wu, dil, out_dtype=odt), "pvT ints")
+
+
+# (b, n, h, w, w_upper, dilation, dtype): rows long enough for a workgroup per row (more
+# than 512 pieces of 16 bytes: 5 pieces per lane up to 1280 pieces, 9 up to 2304), with
+# short sequences so that most rows are clipped at the sequence ends
+LONG_ROW_CASES = [
+    (1, 40, 2, 2100, 2100, 0, "f16"),      # 4201 slots: 526 pieces, 5 per lane
+    (2, 30, 1, 4096, 4096, 0, "bf16"),     # 8193 slots
+    (1, 25, 1, 1100, 1100, 0, "f32"),      # 2201 f32 slots: 551 pieces
+    (1, 20, 1, 6000, 6000, 0, "f16"),      # 12001 slots: 1501 pieces, 9 per lane
+    (1, 33, 3, 3000, 1500, 2, "f16"),      # 4501 slots, dilation 2, odd row starts
+]
+
+
+@pytest.mark.parametrize("inplace", [False, True])
+@pytest.mark.parametrize("case", LONG_ROW_CASES,
+                         ids=lambda c: f"b{c[0]}n{c[1]}h{c[2]}w{c[3]}u{c[4]}s{c[5]}-{c[6]}")
+def test_banded_softmax_long_rows(case, inplace):
+    import sliding_window_attention_diagmm_amd as dm
+    b, n, h, w, wu, dil, dt = case
+    g = datagen.rng(510)
+    scores = datagen.normal(g, (b, n, h, w + wu + 1), dt, 3.0)
+    sc = scores.cuda()
+    got = dm.diagmm_banded_softmax(sc, w, wu, dil, 0.125, inplace=inplace).cpu()
+    ref = oracle.softmax(scores, w, wu, dil, 0.125, out_dtype=torch.float64)
+    mask = in_range_mask(b, n, h, w, wu, dil)
+    check_close(got, ref, DT[dt], "softmax", mask)
+    assert_bits_equal(got[~mask], torch.zeros_like(got[~mask]), "softmax masked slots")

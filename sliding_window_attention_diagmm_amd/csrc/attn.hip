@@ -48,6 +48,8 @@
 // launch merges the nsplit states of each block of global rows and stores the rows (the
 // kernel boundary orders it after every partial state; a merge inside the first launch
 // would need a device-scope release per workgroup, which writes back a whole L2).
+#include <type_traits>
+
 #include "launch.hpp"
 #include "ring.hpp"
 
@@ -60,6 +62,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// An MFMA operand of eight 1.0 values.
+template <class In> struct Ones;
+template <> struct Ones<F16> {
+    __device__ __forceinline__ static f16x8 v() {
+        return f16x8{1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
+    }
+};
+template <> struct Ones<BF16> {
+    __device__ __forceinline__ static bf16x8 v() {
+        const __bf16 o = static_cast<__bf16>(1.0f);
+        return bf16x8{o, o, o, o, o, o, o, o};
+    }
+};
 
 template <class In> struct Mfma;
 template <> struct Mfma<F16> {
@@ -215,7 +233,8 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
     constexpr int kQk = D / 32;                          // MFMA K-steps over the channels
     constexpr int kCb = D / 16;                          // 16-channel output blocks
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, grp = lane >> 4;
     const int ng = a.ng;
 
@@ -308,26 +327,44 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
     // ---- staging of one key block: K and V rows u0 .. u0 + 63 (rows past the class are
     // loaded from its last row and written as zeros)
     u32x4 kreg[kStage], vreg[kStage];
+    // this thread's pieces: row pc / kPieces of the block, channels 8 (pc % kPieces) ..;
+    // the block at u0 reads class row min(u0, len - 1 - row) + row (rows past the class
+    // at its last row)
+    int64_t lane_off[kStage];
+    int lane_lim[kStage];
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+        const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
+        lane_off[i] = base + int64_t(row) * step + 8 * ch;
+        lane_lim[i] = len - 1 - row;
+    }
     auto load_block = [&](int u0) {
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
-            const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
-            int u = u0 + row;
-            u = u < len ? u : len - 1;
-            const int64_t off = base + int64_t(u) * step + 8 * ch;
+            const int du = u0 < lane_lim[i] ? u0 : lane_lim[i];
+            const int64_t off = lane_off[i] + int64_t(du) * step;
             kreg[i] = *reinterpret_cast<const u32x4*>(ksrc + off);
             vreg[i] = *reinterpret_cast<const u32x4*>(vsrc + off);
         }
     };
     auto store_block = [&](int u0) {
+        auto put = [&](auto whole) {
 #pragma unroll
-        for (int i = 0; i < kStage; ++i) {
-            const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
-            const bool ok = u0 + row < len;
-            const u32x4 z{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(klds + kpiece<D>(row, ch)) = ok ? kreg[i] : z;
-            *reinterpret_cast<u32x4*>(vlds + ring_piece<D>(row, ch)) = ok ? vreg[i] : z;
-        }
+            for (int i = 0; i < kStage; ++i) {
+                const int pc = tid + kThreads * i, row = pc / kPieces, ch = pc % kPieces;
+                u32x4 kv = kreg[i], vv = vreg[i];
+                if constexpr (!decltype(whole)::value) {
+                    const bool ok = u0 + row < len;
+                    const u32x4 z{0u, 0u, 0u, 0u};
+                    kv = ok ? kv : z;
+                    vv = ok ? vv : z;
+                }
+                *reinterpret_cast<u32x4*>(klds + kpiece<D>(row, ch)) = kv;
+                *reinterpret_cast<u32x4*>(vlds + ring_piece<D>(row, ch)) = vv;
+            }
+        };
+        if (u0 + kKeys <= len) put(std::true_type{});   // the whole block inside the class
+        else put(std::false_type{});
     };
 
     // a block of global keys: ranks 64 gb .. 64 gb + 63 of the set (zeros past its size)
@@ -357,13 +394,18 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
 #pragma unroll
     for (int cb = 0; cb < kCb; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -__builtin_inff();   // running maximum of this lane's query (log2 units)
-    float l_run = 0.0f;                // this lane's share of the running sum
+    // Running sum of the query's probabilities, as rounded for the product with V: an
+    // MFMA with an all-ones A operand sums each B column (all 32 keys of a chunk, every
+    // lane group) into every element of the lane's accumulator.
+    f32x4 lsum{0.f, 0.f, 0.f, 0.f};
+    const V ones = Ones<In>::v();
 
     int aoff[kCb];
 #pragma unroll
     for (int cb = 0; cb < kCb; ++cb) aoff[cb] = tr_lane_off<D>(col, cb);
     // K rows of this lane's A operand within a 32-key chunk: tile 0 and tile 1
     const int krow0 = 8 * (col >> 2) + (col & 3), krow1 = krow0 + 4;
+    const float cs = a.scale_log2;
 
     // gl: the staged block holds global keys (ranks u0 .. u0 + 63 of the set)
     auto compute_block = [&](int u0, bool gl) {
@@ -381,10 +423,12 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
                 s1[c] = Mfma<In>::run(a1, qop[kk], s1[c]);
             }
         }
-        // ---- scale, mask (only blocks that are not wholly inside every row's window of
-        // this wave need it), block maximum
-        float x[kChunks][8];
+        // ---- mask (only blocks that are not wholly inside every row's window of this
+        // wave need it), block maximum in log2 units.  Inner blocks keep the raw scores
+        // (the scale, when positive, commutes with the maximum and goes into the
+        // exponent's fma); masked blocks replace them by scale * score or -inf.
         float mx = -__builtin_inff();
+        auto sc = [&](int c, int e) { return e < 4 ? s0[c][e] : s1[c][e - 4]; };
         const int lo = tq - w, hi = tq + wu;   // in-range keys of this query (and < len)
         const int tw = t0 + 16 * wv;           // this wave's first row
         // (with global tokens: a window block none of whose keys is global; the bitmap
@@ -398,32 +442,44 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
         else
             inner = !gl && u0 >= tw + 15 - w && u0 + kKeys - 1 <= tw + wu &&
                     u0 + kKeys - 1 < len && (kMode == kBand || no_global_keys());
+        inner = inner && cs > 0.0f;
         if (inner) {
 #pragma unroll
             for (int c = 0; c < kChunks; ++c)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    x[c][e] = (e < 4 ? s0[c][e] : s1[c][e - 4]) * a.scale_log2;
-                    mx = fmaxf(mx, x[c][e]);
-                }
+                for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc(c, e));
+            mx *= cs;
         } else {
 #pragma unroll
             for (int c = 0; c < kChunks; ++c)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int u = u0 + 32 * c + 8 * grp + e;
-                    const float sv = e < 4 ? s0[c][e] : s1[c][e - 4];
                     bool ok;
                     if constexpr (kRowsMode) ok = u < len;
                     else if constexpr (kMode == kBandGlobal)
                         ok = gl ? u < ngd : (u >= lo && u <= hi && u < len && !is_global_key(u));
                     else ok = u >= lo && u <= hi && u < len;
-                    x[c][e] = ok ? sv * a.scale_log2 : -__builtin_inff();
-                    mx = fmaxf(mx, x[c][e]);
+                    const float sv = ok ? sc(c, e) * cs : -__builtin_inff();
+                    if (e < 4) s0[c][e] = sv;               // (e is a constant here)
+                    else s1[c][e - 4] = sv;
+                    mx = fmaxf(mx, sv);
                 }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // the four lane groups of a query: swaps with lanes l ^ 16 and l ^ 32 (each swap
+        // returns this lane's value and its partner's, in some order).  The halves are
+        // read as integers first: bit-casting the pair's elements straight to float was
+        // compiled as if both were the first one.
+        {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx),
+                                                            __float_as_uint(mx), false, false);
+            const uint32_t r0 = r[0], r1 = r[1];
+            mx = fmaxf(__uint_as_float(r0), __uint_as_float(r1));
+            const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                            __float_as_uint(mx), false, false);
+            const uint32_t q0 = q[0], q1 = q[1];
+            mx = fmaxf(__uint_as_float(q0), __uint_as_float(q1));
+        }
         // ---- rescale only when some row's maximum grew by more than 2^8: otherwise the
         // old reference stays, and the block's terms exp2(x - m) stay below 256, exact
         // in the sum and representable in the 16-bit probabilities alike
@@ -432,24 +488,23 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
             const float alpha = __builtin_amdgcn_exp2f(
                 m_run - (m_new == -__builtin_inff() ? 0.0f : m_new));
             m_run = m_new;
-            l_run *= alpha;
+            lsum *= alpha;
 #pragma unroll
             for (int cb = 0; cb < kCb; ++cb) acc[cb] *= alpha;
         }
         const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
 
-        // ---- probabilities as the B operand of out^T = V^T P^T, and the products
+        // ---- probabilities exp2(k s - m) (k = scale on inner blocks, 1 on masked ones)
+        // as the B operand of out^T = V^T P^T, and the products
+        const float k1 = inner ? cs : 1.0f;
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
-            float p[8];
+            f32x8 p;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = __builtin_amdgcn_exp2f(x[c][e] - m_use);
-                l_run += p[e];
-            }
-            const u32x4 pb{pack2(p[0], p[1], In{}), pack2(p[2], p[3], In{}),
-                           pack2(p[4], p[5], In{}), pack2(p[6], p[7], In{})};
-            const V bop = __builtin_bit_cast(V, pb);
+            for (int e = 0; e < 8; ++e)
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc(c, e), k1, -m_use));
+            const V bop = __builtin_convertvector(p, V);
+            lsum = Mfma<In>::run(ones, bop, lsum);
             const unsigned char* rp = vlds + (32 * c + 8 * grp) * (2 * D);
 #pragma unroll
             for (int cb = 0; cb < kCb; ++cb) {
@@ -459,8 +514,6 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
         }
     };
 
-    // The next block's loads overlap this block's compute (a clamped repeat of the last
-    // block when there is none, so the loads are unconditional).
     if constexpr (kMode == kBandGlobal) {
         const int ngb = (ngd + kKeys - 1) / kKeys;
         for (int gb = 0; gb < ngb; ++gb) {
@@ -471,6 +524,8 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
             __syncthreads();
         }
     }
+    // The next block's loads overlap this block's compute (a clamped repeat of the last
+    // block when there is none, so the loads are unconditional).
     load_block(u_lo);
     for (int blk = 0; blk < nblk; ++blk) {
         const int u0 = u_lo + kKeys * blk;
@@ -481,9 +536,7 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
         __syncthreads();
     }
 
-    float l = l_run;
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = lsum[0];
     if constexpr (kRowsMode) {
         // ---- this range's partial state of the rows (merged by the second launch)
         if (tq < ngd) {
@@ -622,12 +675,14 @@ AttnArgs make_args(const Problem& p, float scale, int64_t ng = 0) {
     a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
     a.ng = static_cast<int32_t>(ng);
     if (ng > 0 && p.n > 0) {
-        // key ranges: about 256 global-row workgroups in all (a few 64-key blocks each),
-        // never an empty range
+        // key ranges about as long as a band workgroup's walk (64 + w + w_upper keys), so
+        // that the global-row workgroups end with the band ones and, with them, fill one
+        // round of the machine; never an empty range
         a.nrb = static_cast<int32_t>((ng + kRows - 1) / kRows);
         const int64_t units = p.b * p.h * a.nrb;
         const int64_t blocks = (p.n + kKeys - 1) / kKeys;
-        int64_t nsplit = (256 + units - 1) / units;
+        const int64_t band_blocks = (kRows + p.w + p.wu + kKeys - 1) / kKeys;
+        int64_t nsplit = (blocks + band_blocks - 1) / band_blocks;
         nsplit = nsplit < blocks ? nsplit : blocks;
         nsplit = nsplit < kMaxSplit ? nsplit : kMaxSplit;
         const int64_t kr = (blocks + nsplit - 1) / nsplit * kKeys;

@@ -25,6 +25,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / 64;
+// The group kernel takes G waves: 8 with dilation, so that more rows share one staged run
+// of mask values, else 4.
 constexpr int kPer = 3;                        // pieces per lane in the group kernel
 constexpr int kMaskWin = 4096;                 // mask floats a workgroup stages (dilated rows)
 
@@ -77,8 +79,8 @@ __device__ __forceinline__ RowGeo row_geo(const Problem& p, const RowDiv& rd, in
                   static_cast<int>(p.w + (hi_off < p.wu ? hi_off : p.wu) + 1)};
 }
 
-template <class T, int L>
-__global__ void __launch_bounds__(kThreads)
+template <class T, int L, int G>
+__global__ void __launch_bounds__(G * 64)
 softmax_masked_group_kernel(const typename T::T* scores, typename T::T* probs,
                             const float* __restrict__ key_mask, Problem p, float scale,
                             float mask_value, int64_t nrows, RowDiv rd) {
@@ -87,7 +89,7 @@ softmax_masked_group_kernel(const typename T::T* scores, typename T::T* probs,
     constexpr int kRowsPerWave = 64 / L;
     const int lane = threadIdx.x & 63;
     const int t = lane % L;
-    const int64_t row_raw = (int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6)) *
+    const int64_t row_raw = (int64_t(blockIdx.x) * G + (threadIdx.x >> 6)) *
                                 kRowsPerWave + lane / L;
     const bool row_ok = row_raw < nrows;
     const int64_t row = row_ok ? row_raw : nrows - 1;   // idle groups compute a real row
@@ -131,9 +133,9 @@ softmax_masked_group_kernel(const typename T::T* scores, typename T::T* probs,
     int64_t lo = 0;
     bool staged = false;
     if (p.s > 1) {
-        const int64_t r0 = int64_t(blockIdx.x) * kWavesPerBlock * kRowsPerWave;
-        const int64_t r1 = (r0 + kWavesPerBlock * kRowsPerWave - 1 < nrows - 1)
-                               ? r0 + kWavesPerBlock * kRowsPerWave - 1 : nrows - 1;
+        const int64_t r0 = int64_t(blockIdx.x) * G * kRowsPerWave;
+        const int64_t r1 = (r0 + G * kRowsPerWave - 1 < nrows - 1)
+                               ? r0 + G * kRowsPerWave - 1 : nrows - 1;
         const int64_t m0 = div32(rd.h, static_cast<uint32_t>(r0));
         const int64_t m1 = div32(rd.h, static_cast<uint32_t>(r1));
         lo = m0 - p.w * p.s;
@@ -142,21 +144,25 @@ softmax_masked_group_kernel(const typename T::T* scores, typename T::T* probs,
         hi = hi > p.b * p.n - 1 ? p.b * p.n - 1 : hi;
         staged = hi - lo + 1 <= kMaskWin;            // the same for every thread
         if (staged) {
-            for (int64_t x = threadIdx.x; x <= hi - lo; x += kThreads) mwin[x] = key_mask[lo + x];
+            for (int64_t x = threadIdx.x; x <= hi - lo; x += G * 64) mwin[x] = key_mask[lo + x];
             __syncthreads();
         }
     }
+    // LDS index of this row's slot k: ibase + k s, clamped into the staged run (the value
+    // of an out-of-range slot is not used)
+    const int ibase = static_cast<int>(rg.mrow - lo - p.w * p.s);
+    const int imax = static_cast<int>(kMaskWin - 1);
+    const int si = static_cast<int>(p.s);
     float mk[kPer][kVec];
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
         const int base = (t + L * q) * kVec - sh;
         if (staged) {
+            const int i0 = ibase + base * si;
 #pragma unroll
             for (int e = 0; e < kVec; ++e) {
-                const int k = base + e;
-                const bool in = k >= rg.k_lo && k < rg.k_hi;
-                const int64_t off = in ? static_cast<int64_t>(k - p.w) * p.s : 0;
-                mk[q][e] = mwin[rg.mrow + off - lo];
+                const int ix = i0 + e * si;
+                mk[q][e] = mwin[ix < 0 ? 0 : (ix > imax ? imax : ix)];
             }
         } else if (p.s == 1 && base >= rg.k_lo && base + kVec <= rg.k_hi) {
             const float* mp = key_mask + rg.mrow + (base - p.w);   // consecutive, merged
@@ -283,16 +289,22 @@ int group_lanes_masked(int64_t pieces) {
     return 0;
 }
 
+template <class T, int L, int G>
+hipError_t launch_gw(const void* scores, void* probs, const float* key_mask, const Problem& p,
+                     float scale, float mv, const RowDiv& rd, hipStream_t stream) {
+    const int64_t nrows = p.rows() * p.h;
+    const int64_t per_block = G * (64 / L);
+    const int64_t grid = (nrows + per_block - 1) / per_block;
+    launch_kernel((softmax_masked_group_kernel<T, L, G>), dim3(static_cast<uint32_t>(grid)),
+                  dim3(G * 64), 0, stream, static_cast<const typename T::T*>(scores),
+                  static_cast<typename T::T*>(probs), key_mask, p, scale, mv, nrows, rd);
+    return hipGetLastError();
+}
 template <class T, int L>
 hipError_t launch_g(const void* scores, void* probs, const float* key_mask, const Problem& p,
                     float scale, float mv, const RowDiv& rd, hipStream_t stream) {
-    const int64_t nrows = p.rows() * p.h;
-    const int64_t per_block = kWavesPerBlock * (64 / L);
-    const int64_t grid = (nrows + per_block - 1) / per_block;
-    launch_kernel((softmax_masked_group_kernel<T, L>), dim3(static_cast<uint32_t>(grid)),
-                  dim3(kThreads), 0, stream, static_cast<const typename T::T*>(scores),
-                  static_cast<typename T::T*>(probs), key_mask, p, scale, mv, nrows, rd);
-    return hipGetLastError();
+    if (p.s > 1) return launch_gw<T, L, 8>(scores, probs, key_mask, p, scale, mv, rd, stream);
+    return launch_gw<T, L, 4>(scores, probs, key_mask, p, scale, mv, rd, stream);
 }
 
 template <class T>

@@ -90,6 +90,14 @@ __device__ __forceinline__ piece_t mask_piece(const piece_t& v, int a, int b) {
                    v[2] & keep_mask<ST>(2, a, b), v[3] & keep_mask<ST>(3, a, b)};
 }
 
+// Whether a piece of `vec` elements whose element 0 is slot `base` of its band row holds
+// any slot of the row's in-range interval [lo, hi): a piece that holds none is never read
+// (its values are masked whatever they are), which near the ends of the sequence, where
+// part of the window falls outside it, saves that part of the read.
+__device__ __forceinline__ bool in_reach(int base, int vec, int lo, int hi) {
+    return base + vec > lo && base < hi;
+}
+
 // Elements [a, b) of a piece read one by one (for a piece that runs past the end of its
 // tensor); the others read as zero.
 template <class ST>

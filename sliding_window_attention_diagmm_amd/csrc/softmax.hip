@@ -91,7 +91,7 @@ softmax_wave_kernel(const typename T::T* scores, typename T::T* probs, Problem p
         const int c = lane + 64 * q;
         const int base = c * kVec - sh;                // slot of element 0
         uint32_t dw[4] = {0u, 0u, 0u, 0u};   // the piece as dwords (static indices only)
-        if (c < nc) {
+        if (c < nc && in_reach(base, kVec, k_lo, k_hi)) {
             if (base >= 0 && base + kVec <= K) {
                 const u32x4 v = *reinterpret_cast<const u32x4*>(src + c * kVec);
                 dw[0] = v[0];
@@ -203,14 +203,14 @@ softmax_group_kernel(const typename T::T* scores, typename T::T* probs, Problem 
     for (int q = 0; q < P; ++q) {
         const int c = t + L * q;
         raw[q] = u32x4{0u, 0u, 0u, 0u};
-        if (c < nc && g - sh + (c + 1) * kVec <= total)
+        if (c < nc && in_reach(c * kVec - sh, kVec, k_lo, k_hi) && g - sh + (c + 1) * kVec <= total)
             raw[q] = *reinterpret_cast<const u32x4*>(src + c * kVec);
     }
     if (g + K + kVec > total) {                        // the row ends within a piece of the end
 #pragma unroll
         for (int q = 0; q < P; ++q) {
             const int c = t + L * q;
-            if (c < nc && g - sh + (c + 1) * kVec > total) {
+            if (c < nc && in_reach(c * kVec - sh, kVec, k_lo, k_hi) && g - sh + (c + 1) * kVec > total) {
                 const int b = K - (c * kVec - sh);
                 raw[q] = load_piece_elems<ST>(src + c * kVec, 0, b < kVec ? b : kVec);
             }
@@ -320,14 +320,14 @@ softmax_block_kernel(const typename T::T* scores, typename T::T* probs, Problem 
     for (int q = 0; q < P; ++q) {
         const int c = t + kThreads * q;
         raw[q] = u32x4{0u, 0u, 0u, 0u};
-        if (c < nc && g - sh + (c + 1) * kVec <= total)
+        if (c < nc && in_reach(c * kVec - sh, kVec, k_lo, k_hi) && g - sh + (c + 1) * kVec <= total)
             raw[q] = *reinterpret_cast<const u32x4*>(src + c * kVec);
     }
     if (g + K + kVec > total) {                        // the row ends within a piece of the end
 #pragma unroll
         for (int q = 0; q < P; ++q) {
             const int c = t + kThreads * q;
-            if (c < nc && g - sh + (c + 1) * kVec > total) {
+            if (c < nc && in_reach(c * kVec - sh, kVec, k_lo, k_hi) && g - sh + (c + 1) * kVec > total) {
                 const int b = K - (c * kVec - sh);
                 raw[q] = load_piece_elems<ST>(src + c * kVec, 0, b < kVec ? b : kVec);
             }

@@ -19,7 +19,8 @@
 // the sequence are masked by index: they never enter the dot product, whatever P and dP
 // hold there, and their gradient is exactly +0.
 //
-// Rows of other alignments, or longer than a wavefront's registers hold, go to a
+// Rows longer than a wavefront's registers hold well take a workgroup per row with the
+// same one-read layout; rows of other alignments, or longer still, go to a
 // workgroup-per-row kernel that reads the row twice.
 #include "launch.hpp"
 #include "tiles.hpp"
@@ -106,7 +107,8 @@ softmax_bwd_group_kernel(const typename T::T* probs, const typename T::T* dprobs
     for (int q = 0; q < P; ++q) {
         const int c = t + L * q;
         rp[q] = rd_[q] = u32x4{0u, 0u, 0u, 0u};
-        if (c < nc && g - sh + (c + 1) * kVec <= total) {
+        if (c < nc && in_reach(c * kVec - sh, kVec, rg.k_lo, rg.k_hi) &&
+            g - sh + (c + 1) * kVec <= total) {
             rp[q] = *reinterpret_cast<const u32x4*>(ps + c * kVec);
             rd_[q] = *reinterpret_cast<const u32x4*>(ds + c * kVec);
         }
@@ -115,7 +117,8 @@ softmax_bwd_group_kernel(const typename T::T* probs, const typename T::T* dprobs
 #pragma unroll
         for (int q = 0; q < P; ++q) {
             const int c = t + L * q;
-            if (c < nc && g - sh + (c + 1) * kVec > total) {
+            if (c < nc && in_reach(c * kVec - sh, kVec, rg.k_lo, rg.k_hi) &&
+                g - sh + (c + 1) * kVec > total) {
                 const int b = K - (c * kVec - sh);
                 rp[q] = load_piece_elems<ST>(ps + c * kVec, 0, b < kVec ? b : kVec);
                 rd_[q] = load_piece_elems<ST>(ds + c * kVec, 0, b < kVec ? b : kVec);
@@ -184,6 +187,117 @@ softmax_bwd_group_kernel(const typename T::T* probs, const typename T::T* dprobs
     }
 }
 
+// One workgroup per row for rows longer than a wavefront's registers hold well (a wave
+// kernel with 17 pieces per lane needs every VGPR and runs one wave per SIMD): thread t
+// holds pieces t, t + 256, .., t + 256 (P - 1) of P and dP, the dot product is reduced
+// within each wavefront and then across the four through LDS, and every read completes
+// before the barrier that ends that reduction, so the kernel may run in place.
+template <class T, int P>
+__global__ void __launch_bounds__(kThreads)
+softmax_bwd_block_kernel(const typename T::T* probs, const typename T::T* dprobs,
+                         typename T::T* dscores, Problem p, float scale, int64_t nrows,
+                         RowDiv rd) {
+    using ST = typename T::T;
+    constexpr int kVec = 16 / sizeof(ST);
+    __shared__ float part[kWavesPerBlock];
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const Range rg = row_range(p, rd, row);
+    const int K = static_cast<int>(p.K);
+    const int64_t total = nrows * p.K;
+    const int64_t g = row * p.K;
+    const int sh = static_cast<int>(g & (kVec - 1));
+    const int nc = (sh + K + kVec - 1) / kVec;
+    const ST* ps = probs + (g - sh);
+    const ST* ds = dprobs + (g - sh);
+    ST* dst = dscores + (g - sh);
+
+    u32x4 rp[P], rd_[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int c = t + kThreads * q;
+        rp[q] = rd_[q] = u32x4{0u, 0u, 0u, 0u};
+        if (c < nc && in_reach(c * kVec - sh, kVec, rg.k_lo, rg.k_hi) &&
+            g - sh + (c + 1) * kVec <= total) {
+            rp[q] = *reinterpret_cast<const u32x4*>(ps + c * kVec);
+            rd_[q] = *reinterpret_cast<const u32x4*>(ds + c * kVec);
+        }
+    }
+    if (g + K + kVec > total) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const int c = t + kThreads * q;
+            if (c < nc && in_reach(c * kVec - sh, kVec, rg.k_lo, rg.k_hi) &&
+                g - sh + (c + 1) * kVec > total) {
+                const int b = K - (c * kVec - sh);
+                rp[q] = load_piece_elems<ST>(ps + c * kVec, 0, b < kVec ? b : kVec);
+                rd_[q] = load_piece_elems<ST>(ds + c * kVec, 0, b < kVec ? b : kVec);
+            }
+        }
+    }
+    auto elem = [&](uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3, int e) {
+        const uint32_t d = kVec == 8 ? (e < 2 ? d0 : e < 4 ? d1 : e < 6 ? d2 : d3)
+                                     : (e == 0 ? d0 : e == 1 ? d1 : e == 2 ? d2 : d3);
+        return Elem<T>::get(d, e & 1);
+    };
+    float dot = 0.f;
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int c = t + kThreads * q;
+        const int base = c * kVec - sh;
+        const uint32_t a0 = rp[q][0], a1 = rp[q][1], a2 = rp[q][2], a3 = rp[q][3];
+        const uint32_t b0 = rd_[q][0], b1 = rd_[q][1], b2 = rd_[q][2], b3 = rd_[q][3];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            const int k = base + e;
+            const bool in = c < nc && k >= rg.k_lo && k < rg.k_hi;
+            const float pd = elem(a0, a1, a2, a3, e) * elem(b0, b1, b2, b3, e);
+            dot += in ? pd : 0.f;
+        }
+    }
+    dot = group_sum<64>(dot);
+    if ((t & 63) == 0) part[t >> 6] = dot;
+    __syncthreads();
+    dot = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < kWavesPerBlock; ++wv) dot += part[wv];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int c = t + kThreads * q;
+        if (c >= nc) continue;
+        const int base = c * kVec - sh;
+        const uint32_t a0 = rp[q][0], a1 = rp[q][1], a2 = rp[q][2], a3 = rp[q][3];
+        const uint32_t b0 = rd_[q][0], b1 = rd_[q][1], b2 = rd_[q][2], b3 = rd_[q][3];
+        float gv[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            const int k = base + e;
+            const bool in = k >= rg.k_lo && k < rg.k_hi;
+            const float r = scale * elem(a0, a1, a2, a3, e) * (elem(b0, b1, b2, b3, e) - dot);
+            gv[e] = in ? r : 0.f;
+        }
+        uint32_t o0, o1, o2, o3;
+        if constexpr (kVec == 8) {
+            o0 = Elem<T>::bits(gv[0]) | (Elem<T>::bits(gv[1]) << 16);
+            o1 = Elem<T>::bits(gv[2]) | (Elem<T>::bits(gv[3]) << 16);
+            o2 = Elem<T>::bits(gv[4]) | (Elem<T>::bits(gv[5]) << 16);
+            o3 = Elem<T>::bits(gv[6]) | (Elem<T>::bits(gv[7]) << 16);
+        } else {
+            o0 = Elem<T>::bits(gv[0]);
+            o1 = Elem<T>::bits(gv[1]);
+            o2 = Elem<T>::bits(gv[2]);
+            o3 = Elem<T>::bits(gv[3]);
+        }
+        if (base >= 0 && base + kVec <= K) {
+            *reinterpret_cast<u32x4*>(dst + c * kVec) = u32x4{o0, o1, o2, o3};
+        } else {
+            const int a = base < 0 ? -base : 0;
+            const int b = K - base < kVec ? K - base : kVec;
+            store_part<ST>(dst + c * kVec, o0, o1, o2, o3, a, b);
+        }
+    }
+}
+
 // One workgroup per row, any alignment and length: the dot product over the row's
 // in-range slots (strided over the threads, then reduced across the workgroup), then the
 // gradient element by element.  Every read of the row completes before the first write
@@ -231,19 +345,36 @@ hipError_t launch_g(const void* probs, const void* dprobs, void* dscores, const 
 
 // Lanes per row for a row touching `pieces` 16-byte pieces: the fewest lanes holding at
 // most 3 pieces each (a 513-slot f16 row on 32 lanes: one load instruction then covers two
-// rows of 512 contiguous bytes), or a whole wavefront with up to 17 each; 0 = the row kernel.
+// rows of 512 contiguous bytes), a whole wavefront with up to 8 each, or (returned as 256)
+// a whole workgroup with up to 5 or 9 each; 0 = the row kernel.
 int group_lanes(int64_t pieces, int* per_lane) {
     for (int l = 1; l <= 32; l *= 2)
         if (pieces <= 3 * l) {
             *per_lane = 3;
             return l;
         }
-    for (int pl : {2, 4, 8, 17})
+    for (int pl : {2, 4, 8})
         if (pieces <= 64 * pl) {
             *per_lane = pl;
             return 64;
         }
+    for (int pl : {5, 9})
+        if (pieces <= kThreads * pl) {
+            *per_lane = pl;
+            return kThreads;
+        }
     return 0;
+}
+
+template <class T, int P>
+hipError_t launch_b(const void* probs, const void* dprobs, void* dscores, const Problem& p,
+                    float scale, const RowDiv& rd, hipStream_t stream) {
+    const int64_t nrows = p.rows() * p.h;
+    launch_kernel((softmax_bwd_block_kernel<T, P>), dim3(static_cast<uint32_t>(nrows)),
+                  dim3(kThreads), 0, stream, static_cast<const typename T::T*>(probs),
+                  static_cast<const typename T::T*>(dprobs),
+                  static_cast<typename T::T*>(dscores), p, scale, nrows, rd);
+    return hipGetLastError();
 }
 
 template <class T>
@@ -265,8 +396,10 @@ hipError_t launch_t(const void* probs, const void* dprobs, void* dscores, const 
     case 64:
         if (per == 2) return launch_g<T, 64, 2>(probs, dprobs, dscores, p, scale, rd, stream);
         if (per == 4) return launch_g<T, 64, 4>(probs, dprobs, dscores, p, scale, rd, stream);
-        if (per == 8) return launch_g<T, 64, 8>(probs, dprobs, dscores, p, scale, rd, stream);
-        return launch_g<T, 64, 17>(probs, dprobs, dscores, p, scale, rd, stream);
+        return launch_g<T, 64, 8>(probs, dprobs, dscores, p, scale, rd, stream);
+    case kThreads:
+        if (per == 5) return launch_b<T, 5>(probs, dprobs, dscores, p, scale, rd, stream);
+        return launch_b<T, 9>(probs, dprobs, dscores, p, scale, rd, stream);
     default: {
         const int64_t nrows = p.rows() * p.h;
         const int64_t grid = nrows < (int64_t(1) << 20) ? nrows : (int64_t(1) << 20);
@@ -283,7 +416,7 @@ bool is16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace
 
-// The fast kernel needs 16-byte aligned tensors, rows of at most 64 x 17 pieces and
+// The fast kernels need 16-byte aligned tensors, rows of at most 256 x 9 pieces and
 // 32-bit row arithmetic; the row kernel takes the rest (32-bit row counts).
 bool softmax_bwd_fast(const Problem& p, int dt, const void* a, const void* b, const void* c) {
     const int64_t kvec = dt == kF32 ? 4 : 8;
@@ -304,6 +437,7 @@ int64_t softmax_bwd_workgroups(const Problem& p, int dt, bool fast) {
     int per = 0;
     const int l = fast ? group_lanes((p.K + 2 * kvec - 2) / kvec, &per) : 0;
     if (l == 0) return nrows < (int64_t(1) << 20) ? nrows : (int64_t(1) << 20);
+    if (l == kThreads) return nrows;
     const int64_t per_block = kWavesPerBlock * (64 / l);
     return (nrows + per_block - 1) / per_block;
 }
@@ -312,8 +446,8 @@ const char* softmax_bwd_kernel_name(const Problem& p, int dt, bool fast) {
     if (!fast) return "softmax_bwd_rows";
     const int64_t kvec = dt == kF32 ? 4 : 8;
     int per = 0;
-    return group_lanes((p.K + 2 * kvec - 2) / kvec, &per) == 64 ? "softmax_bwd_wave"
-                                                                  : "softmax_bwd_group";
+    const int l = group_lanes((p.K + 2 * kvec - 2) / kvec, &per);
+    return l == kThreads ? "softmax_bwd_block" : l == 64 ? "softmax_bwd_wave" : "softmax_bwd_group";
 }
 
 hipError_t launch_softmax_bwd(const void* probs, const void* dprobs, void* dscores,

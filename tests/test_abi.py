@@ -229,9 +229,14 @@ def test_softmax_bwd_plan_picks_lanes_by_row_length(lib):
     assert fast["kernel"] == "softmax_bwd_group"
     # 12 * 4096 rows, 32 lanes per row (513 slots: up to 66 pieces of 8), 4 waves per block
     assert fast["workgroups"] == 12 * 4096 // (4 * 2)
+    wave = dm.diagmm_plan("softmax_bwd", 1, 4096, 12, 1, 1200, 1200, 0, torch.float16)
+    assert wave["kernel"] == "softmax_bwd_wave"
+    assert wave["workgroups"] == 12 * 4096 // 4
     long = dm.diagmm_plan("softmax_bwd", 1, 32768, 12, 1, 4096, 4096, 0, torch.float16)
-    assert long["kernel"] == "softmax_bwd_wave"
-    huge = dm.diagmm_plan("softmax_bwd", 1, 64, 1, 1, 9000, 9000, 0, torch.float16)
+    assert long["kernel"] == "softmax_bwd_block" and long["workgroups"] == 12 * 32768
+    longest = dm.diagmm_plan("softmax_bwd", 1, 64, 1, 1, 9000, 9000, 0, torch.float16)
+    assert longest["kernel"] == "softmax_bwd_block"
+    huge = dm.diagmm_plan("softmax_bwd", 1, 64, 1, 1, 10000, 10000, 0, torch.float16)
     assert huge["kernel"] == "softmax_bwd_rows"
     with pytest.raises(dm.DiagmmError) as e:
         dm.diagmm_plan("softmax_bwd", 1, 64, 1, 1, 8, 8, 0, torch.float16, torch.float32)

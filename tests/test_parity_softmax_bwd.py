@@ -3,8 +3,8 @@
 dS = scale * P * (dP - sum(P * dP)) per band row over the in-range slots, exactly +0 in
 the others (the chain rule through the banded softmax; the oracle's pins are in
 test_oracle.py).  Cases cover every lane layout of the kernel (1 .. 32 lanes per row,
-whole wavefronts with 2 .. 17 pieces per lane), the row kernel (forced, and for
-misaligned tensors), the three dtypes, dilation, ragged and tiny sequences, in-place
+whole wavefronts with 2 .. 8 pieces per lane, whole workgroups with 5 or 9), the row
+kernel (forced, for misaligned tensors and for rows longer than 256 x 9 pieces), the three dtypes, dilation, ragged and tiny sequences, in-place
 use and poisoned out-of-range slots; at the benchmark shape and the long-document shape
 the probabilities come from the GPU chain itself (qk -> softmax) and the gradient from
 dP = qk(dO, V), checked on sampled rows.
@@ -25,7 +25,8 @@ pytestmark = pytest.mark.gpu
 DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 # (b, n, h, w, w_upper, dilation, dtype): the comment names the kernel layout it reaches
-# (L lanes per row for rows of up to 3 L pieces of 16 bytes, then whole wavefronts)
+# (L lanes per row for rows of up to 3 L pieces of 16 bytes, then whole wavefronts, then
+# whole workgroups of 256 lanes)
 CASES = [
     (1, 512, 1, 32, 32, 0, "f32"),      # 65 slots, f32 (4 per piece): 8 lanes
     (1, 1, 1, 3, 3, 0, "f16"),          # one position
@@ -41,7 +42,13 @@ CASES = [
     (1, 40, 1, 300, 0, 0, "bf16"),      # 301 slots, causal: 16 lanes
     (1, 30, 1, 700, 700, 0, "f16"),     # 1401 slots: wave, 4 pieces per lane
     (1, 30, 1, 1200, 1200, 0, "f16"),   # 2401 slots: a wavefront, 8 pieces per lane
-    (1, 12, 1, 4096, 4096, 0, "f16"),   # 8193 slots: a wavefront, 17 pieces per lane
+    (1, 12, 1, 4096, 4096, 0, "f16"),   # 8193 slots: a workgroup, up to 5 pieces per lane
+    (1, 8, 1, 2500, 2500, 0, "bf16"),   # 5001 slots: a workgroup, 3 pieces per lane
+    (1, 40, 1, 3000, 3000, 3, "bf16"),  # 6001 slots, dilated: a workgroup
+    (1, 6, 2, 9000, 9000, 0, "f16"),    # 18001 slots: a workgroup, up to 9 pieces per lane
+    (1, 10, 1, 2000, 2000, 0, "f32"),   # 4001 f32 slots: a workgroup, up to 4 pieces
+    (1, 6, 1, 4500, 4500, 0, "f32"),    # 9001 f32 slots: a workgroup, up to 9 pieces
+    (1, 4, 1, 10000, 10000, 0, "f16"),  # 20001 slots (2501 pieces): the row kernel
     (1, 20, 1, 150, 150, 0, "f32"),     # 301 f32 slots: 32 lanes
     (1, 20, 1, 1000, 1000, 0, "f32"),   # 2001 f32 slots: a wavefront, 8 pieces per lane
     (1, 50, 2, 16, 15, 0, "f16"),       # 32 slots: 2 lanes per row
@@ -162,7 +169,7 @@ def test_softmax_bwd_at_the_benchmark_shape(dil):
 
 
 def test_softmax_bwd_at_the_long_document_shape():
-    """n = 32768, 8193 diagonals, h = 12, f16 (a wavefront per row, 17 pieces per lane):
+    """n = 32768, 8193 diagonals, h = 12, f16 (a workgroup per row, up to 5 pieces a lane):
     P and dP from the GPU chain, 64 sampled rows against the oracle."""
     import sliding_window_attention_diagmm_amd as dm
     wl = datagen.WORKLOADS["long_n32768"]

@@ -409,12 +409,17 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
 
     // gl: the staged block holds global keys (ranks u0 .. u0 + 63 of the set)
     auto compute_block = [&](int u0, bool gl) {
+        // 32-key chunks that hold any key: all but a block of global keys whose ranks end
+        // in its first chunk (the rest are -inf before and exact zeros after the exponent,
+        // so skipping them changes nothing)
+        const int nck = gl && ngd - u0 <= 32 ? 1 : kChunks;
 
         // ---- scores: lane (col, grp) gets S[query tq][keys u0 + 32 c + 8 grp + 0..7]
         f32x4 s0[kChunks], s1[kChunks];
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
             s0[c] = s1[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (c >= nck) continue;
 #pragma unroll
             for (int kk = 0; kk < kQk; ++kk) {
                 const V a0 = *reinterpret_cast<const V*>(klds + kpiece<D>(32 * c + krow0, 4 * kk + grp));
@@ -433,10 +438,19 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
         const int tw = t0 + 16 * wv;           // this wave's first row
         // (with global tokens: a window block none of whose keys is global; the bitmap
         // words covering keys u0 .. u0 + 63 lie inside the range when the window test holds)
-        auto no_global_keys = [&]() {
-            const int o = u0 - u_lo, wa = o >> 5, wb = (o + kKeys - 1) >> 5;
-            return (gbits[wa] | gbits[wa + 1] | gbits[wb]) == 0u;
-        };
+        // gm: bit j = key u0 + j is global (window blocks with global tokens; words past
+        // the range hold zeros, and keys past it are masked anyway)
+        uint64_t gm = 0;
+        if constexpr (kMode == kBandGlobal) {
+            if (!gl) {
+                const int o = u0 - u_lo, wa = o >> 5, sh = o & 31;
+                const int w1 = wa + 1 < kBitWords ? wa + 1 : kBitWords - 1;
+                const int w2 = wa + 2 < kBitWords ? wa + 2 : kBitWords - 1;
+                const uint64_t lo64 = gbits[wa] | (static_cast<uint64_t>(gbits[w1]) << 32);
+                gm = sh ? (lo64 >> sh) | (static_cast<uint64_t>(gbits[w2]) << (64 - sh)) : lo64;
+            }
+        }
+        auto no_global_keys = [&]() { return gm == 0; };
         bool inner;
         if constexpr (kRowsMode) inner = u0 + kKeys - 1 < len;
         else
@@ -451,20 +465,23 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
             mx *= cs;
         } else {
 #pragma unroll
-            for (int c = 0; c < kChunks; ++c)
+            for (int c = 0; c < kChunks; ++c) {
+                // this lane's 8 keys' global bits
+                const uint32_t g8 = static_cast<uint32_t>(gm >> (32 * c + 8 * grp)) & 0xffu;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int u = u0 + 32 * c + 8 * grp + e;
                     bool ok;
                     if constexpr (kRowsMode) ok = u < len;
                     else if constexpr (kMode == kBandGlobal)
-                        ok = gl ? u < ngd : (u >= lo && u <= hi && u < len && !is_global_key(u));
+                        ok = gl ? u < ngd : (u >= lo && u <= hi && u < len && !((g8 >> e) & 1u));
                     else ok = u >= lo && u <= hi && u < len;
                     const float sv = ok ? sc(c, e) * cs : -__builtin_inff();
                     if (e < 4) s0[c][e] = sv;               // (e is a constant here)
                     else s1[c][e - 4] = sv;
                     mx = fmaxf(mx, sv);
                 }
+            }
         }
         // the four lane groups of a query: swaps with lanes l ^ 16 and l ^ 32 (each swap
         // returns this lane's value and its partner's, in some order).  The halves are
@@ -499,6 +516,7 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
         const float k1 = inner ? cs : 1.0f;
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
+            if (c >= nck) continue;
             f32x8 p;
 #pragma unroll
             for (int e = 0; e < 8; ++e)

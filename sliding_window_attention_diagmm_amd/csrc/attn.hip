@@ -102,6 +102,7 @@ __host__ __device__ constexpr int attn_min_groups(int d) { return d <= 64 ? 4 : 
 constexpr int kChunks = kKeys / 32;         // 32-key chunks per block
 constexpr int64_t kMaxGlobalN = int64_t(1) << 16;   // the LDS global set: 2 n bits <= 16 KB
 constexpr int kMaxSplit = 32;               // key ranges per block of global rows, at most
+constexpr int kBitWords = 512;   // LDS bitmap of global keys in a workgroup's key range
 
 struct AttnArgs {
     int64_t n, h, w, wu, s;
@@ -132,15 +133,27 @@ template <class T> struct GlobalIn {
 
 // The global set of batch bb in LDS: gmap (nw words, bit x = position x listed) and gpre
 // (exclusive prefix popcounts of the words); returns its size.  wsum: 4 words of LDS.
+// With gbits (kBitWords words), the same pass over the list also marks the listed keys u
+// of residue class r (position r + s u) in [u_lo, u_hi], as bit u - u_lo.
 __device__ __forceinline__ int build_set(const int32_t* __restrict__ glob, int64_t bb, int ng,
-                                         int n, uint32_t* gmap, uint32_t* gpre, uint32_t* wsum) {
+                                         int n, uint32_t* gmap, uint32_t* gpre, uint32_t* wsum,
+                                         uint32_t* gbits = nullptr, int r = 0, int s = 1,
+                                         int u_lo = 0, int u_hi = -1) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nw = (n + 31) >> 5;
     for (int i = tid; i < nw; i += kThreads) gmap[i] = 0u;
+    if (gbits)
+        for (int i = tid; i < kBitWords; i += kThreads) gbits[i] = 0u;
     __syncthreads();
     for (int g = tid; g < ng; g += kThreads) {
         const int x = glob[bb * ng + g];
-        if (x >= 0 && x < n) atomicOr(&gmap[x >> 5], 1u << (x & 31));
+        if (x < 0 || x >= n) continue;
+        atomicOr(&gmap[x >> 5], 1u << (x & 31));
+        if (gbits) {
+            const int u = x / s;
+            if (x - u * s == r && u >= u_lo && u <= u_hi)
+                atomicOr(&gbits[(u - u_lo) >> 5], 1u << ((u - u_lo) & 31));
+        }
     }
     __syncthreads();
     // thread t counts words [w0, w1); a scan within each wave, then over the 4 wave totals
@@ -185,7 +198,6 @@ __device__ __forceinline__ int set_member(const uint32_t* gmap, const uint32_t* 
 // Kernel modes: the window only; the window plus the global keys for rows outside the
 // global set (global query rows are not stored); global rows over one key range.
 constexpr int kBand = 0, kBandGlobal = 1, kGlobalRows = 2;
-constexpr int kBitWords = 512;   // LDS bitmap of global keys in a workgroup's key range
 
 // K block: row r (key), 16-byte piece ch at r * 2D + 16 (ch ^ sw(r)); the swizzle puts the
 // eight rows 8 (m / 4) + (m % 4) (+ 4) read by lanes m = 0..7 of a score tile on distinct
@@ -265,7 +277,7 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
     }
     const int64_t bb = bh / a.h, hh = bh - bb * a.h;
     const int nw = static_cast<int>((a.n + 31) >> 5);
-    if constexpr (kMode != kBand)
+    if constexpr (kRowsMode)
         ngd = build_set(gi.glob, bb, ng, static_cast<int>(a.n), gmap, gpre, wsum);
     if constexpr (kRowsMode) {
         // the first key range's workgroup records the positions of its 64 rows
@@ -307,19 +319,12 @@ __device__ __forceinline__ void attn_body(const typename In::T* __restrict__ q,
     }
     nblk = (u_hi - u_lo + kKeys) / kKeys;
 
-    // global keys of this class inside the key range, as bits of u - u_lo
-    if constexpr (kMode == kBandGlobal) {
-        for (int i = tid; i < kBitWords; i += kThreads) gbits[i] = 0u;
-        __syncthreads();
-        for (int g = tid; g < ng; g += kThreads) {
-            const int x = gi.glob[bb * ng + g];
-            if (x < 0 || x >= a.n) continue;
-            const int u = x / static_cast<int>(a.s);
-            if (x - u * static_cast<int>(a.s) == r && u >= u_lo && u <= u_hi)
-                atomicOr(&gbits[(u - u_lo) >> 5], 1u << ((u - u_lo) & 31));
-        }
-        __syncthreads();
-    }
+    // band workgroups with global keys: the set, and the global keys of this class inside
+    // the key range as bits u - u_lo, in one pass over the list (after the query loads are
+    // issued, so that both latencies overlap)
+    if constexpr (kMode == kBandGlobal)
+        ngd = build_set(gi.glob, bb, ng, static_cast<int>(a.n), gmap, gpre, wsum, gbits,
+                        static_cast<int>(r), static_cast<int>(a.s), u_lo, u_hi);
     auto is_global_key = [&](int u) {
         return ((gbits[(u - u_lo) >> 5] >> ((u - u_lo) & 31)) & 1u) != 0u;
     };

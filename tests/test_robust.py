@@ -250,3 +250,43 @@ def test_inplace_backward_and_dropout_match_out_of_place(shape):
     got = dm.diagmm_banded_dropout(pc, rand, w, wu, dil, 0.25, out=pc)
     assert got.data_ptr() == pc.data_ptr()
     assert_bits_equal(got, ref, "dropout in place")
+
+
+# Rows longer than a wavefront holds (the workgroup-per-row softmax and softmax backward
+# kernels, up to 5 and 9 pieces a lane): guard regions, in place against out of place, and
+# NaN in out-of-range slots (pieces holding no in-range slot are not read at all).
+LONG_ROWS = [  # b, n, h, d, w, wu, dil, dtype
+    (1, 40, 2, 64, 2500, 2500, 0, "bf16"),
+    (1, 30, 1, 64, 4500, 4500, 0, "f32"),
+    (1, 20, 2, 64, 3000, 1000, 3, "f16"),
+]
+
+
+@pytest.mark.parametrize("shape", LONG_ROWS)
+def test_long_row_softmax_kernels_guards_inplace_and_poison(shape):
+    import sliding_window_attention_diagmm_amd as dm
+    b, n, h, d, w, wu, dil, dt = shape
+    K = w + wu + 1
+    g = datagen.rng(77)
+    s = datagen.normal(g, (b, n, h, K), dt, 2.0).cuda()
+    p, dp, _, _ = _band_inputs(shape, 78)
+    inr = in_range_mask(b, n, h, w, wu, dil).cuda()
+    bad = torch.tensor(float("nan"), dtype=s.dtype, device="cuda")
+    for name, fn, args, poisoned in (
+            ("softmax", lambda *t, out=None: dm.diagmm_banded_softmax(
+                t[0], w, wu, dil, 0.125, out=out), (s,), (torch.where(inr, s, bad),)),
+            ("softmax_bwd", lambda *t, out=None: dm.diagmm_banded_softmax_backward(
+                t[0], t[1], w, wu, dil, 0.5, out=out), (p, dp),
+             (torch.where(inr, p, bad), torch.where(inr, dp, bad)))):
+        print(f"long rows: {name} {shape}", flush=True)
+        ref = fn(*args)
+        buf, out, gref, gd, ne = _guarded((b, n, h, K), s.dtype)
+        fn(*args, out=out)
+        torch.cuda.synchronize()
+        _guards_intact(buf, gref, gd, ne)
+        assert_bits_equal(out, ref, f"{name} into a guarded buffer")
+        assert_bits_equal(fn(*poisoned), ref, f"{name} with NaN in out-of-range slots")
+        cl = [t.clone() for t in args]
+        got = fn(*cl, out=cl[-1])
+        assert got.data_ptr() == cl[-1].data_ptr()
+        assert_bits_equal(got, ref, f"{name} in place")

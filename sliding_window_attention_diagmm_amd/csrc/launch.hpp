@@ -101,6 +101,9 @@ struct QkStreamPlan {
     int64_t workgroups = 0;
     int64_t rows_per_range = 0; // longest range (class rows)
     int64_t lds_bytes = 0;
+    bool lines = false;         // whole 128-byte lines per store (pieces held one step)
+    int32_t order = 0;          // range order: 0 strip-major, 1 head-fastest
+    bool interleave = false;    // each XCD's ranges dealt round-robin over its workgroups
     bool ok = false;
 };
 QkStreamPlan plan_qk_stream(const Problem& p, int in_dt, int out_dt);

@@ -27,6 +27,15 @@
 // element, for the row's own slots only, at the end of the range.  Keys outside the
 // sequence take the padding constant; values are rounded to nearest even.
 //
+// Long rows.  Each step's 64 columns of a row are 128 bytes at the row's 16-byte phase, so
+// they end in the middle of a 128-byte line that the next step completes.  With rows of
+// more than 1000 slots the L2 no longer keeps such half-written lines until then, and they
+// go to HBM twice.  There the kernel trades pieces between lane halves and holds the ones
+// past the row's line boundary for one step, so that every store writes whole aligned
+// lines; it also numbers the ranges head-fastest (the same rows of neighbouring heads,
+// adjacent in memory, run together), and below 3000 slots deals each XCD's ranges
+// round-robin over its workgroups when there are more ranges than workgroups.
+//
 // Keys.  Four loader waves stream the range's key window through a ring of 1024 key
 // rows (16 chunks of 64 keys, plus a copy of the chunk in ring slot 0 past slot 15, so
 // that a step's 128 rows are always contiguous), up to four chunks in flight.  Each ring
@@ -38,6 +47,8 @@
 // No barrier inside a range; the waits are bounded.  Compute waves only store while
 // loader waves only load (a wave's vector memory counter covers its loads and stores
 // alike, in issue order, so mixing them would make loads wait behind stores).
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "launch.hpp"
@@ -108,6 +119,8 @@ struct StreamArgs {
     int32_t rq, rrem;   // ranges per workgroup: rq, and one more for the first rrem ranks
     int32_t nq, nm;     // n = nq s + nm: class r has nq + (r < nm) rows
     uint32_t pad;       // padding constant in the output type
+    int32_t order;      // range ids: 0 strip-major (a strip's parts consecutive), 1 head-fastest
+    int32_t interleave; // ranges dealt round-robin over each XCD's workgroups
 };
 
 // Window offset of (key row, 16-byte chunk): chunks XOR-swizzled by the row, so that
@@ -120,7 +133,7 @@ __device__ __forceinline__ int ring_off(int row, int chunk) {
     return row * (D * 2) + ((chunk ^ ((row >> kShift) & kMask)) << 4);
 }
 
-template <class In, int D>
+template <class In, int D, bool kLines>
 __global__ void __launch_bounds__(kThreads)
 qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __restrict__ kx,
                  typename In::T* __restrict__ band, StreamArgs a) {
@@ -153,10 +166,26 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
     const int RB = static_cast<int>(row_elems * 2);     // band bytes between class rows
     const int qk_bytes = static_cast<int>(s * h * D * 2);   // q / k bytes between class rows
 
-    const uint32_t rank = xcd_rank(blockIdx.x, static_cast<uint32_t>(a.nwg));
+    // This workgroup's ranges rfirst + m rstride, m < rcount: a contiguous run, or (with
+    // more ranges than workgroups, on the line path) each XCD's share of the ids dealt
+    // round-robin over its workgroups, so that the XCD works on consecutive ids at once.
+    const uint32_t nwg = static_cast<uint32_t>(a.nwg);
     const uint32_t rq = static_cast<uint32_t>(a.rq), rrem = static_cast<uint32_t>(a.rrem);
-    const uint32_t rbeg = rank * rq + (rank < rrem ? rank : rrem);
-    const uint32_t rend = rbeg + rq + (rank < rrem ? 1u : 0u);
+    uint32_t rfirst, rcount, rstride;
+    if (a.interleave) {
+        const uint32_t ranges = rq * nwg + rrem, per = nwg / kXcds;
+        const uint32_t x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+        const uint32_t lo = static_cast<uint32_t>(uint64_t(ranges) * x / kXcds);
+        const uint32_t hi = static_cast<uint32_t>(uint64_t(ranges) * (x + 1) / kXcds);
+        rfirst = lo + j;
+        rcount = rfirst < hi ? (hi - rfirst + per - 1) / per : 0u;
+        rstride = per;
+    } else {
+        const uint32_t rank = xcd_rank(blockIdx.x, nwg);
+        rfirst = rank * rq + (rank < rrem ? rank : rrem);
+        rcount = rq + (rank < rrem ? 1u : 0u);
+        rstride = 1;
+    }
 
     if (tid < kRingChunks + kComputeWaves) ready[tid] = 0u;
     __syncthreads();
@@ -176,13 +205,25 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
         asm volatile("" ::: "memory");
     };
 
-    for (uint32_t rg = rbeg; rg < rend; ++rg) {
+    for (uint32_t m = 0; m < rcount; ++m) {
+        const uint32_t rg = rfirst + m * rstride;
         // Range rg: strip sigma = rg / g (batch, head, class), part j of g.
         const uint32_t g = static_cast<uint32_t>(a.g);
-        const uint32_t sigma = rg / g, jpart = rg - sigma * g;
         const uint32_t res = static_cast<uint32_t>(a.res), h32 = static_cast<uint32_t>(h);
-        const uint32_t r = sigma % res, bh = sigma / res;
-        const uint32_t hh = bh % h32, bb = bh / h32;
+        uint32_t jpart, r, hh, bb;
+        if (a.order == 0) {                          // strip (batch, head, class) major
+            const uint32_t sigma = rg / g, bh = sigma / res;
+            jpart = rg - sigma * g;
+            r = sigma - bh * res;
+            hh = bh % h32;
+            bb = bh / h32;
+        } else {                                     // head fastest, then part, class, batch
+            const uint32_t rest = rg / h32, rest2 = rest / g;
+            hh = rg - rest * h32;
+            jpart = rest - rest2 * g;
+            r = rest2 % res;
+            bb = rest2 / res;
+        }
         const int n_r = a.nq + (static_cast<int>(r) < a.nm ? 1 : 0);
         const int qr = n_r / static_cast<int>(g), mr = n_r - qr * static_cast<int>(g);
         const int jp = static_cast<int>(jpart);
@@ -351,6 +392,54 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
                     ok && !whole && static_cast<unsigned>(di + 7) < static_cast<unsigned>(K + 7);
                 if (edge) *reinterpret_cast<u32x4*>(part + t * 32 + (di < 0 ? 0 : 16)) = v;
             };
+            // Whole-line stores (kLines).  The two query sets' pieces are traded between the
+            // lane halves (col and col ^ 8, a DPP rotation by 8 within each 16-lane row), so
+            // that lane (col, grp) holds row 16 q2 + 8 half + (col & 7), columns
+            // 8 m .. 8 m + 7 of the step, m = 4 (col >= 8) + sj: each store instruction then
+            // covers 8 rows x 128 contiguous bytes.  Those 128 bytes start at the row's
+            // 16-byte phase, so they straddle two 128-byte lines; the pieces m >= lb, lb the
+            // piece where the row's next line begins (the same at every step), are held one
+            // step and stored with the next step's pieces m < lb, so that the 8 lanes of a row
+            // always write one whole aligned line.  The pieces held after the last step are
+            // stored after the sweep.
+            const bool hi8 = col >= 8;
+            const int r8 = col & 7;
+            const int mpc = 4 * (hi8 ? 1 : 0) + sj;
+            const int prow8 = (c + 8 * r8) * (RB - 2);
+            auto put8 = [&](int x, int q2, int half, const u32x4& v) {
+                const int t = 16 * q2 + 8 * half + r8;
+                const bool ok = t < nr;
+                const int di = x - (c + 8 * t);
+                const bool whole = ok && static_cast<unsigned>(di) <= static_cast<unsigned>(K - 8);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    v, brs, whole ? prow8 + (128 * q2 + 64 * half) * (RB - 2) + 2 * x : kBufDrop,
+                    0, 0);
+                const bool edge =
+                    ok && !whole && static_cast<unsigned>(di + 7) < static_cast<unsigned>(K + 7);
+                if (edge) *reinterpret_cast<u32x4*>(part + t * 32 + (di < 0 ? 0 : 16)) = v;
+            };
+            bool late[2][2];
+            u32x4 held[2][2];
+            if constexpr (kLines) {
+                const int bmod128 = static_cast<int>(reinterpret_cast<uintptr_t>(bs) & 127);
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int lo = c + 8 * (16 * q2 + 8 * hf + r8);
+                        const int lb = ((-(bmod128 + lo * (RB - 2) + 2 * xs)) & 127) >> 4;
+                        late[q2][hf] = mpc >= lb;
+                        held[q2][hf] = u32x4{0u, 0u, 0u, 0u};   // (step 0: columns before every row)
+                    }
+            }
+            auto put_line = [&](int x, int q2, int hf, const u32x4& v) {
+                const bool lt = late[q2][hf];
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = lt ? held[q2][hf][e] : v[e];
+                put8(lt ? x - kStep : x, q2, hf, w);
+                held[q2][hf] = v;
+            };
             // One step: the four blocks at columns x0 .. x0 + 63: window reads, the MFMAs of
             // both query sets (the second set's rows past the class are computed and
             // dropped), rounding, stores.
@@ -374,12 +463,31 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
                         for (int dc = 0; dc < kDC; ++dc)
                             acc[q2][bk] = Mm<In>::run(kf[bk][dc], qf[q2][dc], acc[q2][bk]);
                     }
+                if constexpr (kLines) {
 #pragma unroll
-                for (int pr = 0; pr < 2; ++pr) {
-                    const u32x4 p0 = piece(edge, x0 + 32 * pr, acc[0][2 * pr], acc[0][2 * pr + 1]);
-                    const u32x4 p1 = piece(edge, x0 + 32 * pr, acc[1][2 * pr], acc[1][2 * pr + 1]);
-                    put_direct(x0 + 32 * pr + 8 * sj, 0, ok0, p0);
-                    put_direct(x0 + 32 * pr + 8 * sj, 1, ok1, p1);
+                    for (int q2 = 0; q2 < 2; ++q2) {
+                        const u32x4 p0 = piece(edge, x0, acc[q2][0], acc[q2][1]);
+                        const u32x4 p1 = piece(edge, x0 + 32, acc[q2][2], acc[q2][3]);
+                        u32x4 ra, rb;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t send = hi8 ? p0[e] : p1[e];
+                            const uint32_t recv = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(
+                                static_cast<int>(send), 0x128, 0xf, 0xf, false));   // row_ror:8
+                            ra[e] = hi8 ? recv : p0[e];
+                            rb[e] = hi8 ? p1[e] : recv;
+                        }
+                        put_line(x0 + 8 * mpc, q2, 0, ra);
+                        put_line(x0 + 8 * mpc, q2, 1, rb);
+                    }
+                } else {
+#pragma unroll
+                    for (int pr = 0; pr < 2; ++pr) {
+                        const u32x4 p0 = piece(edge, x0 + 32 * pr, acc[0][2 * pr], acc[0][2 * pr + 1]);
+                        const u32x4 p1 = piece(edge, x0 + 32 * pr, acc[1][2 * pr], acc[1][2 * pr + 1]);
+                        put_direct(x0 + 32 * pr + 8 * sj, 0, ok0, p0);
+                        put_direct(x0 + 32 * pr + 8 * sj, 1, ok1, p1);
+                    }
                 }
             };
             // The head and tail pieces of rows t < nr, element by element: lane l takes row
@@ -447,6 +555,14 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
             if (lane == 0 && C > kRingChunks)
                 __hip_atomic_store(done + c, kAllDone, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+            if constexpr (kLines) {                  // the pieces held after the last step
+                const int xl = xs + kStep * (J - 1) + 8 * mpc;
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf)
+                        if (late[q2][hf]) put8(xl, q2, hf, held[q2][hf]);
+            }
             write_edges();
         }
         __syncthreads();                                     // the window is free again
@@ -455,10 +571,10 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
     }
 }
 
-template <class In, int D>
+template <class In, int D, bool kLines>
 hipError_t launch_typed(const void* q, const void* k, void* band, const StreamArgs& a,
                         hipStream_t stream) {
-    auto kern = qk_stream_kernel<In, D>;
+    auto kern = qk_stream_kernel<In, D, kLines>;
     const int lds = lds_bytes(D);
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -492,6 +608,22 @@ QkStreamPlan plan_qk_stream(const Problem& p, int in_dt, int out_dt) {
     if (sp.workgroups % kXcds != 0 && ceil_div(sp.workgroups, kXcds) * kXcds <= cus)
         sp.workgroups = ceil_div(sp.workgroups, kXcds) * kXcds;
     sp.rows_per_range = ceil_div(longest, g);
+    // Whole-line stores and the head-fastest range order for rows of more than 1000 slots
+    // (DIAGMM_QK_LINES=0 / 1 overrides): there a step's half-written lines no longer wait in
+    // L2 for the next step (n = 8192, 1025 slots: 74 -> 61 us; n = 32768, 4097 slots:
+    // 1286 -> 1027 us; long document: 2512 -> 1997 us), while at 513 slots they do, and the
+    // held pieces only add work (17.6 -> 19.5 us).
+    sp.lines = p.K > 1000;
+    if (const char* e = std::getenv("DIAGMM_QK_LINES")) {
+        if (std::strcmp(e, "0") == 0) sp.lines = false;
+        if (std::strcmp(e, "1") == 0) sp.lines = true;
+    }
+    sp.order = sp.lines ? 1 : 0;
+    // With more ranges than workgroups, each XCD's ranges are dealt round-robin below 3000
+    // slots (n = 16384, 2049 slots: 309 -> 259 us), not beyond (4097 slots: 509 -> 535 us
+    // at n = 16384, 1027 -> 1153 us at n = 32768).
+    sp.interleave = sp.lines && sp.ranges > sp.workgroups && sp.workgroups % kXcds == 0 &&
+                    p.K < 3000;
     sp.lds_bytes = lds_bytes(static_cast<int>(p.d));
     const int64_t row_elems = p.s * p.h * p.K;
     const int64_t span = ((sp.rows_per_range - 1) * row_elems + p.K) * 2;
@@ -513,14 +645,19 @@ hipError_t launch_qk_stream(const void* q, const void* k, void* band, const Prob
                  static_cast<int32_t>(sp.g), static_cast<int32_t>(sp.workgroups),
                  static_cast<int32_t>(sp.ranges / sp.workgroups),
                  static_cast<int32_t>(sp.ranges % sp.workgroups),
-                 static_cast<int32_t>(p.n / p.s), static_cast<int32_t>(p.n % p.s), pad};
+                 static_cast<int32_t>(p.n / p.s), static_cast<int32_t>(p.n % p.s), pad,
+                 sp.order, sp.interleave ? 1 : 0};
     if (in_dt == kF16) {
         switch (p.d) {
-        case 64: return launch_typed<F16, 64>(q, k, band, a, stream);
+        case 64:
+            return sp.lines ? launch_typed<F16, 64, true>(q, k, band, a, stream)
+                            : launch_typed<F16, 64, false>(q, k, band, a, stream);
         }
     } else if (in_dt == kBF16) {
         switch (p.d) {
-        case 64: return launch_typed<BF16, 64>(q, k, band, a, stream);
+        case 64:
+            return sp.lines ? launch_typed<BF16, 64, true>(q, k, band, a, stream)
+                            : launch_typed<BF16, 64, false>(q, k, band, a, stream);
         }
     }
     return hipErrorInvalidValue;

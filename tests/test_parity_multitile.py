@@ -201,3 +201,46 @@ def test_tile_orders_match_oracle(case, order, monkeypatch):
     check_close(got, oracle.pvT(probs, x, w, wu, dil, out_dtype=torch.float64), DT[ind], "pvT")
     got = dm.diagmm_pv(pc, xc, w, wu, dil, out_dtype=DT[outd]).cpu()
     check_close(got, oracle.pv(probs, x, w, wu, dil, out_dtype=torch.float64), DT[ind], "pv")
+
+
+# qk's whole-line store path (rows of more than 1000 slots, or forced with
+# DIAGMM_QK_LINES=1): pieces traded between lane halves and held one step so that every
+# store writes whole aligned 128-byte lines, ranges in head-fastest order.  Whole band
+# against the oracle, padding slots bit for bit, both paths where forced.
+# (b, n, h, w, w_upper, dilation, dtype, DIAGMM_QK_LINES, workgroups or 0 for the default)
+LINE_CASES = [
+    (1, 700, 2, 600, 600, 0, "f16", None, 0),       # 1201 slots: the line path by default
+    (1, 2100, 1, 520, 490, 2, "bf16", None, 0),     # 1011 slots, dilation 2, ragged classes
+    (1, 1000, 2, 256, 256, 0, "f16", "1", 0),       # 513 slots, forced
+    (2, 500, 3, 100, 30, 3, "f16", "1", 0),         # dilation 3, two batches, forced
+    (1, 300, 3, 40, 40, 0, "bf16", "1", 5),         # small grid: several ranges per workgroup
+    (2, 700, 3, 100, 100, 0, "f16", "1", 16),       # 24 ranges on 16: dealt round-robin per XCD
+    (1, 64, 2, 9, 0, 0, "f16", "1", 0),             # 10 slots, causal
+    (1, 1300, 2, 700, 700, 1, "bf16", "0", 7),      # 1401 slots with the line path off
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", LINE_CASES,
+                         ids=lambda c: f"b{c[0]}n{c[1]}h{c[2]}w{c[3]}u{c[4]}s{c[5]}-{c[6]}-L{c[7]}-wg{c[8]}")
+def test_qk_stream_line_stores_match_oracle(case, monkeypatch):
+    b, n, h, w, wu, dil, dt, lines, wg = case
+    if lines is None:
+        monkeypatch.delenv("DIAGMM_QK_LINES", raising=False)
+    else:
+        monkeypatch.setenv("DIAGMM_QK_LINES", lines)
+    if wg:
+        monkeypatch.setenv("DIAGMM_MAX_WORKGROUPS", str(wg))
+    else:
+        monkeypatch.delenv("DIAGMM_MAX_WORKGROUPS", raising=False)
+    assert dm.diagmm_plan("qk", b, n, h, 64, w, wu, dil, DT[dt])["kernel"] == "qk_stream"
+    g = datagen.rng(123)
+    q = datagen.normal(g, (b, n, h, 64), dt, 0.125)
+    k = datagen.normal(g, (b, n, h, 64), dt, 0.125)
+    pad = 2.5
+    got = dm.diagmm_qk(q.cuda(), k.cuda(), w, wu, dil, pad).cpu()
+    ref = oracle.qk(q, k, w, wu, dil, pad, out_dtype=torch.float64)
+    ref_out = oracle.qk(q, k, w, wu, dil, pad, out_dtype=DT[dt])
+    mask = in_range_mask(b, n, h, w, wu, dil)
+    check_close(got, ref, DT[dt], "qk line stores", mask)
+    assert_bits_equal(got[~mask], ref_out[~mask], "qk line stores: padding slots")

@@ -102,6 +102,7 @@ struct QkStreamPlan {
     int64_t rows_per_range = 0; // longest range (class rows)
     int64_t lds_bytes = 0;
     bool lines = false;         // whole 128-byte lines per store (pieces held one step)
+    bool stream_stores = false; // line-path stores non-temporal (bands larger than the MALL)
     int32_t order = 0;          // range order: 0 strip-major, 1 head-fastest
     bool interleave = false;    // each XCD's ranges dealt round-robin over its workgroups
     bool ok = false;

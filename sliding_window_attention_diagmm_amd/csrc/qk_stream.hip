@@ -33,8 +33,10 @@
 // go to HBM twice.  There the kernel trades pieces between lane halves and holds the ones
 // past the row's line boundary for one step, so that every store writes whole aligned
 // lines; it also numbers the ranges head-fastest (the same rows of neighbouring heads,
-// adjacent in memory, run together), and below 3000 slots deals each XCD's ranges
-// round-robin over its workgroups when there are more ranges than workgroups.
+// adjacent in memory, run together) and, with more ranges than workgroups, deals each
+// XCD's ranges round-robin over its workgroups.  Bands larger than the Infinity Cache
+// (256 MB) are stored with the non-temporal hint: no later kernel would find them cached,
+// and streamed out they no longer hold the L2 until the end of the launch.
 //
 // Keys.  Four loader waves stream the range's key window through a ring of 1024 key
 // rows (16 chunks of 64 keys, plus a copy of the chunk in ring slot 0 past slot 15, so
@@ -99,6 +101,7 @@ constexpr uint32_t kAllDone = 1u << 30;          // a compute wave's count once 
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kBufWord3 = 0x00020000;            // raw 32-bit buffer access (gfx9 word 3)
 constexpr int kBufDrop = static_cast<int>(0x80000000u);   // offset past every range
+constexpr int kPolNt = 2;                        // buffer store cache policy: non-temporal
 
 // LDS: the key ring, the compute waves' head and tail pieces, and the progress counters
 // (one per ring slot, one per compute wave).
@@ -133,7 +136,7 @@ __device__ __forceinline__ int ring_off(int row, int chunk) {
     return row * (D * 2) + ((chunk ^ ((row >> kShift) & kMask)) << 4);
 }
 
-template <class In, int D, bool kLines>
+template <class In, int D, bool kLines, int kPol>
 __global__ void __launch_bounds__(kThreads)
 qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __restrict__ kx,
                  typename In::T* __restrict__ band, StreamArgs a) {
@@ -413,7 +416,7 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
                 const bool whole = ok && static_cast<unsigned>(di) <= static_cast<unsigned>(K - 8);
                 __builtin_amdgcn_raw_buffer_store_b128(
                     v, brs, whole ? prow8 + (128 * q2 + 64 * half) * (RB - 2) + 2 * x : kBufDrop,
-                    0, 0);
+                    0, kPol);
                 const bool edge =
                     ok && !whole && static_cast<unsigned>(di + 7) < static_cast<unsigned>(K + 7);
                 if (edge) *reinterpret_cast<u32x4*>(part + t * 32 + (di < 0 ? 0 : 16)) = v;
@@ -571,10 +574,10 @@ qk_stream_kernel(const typename In::T* __restrict__ q, const typename In::T* __r
     }
 }
 
-template <class In, int D, bool kLines>
+template <class In, int D, bool kLines, int kPol>
 hipError_t launch_typed(const void* q, const void* k, void* band, const StreamArgs& a,
                         hipStream_t stream) {
-    auto kern = qk_stream_kernel<In, D, kLines>;
+    auto kern = qk_stream_kernel<In, D, kLines, kPol>;
     const int lds = lds_bytes(D);
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -618,12 +621,24 @@ QkStreamPlan plan_qk_stream(const Problem& p, int in_dt, int out_dt) {
         if (std::strcmp(e, "0") == 0) sp.lines = false;
         if (std::strcmp(e, "1") == 0) sp.lines = true;
     }
+    // Bands larger than the 256 MB Infinity Cache are stored non-temporal on the line path:
+    // the band then streams out instead of filling the L2 with lines that no later kernel
+    // finds there anyway (long document 1960 -> 1533 us with the ranges dealt round-robin).  Smaller
+    // bands are kept cached for the call that reads them next (at 513 slots non-temporal
+    // stores cost the in-place softmax after qk 21 -> 28 us).  DIAGMM_QK_NT=0 / 1 overrides.
+    const int64_t band_bytes = p.b * p.n * p.h * p.K * 2;
+    sp.stream_stores = sp.lines && band_bytes > (int64_t(256) << 20);
+    if (const char* e = std::getenv("DIAGMM_QK_NT")) {
+        if (std::strcmp(e, "0") == 0) sp.stream_stores = false;
+        if (std::strcmp(e, "1") == 0) sp.stream_stores = sp.lines;
+    }
     sp.order = sp.lines ? 1 : 0;
-    // With more ranges than workgroups, each XCD's ranges are dealt round-robin below 3000
-    // slots (n = 16384, 2049 slots: 309 -> 259 us), not beyond (4097 slots: 509 -> 535 us
-    // at n = 16384, 1027 -> 1153 us at n = 32768).
+    // With more ranges than workgroups, each XCD's ranges are dealt round-robin: with
+    // non-temporal stores always (n = 32768, 8193 slots: 1600 -> 1533 us), with cached ones
+    // below 3000 slots (n = 16384, 2049 slots: 309 -> 259 us) but not beyond (4097 slots:
+    // 509 -> 535 us at n = 16384, 1027 -> 1153 us at n = 32768).
     sp.interleave = sp.lines && sp.ranges > sp.workgroups && sp.workgroups % kXcds == 0 &&
-                    p.K < 3000;
+                    (sp.stream_stores || p.K < 3000);
     sp.lds_bytes = lds_bytes(static_cast<int>(p.d));
     const int64_t row_elems = p.s * p.h * p.K;
     const int64_t span = ((sp.rows_per_range - 1) * row_elems + p.K) * 2;
@@ -650,14 +665,16 @@ hipError_t launch_qk_stream(const void* q, const void* k, void* band, const Prob
     if (in_dt == kF16) {
         switch (p.d) {
         case 64:
-            return sp.lines ? launch_typed<F16, 64, true>(q, k, band, a, stream)
-                            : launch_typed<F16, 64, false>(q, k, band, a, stream);
+            return !sp.lines ? launch_typed<F16, 64, false, 0>(q, k, band, a, stream)
+                   : sp.stream_stores ? launch_typed<F16, 64, true, kPolNt>(q, k, band, a, stream)
+                                      : launch_typed<F16, 64, true, 0>(q, k, band, a, stream);
         }
     } else if (in_dt == kBF16) {
         switch (p.d) {
         case 64:
-            return sp.lines ? launch_typed<BF16, 64, true>(q, k, band, a, stream)
-                            : launch_typed<BF16, 64, false>(q, k, band, a, stream);
+            return !sp.lines ? launch_typed<BF16, 64, false, 0>(q, k, band, a, stream)
+                   : sp.stream_stores ? launch_typed<BF16, 64, true, kPolNt>(q, k, band, a, stream)
+                                      : launch_typed<BF16, 64, true, 0>(q, k, band, a, stream);
         }
     }
     return hipErrorInvalidValue;

@@ -207,7 +207,8 @@ def test_tile_orders_match_oracle(case, order, monkeypatch):
 # DIAGMM_QK_LINES=1): pieces traded between lane halves and held one step so that every
 # store writes whole aligned 128-byte lines, ranges in head-fastest order.  Whole band
 # against the oracle, padding slots bit for bit, both paths where forced.
-# (b, n, h, w, w_upper, dilation, dtype, DIAGMM_QK_LINES, workgroups or 0 for the default)
+# (b, n, h, w, w_upper, dilation, dtype, DIAGMM_QK_LINES (+ "nt": DIAGMM_QK_NT=1),
+#  workgroups or 0 for the default)
 LINE_CASES = [
     (1, 700, 2, 600, 600, 0, "f16", None, 0),       # 1201 slots: the line path by default
     (1, 2100, 1, 520, 490, 2, "bf16", None, 0),     # 1011 slots, dilation 2, ragged classes
@@ -217,6 +218,9 @@ LINE_CASES = [
     (2, 700, 3, 100, 100, 0, "f16", "1", 16),       # 24 ranges on 16: dealt round-robin per XCD
     (1, 64, 2, 9, 0, 0, "f16", "1", 0),             # 10 slots, causal
     (1, 1300, 2, 700, 700, 1, "bf16", "0", 7),      # 1401 slots with the line path off
+    # non-temporal line stores (bands over 256 MB by default), forced on small bands
+    (1, 700, 2, 600, 600, 0, "f16", "1nt", 0),
+    (2, 700, 3, 100, 100, 3, "bf16", "1nt", 16),    # dilation 3, ranges dealt round-robin
 ]
 
 
@@ -225,10 +229,13 @@ LINE_CASES = [
                          ids=lambda c: f"b{c[0]}n{c[1]}h{c[2]}w{c[3]}u{c[4]}s{c[5]}-{c[6]}-L{c[7]}-wg{c[8]}")
 def test_qk_stream_line_stores_match_oracle(case, monkeypatch):
     b, n, h, w, wu, dil, dt, lines, wg = case
+    monkeypatch.delenv("DIAGMM_QK_NT", raising=False)
     if lines is None:
         monkeypatch.delenv("DIAGMM_QK_LINES", raising=False)
     else:
-        monkeypatch.setenv("DIAGMM_QK_LINES", lines)
+        monkeypatch.setenv("DIAGMM_QK_LINES", lines[0])
+        if lines.endswith("nt"):
+            monkeypatch.setenv("DIAGMM_QK_NT", "1")
     if wg:
         monkeypatch.setenv("DIAGMM_MAX_WORKGROUPS", str(wg))
     else:

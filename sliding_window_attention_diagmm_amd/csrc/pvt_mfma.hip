@@ -35,14 +35,16 @@
 //
 // Order.  Neighbouring tiles of a residue class read the same 128-byte lines of each band
 // row: the parallelogram of a tile starts and ends inside a line of every row it crosses,
-// and the tile next to it reads the rest of that line.  On the flat split the tiles of
-// each XCD can therefore be dealt round-robin over its workgroups (tiles lo + j + m nwg / 8
-// for its j-th workgroup), so neighbouring tiles run at the same time and the lines they
-// share are fetched from HBM once while they sit in the XCD's L2; a workgroup's
-// consecutive tiles are then apart, and each tile loads its whole X window.  That is done
-// where a round of tiles over the XCD reads more band lines than its L2 holds (the shared
-// lines would be gone by the workgroup's next tile).  Otherwise, and on the strip split,
-// a workgroup keeps a contiguous run of tiles, its window sliding by 64 rows from one to
+// and the tile next to it reads the rest of that line.  The tiles can therefore be dealt
+// round-robin, on the flat split over the XCD's workgroups (tiles lo + j + m nwg / 8 for
+// its j-th workgroup), on the strip split over the strip's (tiles j + m g of the strip),
+// so neighbouring tiles run at the same time and the lines they share are fetched from
+// HBM once while they sit in the XCD's L2; a workgroup's consecutive tiles are then
+// apart, and each tile loads its whole X window.  That is done on the flat split where a
+// round of tiles over the XCD reads more band lines than its L2 holds (the shared lines
+// would be gone by the workgroup's next tile), and on the strip split only when asked for
+// (the whole-window loads cost more time there than the band lines save).  Otherwise a
+// workgroup keeps a contiguous run of tiles, its window sliding by 64 rows from one to
 // the next.
 //
 // Pipelining.  The next tile's band pieces (and, when the window slides, its 64 new X
@@ -96,7 +98,7 @@ struct PvTArgs {
     int64_t band_elems;
     TileDecode dc;         // whole tiles (units) over workgroups, unit -> coordinates
     Div32 chunks;          // item -> (unit, chunk)
-    int32_t interleave;    // units interleaved over each XCD's workgroups (flat split)
+    int32_t interleave;    // units interleaved over the XCD's (flat split) or strip's workgroups
 };
 
 struct Item {
@@ -137,7 +139,7 @@ pvt_mfma_kernel(const typename In::T* __restrict__ band, const typename In::T* _
     const int cb0 = (wave & 1) * kCBPerWave;                // first channel block
 
     // Items: the chunks of this workgroup's units, the units taken as a sequence
-    // ufirst + ustride m (interleaved over the XCD's workgroups on the flat split).
+    // ufirst + ustride m (interleaved over the XCD's or the strip's workgroups).
     uint32_t item = 0, iend, ufirst, ustride;
     {
         uint32_t cnt;
@@ -523,16 +525,20 @@ PvTilePlan plan_pvt_mfma(const Problem& p) {
         tp.strip_wgs = pick_strip_split(tp.grid.tiles / tp.grid.nkb / per_strip, per_strip,
                                         kRows, ceil_div(p.n, p.s) - (per_strip - 1) * kRows,
                                         tp.workgroups);
-    // Tile order on the flat split: a workgroup's next tile shares lines with its current
-    // one, but by then every workgroup of the XCD has read a whole tile's band lines
-    // (2 lines of each of its 64 + KC - 1 window rows, every chunk of the tile).  Where that
-    // round exceeds the XCD's L2 (4 MB), the shared lines are gone before they are read
-    // again: deal the tiles round-robin instead (each tile then loads its whole X window).
+    // Tile order: a workgroup's next tile shares lines with its current one, but by then
+    // every workgroup of the XCD has read a whole tile's band lines (2 lines of each of its
+    // 64 + KC - 1 window rows, every chunk of the tile).  Where that round exceeds the
+    // XCD's L2 (4 MB), the shared lines are gone before they are read again: deal the
+    // tiles round-robin instead (each tile then loads its whole X window).  That is done
+    // on the flat split; on the strip split only when forced, since there the extra X
+    // window loads cost more time than the band lines it saves (at n = 4096, h = 12, 513
+    // slots, dilation 3: 62 instead of 90 MB fetched, but 1.5 us slower).
     const int64_t round_bytes = (tp.workgroups / kXcds) * tp.grid.nkb *
                                 (kRows + tp.grid.kb - 1) * 256;
     const int forced = tile_order_forced();
-    tp.interleave = tp.strip_wgs == 0 && tp.workgroups % kXcds == 0 &&
-                    (forced ? forced == 1 : round_bytes > (int64_t(4) << 20));
+    tp.interleave = tp.workgroups % kXcds == 0 &&
+                    (forced ? forced == 1
+                            : tp.strip_wgs == 0 && round_bytes > (int64_t(4) << 20));
     tp.ok = tp.grid.tiles <= kMaxTiles && ceil_div(p.n, p.s) < (int64_t(1) << 30) &&
             p.K < (int64_t(1) << 30) && p.w < (int64_t(1) << 30) && l.bytes <= kPvLdsBytes &&
             tp.workgroups >= 1 && (p.d == 32 || p.d == 64 || p.d == 128);

@@ -21,8 +21,9 @@ static bool qk_tiles_forced() {
     return e && std::strcmp(e, "tiles") == 0;
 }
 
-// DIAGMM_TILE_ORDER=interleaved / contiguous overrides the choice of tile order of pv and
-// pvT on the flat split (a testing and comparison switch): 1 and 2, else 0.
+// DIAGMM_TILE_ORDER=interleaved / contiguous overrides the choice of tile order of pv on
+// the flat split and of pvT on either split (a testing and comparison switch): 1 and 2,
+// else 0.
 int tile_order_forced() {
     const char* e = std::getenv("DIAGMM_TILE_ORDER");
     if (!e) return 0;

@@ -225,6 +225,10 @@ __host__ __device__ inline void unit_range(const TileDecode& dc, uint32_t rank,
 // units [U x / 8, U (x + 1) / 8) of the U in all, and its j-th workgroup (j = wg / 8) takes
 // every (nwg / 8)-th of them from the j-th on, so that at any moment the XCD's workgroups
 // hold neighbouring units and read the cache lines those share while they are in its L2.
+// Interleaved on the strip split: the j-th workgroup of a strip (ranks taken as in
+// unit_range) takes the strip's units j, j + g, j + 2 g, ... (g workgroups per strip), so
+// that a strip's neighbouring units run at the same time; a strip's workgroups are
+// consecutive XCD ranks, mostly on one XCD.
 // Otherwise the contiguous range of unit_range for the workgroup's XCD rank.
 __host__ __device__ inline void unit_seq(const TileDecode& dc, uint32_t wg, uint32_t nwg,
                                          bool interleave, uint32_t* first, uint32_t* count,
@@ -237,6 +241,19 @@ __host__ __device__ inline void unit_seq(const TileDecode& dc, uint32_t wg, uint
         *first = lo + j;
         *stride = per;
         *count = lo + j < hi ? (hi - lo - j + per - 1) / per : 0u;
+        return;
+    }
+    if (interleave && dc.strip_wgs != 0) {
+        const uint32_t rank = xcd_rank(wg, nwg);
+        const uint32_t strip = rank / dc.strip_wgs, j = rank - strip * dc.strip_wgs;
+        *stride = dc.strip_wgs;
+        if (strip >= dc.strip_count || j >= dc.strip_units) {
+            *first = 0;
+            *count = 0;
+            return;
+        }
+        *first = strip * dc.strip_units + j;
+        *count = (dc.strip_units - j + dc.strip_wgs - 1) / dc.strip_wgs;
         return;
     }
     uint32_t b, e;

@@ -108,6 +108,44 @@ int main() {
                 }
         }
     }
+    // the strip split (g workgroups per strip of whole tiles), contiguous and interleaved:
+    // every unit exactly once, each workgroup's units inside one strip, counts within one
+    // (g x strips <= nwg, as the planner picks g)
+    struct SCase { int64_t b, n, h, K, s, nwg, g; };
+    const SCase scases[] = {{1, 4096, 12, 513, 3, 256, 7}, {2, 1100, 2, 169, 2, 24, 3},
+                            {1, 300, 3, 65, 4, 24, 2}, {1, 640, 1, 33, 1, 7, 7}};
+    for (const SCase& c : scases) {
+        const TileGrid g = make_grid(c.b, c.n, c.h, c.K, c.s, 64, c.K);
+        const int64_t per_strip = g.rb, strips = g.tiles / per_strip;
+        TileDecode dc = make_decode(g, c.h, c.n, c.s, g.tiles, c.nwg);
+        set_strip_split(&dc, strips, per_strip, c.g);
+        for (bool il : {true, false}) {
+            std::vector<int> seen(static_cast<size_t>(g.tiles), 0);
+            for (uint32_t wg = 0; wg < static_cast<uint32_t>(c.nwg); ++wg) {
+                uint32_t f, cnt, st;
+                unit_seq(dc, wg, static_cast<uint32_t>(c.nwg), il, &f, &cnt, &st);
+                const uint64_t want = per_strip / c.g;
+                if (cnt && (cnt < want || cnt > want + 1)) {
+                    std::printf("strip unit_seq unbalanced at wg %u\n", wg);
+                    return 1;
+                }
+                for (uint32_t m = 0; m < cnt; ++m) {
+                    const uint64_t u = f + uint64_t(m) * st;
+                    if (u >= static_cast<uint64_t>(g.tiles) || seen[u]++ ||
+                        u / per_strip != f / per_strip) {
+                        std::printf("strip unit_seq bad at wg %u (interleave %d)\n", wg, int(il));
+                        return 1;
+                    }
+                }
+            }
+            for (int64_t t = 0; t < g.tiles; ++t)
+                if (seen[t] != 1) {
+                    std::printf("strip unit_seq misses unit %lld (interleave %d)\n",
+                                (long long)t, int(il));
+                    return 1;
+                }
+        }
+    }
     std::printf("ok\n");
     return 0;
 }

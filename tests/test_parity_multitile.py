@@ -149,8 +149,9 @@ def test_tile_order(monkeypatch):
     same time) where a round of contiguous runs would read more band lines than an XCD's
     4 MB L2 holds before a workgroup's next tile reuses them: at n = 4096, h = 12, 513
     slots (32 workgroups x 576 window rows x 256 bytes = 4.7 MB) and at 8193 slots (16
-    chunks a tile); not at 257 slots (320 rows, 2.6 MB), nor on the strip split.  pv does
-    the same for tiles of several chunks only (one-chunk tiles slide their key window)."""
+    chunks a tile); not at 257 slots (320 rows, 2.6 MB), nor on the strip split unless
+    forced (dilation 3: each strip's 7 workgroups).  pv does the same for tiles of several
+    chunks on the flat split only (one-chunk tiles slide their key window)."""
     monkeypatch.delenv("DIAGMM_MAX_WORKGROUPS", raising=False)
     pl = dm.diagmm_plan("pvT", 1, 4096, 12, 64, 256, 256, 0, torch.float16)
     if pl["workgroups"] == 256:
@@ -160,8 +161,14 @@ def test_tile_order(monkeypatch):
         assert dm.diagmm_plan("pvT", 12, 4096, 12, 64, 256, 0, 0, torch.bfloat16,
                               torch.float32)["interleaved"] == 0
     pl3 = dm.diagmm_plan("pvT", 1, 4096, 12, 64, 256, 256, 3, torch.float16)
-    if pl3["strip_workgroups"]:
-        assert pl3["interleaved"] == 0, pl3
+    if pl3["workgroups"] == 256:
+        assert pl3["strip_workgroups"] == 7 and pl3["interleaved"] == 0, pl3
+        monkeypatch.setenv("DIAGMM_TILE_ORDER", "interleaved")
+        assert dm.diagmm_plan("pvT", 1, 4096, 12, 64, 256, 256, 3,
+                              torch.float16)["interleaved"] == 1
+        pv3 = dm.diagmm_plan("pv", 1, 4096, 12, 64, 256, 256, 3, torch.float16)
+        assert pv3["strip_workgroups"] == 7 and pv3["interleaved"] == 0, pv3
+        monkeypatch.delenv("DIAGMM_TILE_ORDER")
     # pv: one-chunk tiles slide their key window, several-chunk tiles are interleaved
     assert dm.diagmm_plan("pv", 1, 4096, 12, 64, 256, 256, 0, torch.float16)["interleaved"] == 0
     if pl["workgroups"] == 256:
@@ -201,6 +208,36 @@ def test_tile_orders_match_oracle(case, order, monkeypatch):
     check_close(got, oracle.pvT(probs, x, w, wu, dil, out_dtype=torch.float64), DT[ind], "pvT")
     got = dm.diagmm_pv(pc, xc, w, wu, dil, out_dtype=DT[outd]).cpu()
     check_close(got, oracle.pv(probs, x, w, wu, dil, out_dtype=torch.float64), DT[ind], "pv")
+
+
+# (b, n, h, d, w, w_upper, dilation, in, out, workgroups, workgroups per strip): strip
+# splits on grids of a multiple of 8 workgroups, where pvT deals each strip's tiles
+# round-robin over the strip's workgroups when forced (ragged last row blocks of 29, 17,
+# 16 and 18 rows)
+STRIP_ORDER_CASES = [
+    (1, 1081, 1, 64, 200, 200, 2, "f16", "f16", 8, 4),
+    (1, 1969, 1, 64, 256, 256, 3, "f16", "f16", 16, 5),
+    (1, 2080, 1, 128, 150, 100, 2, "bf16", "bf16", 16, 8),
+    (1, 2006, 1, 32, 300, 0, 5, "bf16", "f32", 16, 3),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("order", ["interleaved", "contiguous"])
+@pytest.mark.parametrize("case", STRIP_ORDER_CASES,
+                         ids=lambda c: _ids(c[:10]) + f"-g{c[10]}")
+def test_strip_tile_orders_match_oracle(case, order, monkeypatch):
+    b, n, h, d, w, wu, dil, ind, outd, wg, per_strip = case
+    monkeypatch.setenv("DIAGMM_MAX_WORKGROUPS", str(wg))
+    monkeypatch.setenv("DIAGMM_TILE_ORDER", order)
+    pl = dm.diagmm_plan("pvT", b, n, h, d, w, wu, dil, DT[ind], DT[outd])
+    assert pl["kernel"] == "pvT_mfma" and pl["strip_workgroups"] == per_strip, pl
+    assert pl["interleaved"] == (order == "interleaved"), pl
+    g = datagen.rng(93)
+    x = datagen.normal(g, (b, n, h, d), ind, 1.0 / math.sqrt(d))
+    probs = datagen.softmax_rows(g, (b, n, h, w + wu + 1), ind)
+    got = dm.diagmm_pvT(probs.cuda(), x.cuda(), w, wu, dil, out_dtype=DT[outd]).cpu()
+    check_close(got, oracle.pvT(probs, x, w, wu, dil, out_dtype=torch.float64), DT[ind], "pvT")
 
 
 # qk's whole-line store path (rows of more than 1000 slots, or forced with

@@ -63,3 +63,23 @@ def test_bench_launch_matches_oracle(inputs, mode, dil):
     else:
         ref = oracle.pvT(probs, dense, W, WU, dil, out_dtype=torch.float64, rows=rows)
     check_close(flat_out, ref, torch.float16, f"{mode} dil{dil} bench launch")
+
+
+def test_pvt_strip_tile_orders_agree_bitwise(inputs, monkeypatch):
+    """pvT at dilation 3 on its default strip split, and with each strip's tiles dealt
+    round-robin over the strip's workgroups (forced): the same bits, since a tile's sums
+    do not depend on the workgroup that takes it; both against the oracle on the sampled
+    rows through the test above."""
+    import sliding_window_attention_diagmm_amd as dm
+    probs, _, x = inputs
+    monkeypatch.delenv("DIAGMM_TILE_ORDER", raising=False)
+    monkeypatch.delenv("DIAGMM_MAX_WORKGROUPS", raising=False)
+    plan = dm.diagmm_plan("pvT", B, N, H, D, W, WU, 3, torch.float16)
+    pc, xc = probs.cuda(), x.cuda()
+    base = dm.diagmm_pvT(pc, xc, W, WU, 3).cpu()
+    monkeypatch.setenv("DIAGMM_TILE_ORDER", "interleaved")
+    forced = dm.diagmm_plan("pvT", B, N, H, D, W, WU, 3, torch.float16)
+    assert forced["interleaved"] == 1 or plan["workgroups"] % 8 != 0, (plan, forced)
+    assert forced["strip_workgroups"] == plan["strip_workgroups"], (plan, forced)
+    got = dm.diagmm_pvT(pc, xc, W, WU, 3).cpu()
+    assert torch.equal(got, base)
